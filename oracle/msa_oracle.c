@@ -1,0 +1,275 @@
+/*
+ * msa_oracle.c -- plain, slow, fp64 CPU oracle for MiniMax Sparse Attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark load this file's library. The GPU library never links,
+ * includes or calls it, and it shares no code, header or table with the GPU
+ * path.
+ *
+ * What it computes, step by step, follows the page "MiniMax-M3: MSA 技术报告速读"
+ * (mloasisblog.com/blog/ML/minimax-m3-msa-tech-report), section 核心机制:
+ *   - 索引分支 (index branch): the token score equation S^idx and the block
+ *     max-pool M^idx (scores of visible keys j <= i only), then the TopK
+ *     equation per GQA group, with the query's own block always selected.
+ *   - 主分支 (main branch): the softmax attention equation O^(h)_i over the
+ *     selected blocks' visible tokens, all heads of a group sharing the group's
+ *     selection.
+ *
+ * Readings where the page is silent (each is listed with its reason in the
+ * design notes):
+ *   - top_k counts the forced local block: the selection is the local block
+ *     plus the best top_k-1 of the earlier blocks.
+ *   - order of blocks: score descending, then block index ascending.
+ *   - if the query sees top_k blocks or fewer, all of them are selected.
+ *   - the selection is reported in ascending block order, padded with -1.
+ *   - the positive factor 1/sqrt(d_idx) does not change the order, so block
+ *     scores are reported as raw maxima of the dot products.
+ *   - head h belongs to group h / (H_q / H_kv).
+ *
+ * Precision: every input element (fp32 or bf16 storage) is widened exactly to
+ * double; all arithmetic is double; outputs are double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* storage type of an input array */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+/* Widen element i of an fp32 or bf16 array to double, exactly. */
+static double elem(const void *base, int64_t i, int type) {
+  if (type == ORACLE_F32) return (double)((const float *)base)[i];
+  uint32_t bits = ((uint32_t)((const uint16_t *)base)[i]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+typedef struct {
+  double score;
+  int32_t block;
+} scored_block;
+
+/* Order used by TopK: higher score first; equal scores -> lower block first. */
+static int by_score_then_block(const void *a, const void *b) {
+  const scored_block *x = (const scored_block *)a, *y = (const scored_block *)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->block > y->block) - (x->block < y->block);
+}
+
+static int ascending_int(const void *a, const void *b) {
+  int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+  return (x > y) - (x < y);
+}
+
+/*
+ * Index branch for one (sequence, group, query row) at absolute position p.
+ *   q_idx_row : d_idx elements of this row's index query (group r)
+ *   k_idx_seq : the sequence's shared index keys, row j at j*d_idx
+ *   scores    : scratch of p+1 doubles
+ *   bmax      : out, n_blocks doubles: raw block maxima, -inf past the local block
+ *   sel       : out, top_k block indices ascending, -1 padded
+ */
+static void index_row(const void *q_idx_row, const void *k_idx_seq, int type, int d_idx,
+                      int n_blocks, int64_t p, int block_size, int top_k, double *scores,
+                      scored_block *cand, double *bmax, int32_t *sel) {
+  /* token scores S_j = q_idx . k_idx_j for visible keys j <= p (the 1/sqrt(d_idx)
+     factor is positive and left out) */
+  for (int64_t j = 0; j <= p; ++j) {
+    double s = 0.0;
+    for (int d = 0; d < d_idx; ++d)
+      s += elem(q_idx_row, d, type) * elem(k_idx_seq, j * d_idx + d, type);
+    scores[j] = s;
+  }
+  /* causal block max-pool: block c covers keys [c*bs, (c+1)*bs), clipped at p */
+  const int64_t local = p / block_size;
+  for (int c = 0; c < n_blocks; ++c) {
+    if (c > local) {
+      bmax[c] = -INFINITY;
+      continue;
+    }
+    int64_t lo = (int64_t)c * block_size, hi = lo + block_size;
+    if (hi > p + 1) hi = p + 1;
+    double m = -INFINITY;
+    for (int64_t j = lo; j < hi; ++j)
+      if (scores[j] > m) m = scores[j];
+    bmax[c] = m;
+  }
+  /* TopK with the local block forced in */
+  int n_sel = 0;
+  if (local + 1 <= top_k) {
+    for (int c = 0; c <= local; ++c) sel[n_sel++] = c;
+  } else {
+    for (int c = 0; c < local; ++c) {
+      cand[c].score = bmax[c];
+      cand[c].block = c;
+    }
+    qsort(cand, (size_t)local, sizeof(scored_block), by_score_then_block);
+    for (int i = 0; i < top_k - 1; ++i) sel[n_sel++] = cand[i].block;
+    sel[n_sel++] = (int32_t)local;
+    qsort(sel, (size_t)n_sel, sizeof(int32_t), ascending_int);
+  }
+  for (int i = n_sel; i < top_k; ++i) sel[i] = -1;
+}
+
+/*
+ * Main branch for one (sequence, head, query row) at position p:
+ *   T = union over selected blocks c of the visible keys [c*bs, min((c+1)*bs, p+1))
+ *   z_j = q . k_j / sqrt(d_h);  O = sum_j softmax(z)_j v_j;  lse = log sum_j exp(z_j)
+ *   q_row : d_h elements; k_plane, v_plane : the group's keys/values, row j at j*d_h
+ */
+static void attend_row(const void *q_row, const void *k_plane, const void *v_plane, int type,
+                       int d_h, int64_t p, int block_size, const int32_t *sel, int top_k,
+                       double *z, double *o, double *lse) {
+  const double scale = 1.0 / sqrt((double)d_h);
+  int64_t n = 0;
+  double mu = -INFINITY;
+  for (int i = 0; i < top_k; ++i) {
+    if (sel[i] < 0) continue;
+    int64_t lo = (int64_t)sel[i] * block_size, hi = lo + block_size;
+    if (hi > p + 1) hi = p + 1;
+    for (int64_t j = lo; j < hi; ++j) {
+      double s = 0.0;
+      for (int d = 0; d < d_h; ++d) s += elem(q_row, d, type) * elem(k_plane, j * d_h + d, type);
+      z[n] = s * scale;
+      if (z[n] > mu) mu = z[n];
+      ++n;
+    }
+  }
+  for (int d = 0; d < d_h; ++d) o[d] = 0.0;
+  double total = 0.0;
+  n = 0;
+  for (int i = 0; i < top_k; ++i) {
+    if (sel[i] < 0) continue;
+    int64_t lo = (int64_t)sel[i] * block_size, hi = lo + block_size;
+    if (hi > p + 1) hi = p + 1;
+    for (int64_t j = lo; j < hi; ++j) {
+      double w = exp(z[n++] - mu);
+      total += w;
+      for (int d = 0; d < d_h; ++d) o[d] += w * elem(v_plane, j * d_h + d, type);
+    }
+  }
+  for (int d = 0; d < d_h; ++d) o[d] /= total;
+  *lse = mu + log(total);
+}
+
+/*
+ * The whole MSA step for a list of query rows.
+ *
+ * Layouts (contiguous):
+ *   q_idx [B, H_kv, n_q, d_idx]   k_idx [B, n_k, d_idx]
+ *   q     [B, H_q,  n_q, d_h]     k, v  [B, H_kv, n_k, d_h]
+ * rows[i] in [0, n_q) selects query row rows[i]; its position is q_start + rows[i].
+ * Outputs (per listed row, in list order):
+ *   sel   [B, H_kv, n_rows, top_k]            int32
+ *   bmax  [B, H_kv, n_rows, n_blocks] or NULL double
+ *   o     [B, H_q, n_rows, d_h] or NULL       double (NULL: index branch only)
+ *   lse   [B, H_q, n_rows] or NULL            double
+ * Returns 0, or -1 on a bad argument, -2 when out of memory.
+ */
+int msa_oracle_run(int batch, int n_q, int n_k, int q_start, int h_q, int h_kv, int d_h,
+                   int d_idx, int block_size, int top_k, int type, const void *q_idx,
+                   const void *k_idx, const void *q, const void *k, const void *v, int n_rows,
+                   const int32_t *rows, int32_t *sel, double *bmax, double *o, double *lse,
+                   int n_threads) {
+  if (batch < 1 || n_q < 1 || n_k < 1 || q_start < 0 || h_kv < 1 || h_q < h_kv ||
+      h_q % h_kv || d_idx < 1 || block_size < 1 || top_k < 1 || n_rows < 0 || !q_idx ||
+      !k_idx || !rows || !sel || (type != ORACLE_F32 && type != ORACLE_BF16))
+    return -1;
+  if (o && (!q || !k || !v || d_h < 1)) return -1;
+  for (int i = 0; i < n_rows; ++i)
+    if (rows[i] < 0 || rows[i] >= n_q || (int64_t)q_start + rows[i] >= n_k) return -1;
+  const int n_blocks = (n_k + block_size - 1) / block_size;
+  const int group = h_q / h_kv;
+#ifdef _OPENMP
+  if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+  (void)n_threads;
+#endif
+  int failed = 0;
+
+  /* index branch: one task per (b, r, row) */
+  const int64_t n_idx_tasks = (int64_t)batch * h_kv * n_rows;
+#pragma omp parallel
+  {
+    double *scores = (double *)malloc(sizeof(double) * (size_t)n_k);
+    double *bm = (double *)malloc(sizeof(double) * (size_t)n_blocks);
+    scored_block *cand = (scored_block *)malloc(sizeof(scored_block) * (size_t)n_blocks);
+    if (!scores || !bm || !cand) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < n_idx_tasks; ++task) {
+      if (failed) continue;
+      const int i = (int)(task % n_rows);
+      const int r = (int)((task / n_rows) % h_kv);
+      const int b = (int)(task / ((int64_t)n_rows * h_kv));
+      const int64_t t = rows[i], p = (int64_t)q_start + t;
+      const int64_t qoff = (((int64_t)b * h_kv + r) * n_q + t) * d_idx;
+      const int64_t koff = (int64_t)b * n_k * d_idx;
+      const void *qrow = (type == ORACLE_F32) ? (const void *)((const float *)q_idx + qoff)
+                                              : (const void *)((const uint16_t *)q_idx + qoff);
+      const void *kseq = (type == ORACLE_F32) ? (const void *)((const float *)k_idx + koff)
+                                              : (const void *)((const uint16_t *)k_idx + koff);
+      const int64_t out = ((int64_t)b * h_kv + r) * n_rows + i;
+      index_row(qrow, kseq, type, d_idx, n_blocks, p, block_size, top_k, scores, cand, bm,
+                sel + out * top_k);
+      if (bmax) memcpy(bmax + out * n_blocks, bm, sizeof(double) * (size_t)n_blocks);
+    }
+    free(scores);
+    free(bm);
+    free(cand);
+  }
+  if (failed) return -2;
+  if (!o) return 0;
+
+  /* main branch: one task per (b, h, row) */
+  const int64_t n_att_tasks = (int64_t)batch * h_q * n_rows;
+  const int64_t max_t = (int64_t)top_k * block_size;
+#pragma omp parallel
+  {
+    double *z = (double *)malloc(sizeof(double) * (size_t)max_t);
+    if (!z) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t task = 0; task < n_att_tasks; ++task) {
+      if (failed) continue;
+      const int i = (int)(task % n_rows);
+      const int h = (int)((task / n_rows) % h_q);
+      const int b = (int)(task / ((int64_t)n_rows * h_q));
+      const int r = h / group;
+      const int64_t t = rows[i], p = (int64_t)q_start + t;
+      const int64_t qoff = (((int64_t)b * h_q + h) * n_q + t) * d_h;
+      const int64_t kvoff = ((int64_t)b * h_kv + r) * (int64_t)n_k * d_h;
+      const size_t es = (type == ORACLE_F32) ? 4 : 2;
+      const void *qrow = (const char *)q + qoff * (int64_t)es;
+      const void *kp = (const char *)k + kvoff * (int64_t)es;
+      const void *vp = (const char *)v + kvoff * (int64_t)es;
+      const int32_t *s = sel + (((int64_t)b * h_kv + r) * n_rows + i) * top_k;
+      const int64_t out = ((int64_t)b * h_q + h) * n_rows + i;
+      double l;
+      attend_row(qrow, kp, vp, type, d_h, p, block_size, s, top_k, z, o + out * d_h, &l);
+      if (lse) lse[out] = l;
+    }
+    free(z);
+  }
+  return failed ? -2 : 0;
+}
+
+/* Threads the oracle will use when n_threads <= 0. */
+int msa_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

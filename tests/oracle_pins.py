@@ -1,0 +1,245 @@
+"""Pins for the fp64 oracle: checks against what the MSA definition and plain
+mathematics fix, none of which re-types the oracle's own code.
+
+Definitions pinned (page "MiniMax-M3: MSA 技术报告速读", section 核心机制):
+  index-branch token scores and causal block max-pool, the per-group TopK with
+  the local block forced in, and the main-branch sparse softmax attention.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError on a mismatch, so
+the same pins also run against deliberately broken oracle builds.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from types import SimpleNamespace
+
+import numpy as np
+import torch
+
+
+def shape(**kw):
+    base = dict(dtype="f32", batch=1, n_q=8, n_k=8, q_start=0, h_q=2, h_kv=1, d_h=4, d_idx=2,
+                block_size=2, top_k=2)
+    base.update(kw)
+    return SimpleNamespace(**base)
+
+
+def rand_inputs(w, seed, idx_values=(-2, 3), cont_idx=False):
+    """Small fp32 inputs: Gaussian q, k, v; integer (or Gaussian) index inputs."""
+    g = torch.Generator().manual_seed(seed)
+    B, R, H = w.batch, w.h_kv, w.h_q
+    out = dict(
+        q=torch.randn(B, H, w.n_q, w.d_h, generator=g),
+        k=torch.randn(B, R, w.n_k, w.d_h, generator=g),
+        v=torch.randn(B, R, w.n_k, w.d_h, generator=g),
+    )
+    if cont_idx:
+        out["q_idx"] = torch.randn(B, R, w.n_q, w.d_idx, generator=g)
+        out["k_idx"] = torch.randn(B, w.n_k, w.d_idx, generator=g)
+    else:
+        lo, hi = idx_values
+        out["q_idx"] = torch.randint(lo, hi, (B, R, w.n_q, w.d_idx), generator=g).float()
+        out["k_idx"] = torch.randint(lo, hi, (B, w.n_k, w.d_idx), generator=g).float()
+    return out
+
+
+def exact_block_max(w, inp):
+    """Causal block maxima in exact int64 arithmetic (integer-valued index inputs)."""
+    qi = inp["q_idx"].numpy().astype(np.int64)      # [B,R,n_q,d]
+    ki = inp["k_idx"].numpy().astype(np.int64)      # [B,n_k,d]
+    s = np.einsum("brtd,bjd->brtj", qi, ki).astype(np.float64)
+    pos = w.q_start + np.arange(w.n_q)
+    j = np.arange(w.n_k)
+    s[:, :, j[None, :] > pos[:, None]] = -np.inf     # keys after the query are invisible
+    nb = -(-w.n_k // w.block_size)
+    pad = nb * w.block_size - w.n_k
+    s = np.concatenate([s, np.full(s.shape[:-1] + (pad,), -np.inf)], axis=-1)
+    return s.reshape(s.shape[:-1] + (nb, w.block_size)).max(axis=-1)
+
+
+def visible_token_mask(w, sel):
+    """[B,R,n_q,n_k] bool: token j attended by row t of group r under selection ``sel``."""
+    B, R, n, k = sel.shape
+    mask = np.zeros((B, R, n, w.n_k), bool)
+    for b, r, t in itertools.product(range(B), range(R), range(n)):
+        p = w.q_start + t
+        for c in sel[b, r, t]:
+            if c >= 0:
+                lo, hi = c * w.block_size, min((c + 1) * w.block_size, p + 1)
+                mask[b, r, t, lo:hi] = True
+    return mask
+
+
+def sdpa_reference(w, inp, mask_brtj):
+    """Attention output and LSE with torch's SDPA (fp64) under a token mask, GQA via repeat."""
+    G = w.h_q // w.h_kv
+    q = inp["q"].double()
+    k = inp["k"].double().repeat_interleave(G, dim=1)
+    v = inp["v"].double().repeat_interleave(G, dim=1)
+    m = torch.from_numpy(mask_brtj).repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m)
+    z = (q @ k.transpose(-1, -2)) / math.sqrt(w.d_h)
+    lse = torch.logsumexp(z.masked_fill(~m, -math.inf), dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+def causal_mask(w):
+    pos = w.q_start + np.arange(w.n_q)
+    m = np.arange(w.n_k)[None, :] <= pos[:, None]
+    return np.broadcast_to(m, (w.batch, w.h_kv, w.n_q, w.n_k)).copy()
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_block_scores_exact(orc):
+    """Block scores equal exact integer causal block maxima (ragged last block, q_start>0)."""
+    for kw in (dict(batch=2, h_kv=3, h_q=3, n_q=37, n_k=37, d_idx=5, block_size=8, top_k=3),
+               dict(batch=1, h_kv=2, h_q=4, n_q=9, n_k=30, q_start=21, d_idx=3, block_size=4,
+                    top_k=2)):
+        w = shape(**kw)
+        inp = rand_inputs(w, seed=11)
+        got = orc.run(w, inp, attention=False, block_scores=True)["block_scores"]
+        want = exact_block_max(w, inp)
+        assert np.array_equal(got, want), "block scores differ from exact causal block maxima"
+
+
+def pin_topk_bruteforce(orc):
+    """Selections equal the unique subset no unselected block beats (exhaustive search).
+
+    Block c beats block u when its score is higher, or equal with a lower index.
+    The query's own block is always in, top_k counts it, and a query that sees
+    top_k blocks or fewer takes them all. Heavy ties come from index values in {-1,0,1}.
+    """
+    for top_k in (1, 2, 3, 4, 9, 10):
+        w = shape(batch=1, h_kv=2, h_q=2, n_q=18, n_k=18, d_idx=2, block_size=2, top_k=top_k)
+        inp = rand_inputs(w, seed=5 + top_k, idx_values=(-1, 2))
+        sel = orc.run(w, inp, attention=False)["sel"]
+        bm = exact_block_max(w, inp)
+        for r, t in itertools.product(range(w.h_kv), range(w.n_q)):
+            p = w.q_start + t
+            local = p // w.block_size
+            m = min(top_k - 1, local)
+            valid = []
+            for sub in itertools.combinations(range(local), m):
+                rest = [u for u in range(local) if u not in sub]
+                if all(bm[0, r, t, c] > bm[0, r, t, u] or
+                       (bm[0, r, t, c] == bm[0, r, t, u] and c < u) for c in sub for u in rest):
+                    valid.append(sub)
+            assert len(valid) == 1
+            want = sorted(valid[0] + (local,))
+            want += [-1] * (top_k - len(want))
+            assert list(sel[0, r, t]) == want, (top_k, r, t, list(sel[0, r, t]), want)
+
+
+def pin_dense_when_k_covers(orc):
+    """k >= number of blocks: the step equals dense causal GQA attention (torch SDPA, fp64)."""
+    for kw in (dict(batch=2, h_q=6, h_kv=3, n_q=40, n_k=40, d_h=8, d_idx=3, block_size=8,
+                    top_k=5),
+               dict(batch=1, h_q=4, h_kv=2, n_q=10, n_k=29, q_start=19, d_h=6, d_idx=2,
+                    block_size=4, top_k=8)):
+        w = shape(**kw)
+        inp = rand_inputs(w, seed=3)
+        out = orc.run(w, inp)
+        o, lse = sdpa_reference(w, inp, causal_mask(w))
+        assert np.allclose(out["o"], o, rtol=0, atol=1e-12)
+        assert np.allclose(out["lse"], lse, rtol=0, atol=1e-12)
+
+
+def pin_local_block_only(orc):
+    """k = 1: each query attends exactly to the visible part of its own block."""
+    w = shape(batch=1, h_q=4, h_kv=2, n_q=21, n_k=21, d_h=5, d_idx=2, block_size=4, top_k=1)
+    inp = rand_inputs(w, seed=4)
+    out = orc.run(w, inp)
+    pos = np.arange(w.n_q)[:, None]
+    j = np.arange(w.n_k)[None, :]
+    m = (j <= pos) & (j // w.block_size == pos // w.block_size)
+    o, lse = sdpa_reference(w, inp, np.broadcast_to(m, (1, 2, w.n_q, w.n_k)).copy())
+    assert np.allclose(out["o"], o, rtol=0, atol=1e-12)
+    assert np.allclose(out["lse"], lse, rtol=0, atol=1e-12)
+
+
+def pin_token_level(orc):
+    """block_size = 1: selection is the query token plus torch.topk of earlier token scores."""
+    w = shape(batch=1, h_q=2, h_kv=2, n_q=24, n_k=24, d_h=4, d_idx=3, block_size=1, top_k=5)
+    inp = rand_inputs(w, seed=9, cont_idx=True)   # continuous scores: no ties
+    out = orc.run(w, inp)
+    s = torch.einsum("brtd,bjd->brtj", inp["q_idx"].double(), inp["k_idx"].double())
+    want = np.full((1, 2, w.n_q, w.top_k), -1, np.int32)
+    for r, t in itertools.product(range(2), range(w.n_q)):
+        if t + 1 <= w.top_k:
+            chosen = list(range(t + 1))
+        else:
+            chosen = torch.topk(s[0, r, t, :t], w.top_k - 1).indices.tolist() + [t]
+        chosen = sorted(chosen)
+        want[0, r, t, :len(chosen)] = chosen
+    assert np.array_equal(out["sel"], want)
+    o, lse = sdpa_reference(w, inp, visible_token_mask(w, want))
+    assert np.allclose(out["o"], o, rtol=0, atol=1e-12)
+    assert np.allclose(out["lse"], lse, rtol=0, atol=1e-12)
+
+
+def pin_zero_query_closed_form(orc):
+    """q = 0: uniform weights, so lse = ln|T| with |T| = (min(k, b+1)-1)*bs + (p - b*bs + 1)
+    and o = mean of v over the attended tokens."""
+    w = shape(batch=1, h_q=2, h_kv=1, n_q=45, n_k=45, d_h=3, d_idx=2, block_size=4, top_k=3)
+    inp = rand_inputs(w, seed=6)
+    inp["q"].zero_()
+    out = orc.run(w, inp)
+    v = inp["v"].double().numpy()
+    mask = visible_token_mask(w, out["sel"])
+    for t in range(w.n_q):
+        p = t
+        b = p // w.block_size
+        n_tok = (min(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
+        assert mask[0, 0, t].sum() == n_tok
+        for h in range(w.h_q):
+            assert abs(out["lse"][0, h, t] - math.log(n_tok)) < 1e-12
+            assert np.allclose(out["o"][0, h, t], v[0, 0, mask[0, 0, t]].mean(axis=0), atol=1e-12)
+
+
+def pin_group_map_and_ones(orc):
+    """v = r + 1 on group r: head h must output h // (H_q/H_kv) + 1 exactly (softmax sums to 1)."""
+    w = shape(batch=2, h_q=6, h_kv=3, n_q=20, n_k=20, d_h=4, d_idx=2, block_size=4, top_k=2)
+    inp = rand_inputs(w, seed=8)
+    for r in range(w.h_kv):
+        inp["v"][:, r] = float(r + 1)
+    out = orc.run(w, inp)
+    G = w.h_q // w.h_kv
+    for h in range(w.h_q):
+        assert np.allclose(out["o"][:, h], h // G + 1, rtol=0, atol=1e-13)
+
+
+def pin_entry_point_consistency(orc):
+    """A chunk at q_start > 0 and a single decode row equal the matching rows of the full
+    prefill (causality is by absolute position)."""
+    w = shape(batch=2, h_q=4, h_kv=2, n_q=33, n_k=33, d_h=4, d_idx=3, block_size=4, top_k=3)
+    inp = rand_inputs(w, seed=10)
+    full = orc.run(w, inp, block_scores=True)
+    for start in (20, 32):
+        wc = shape(**{**vars(w), "n_q": w.n_q - start, "q_start": start})
+        ic = dict(inp)
+        ic["q"] = inp["q"][:, :, start:].contiguous()
+        ic["q_idx"] = inp["q_idx"][:, :, start:].contiguous()
+        part = orc.run(wc, ic, block_scores=True)
+        for key in ("sel", "block_scores", "o", "lse"):
+            a, b = part[key], full[key][:, :, start:]
+            assert np.array_equal(a, b), key
+
+
+def pin_bf16_storage_widening(orc):
+    """bf16 storage is widened exactly: bf16 inputs give bit-identical results to the same
+    values stored as fp32."""
+    w = shape(batch=1, h_q=4, h_kv=2, n_q=19, n_k=19, d_h=8, d_idx=4, block_size=4, top_k=3)
+    inp = rand_inputs(w, seed=12)
+    as_bf16 = {k: x.to(torch.bfloat16) for k, x in inp.items()}
+    as_f32 = {k: x.float() for k, x in as_bf16.items()}
+    a = orc.run(shape(**{**vars(w), "dtype": "bf16"}), as_bf16, block_scores=True)
+    b = orc.run(w, as_f32, block_scores=True)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+PINS = [pin_block_scores_exact, pin_topk_bruteforce, pin_dense_when_k_covers,
+        pin_local_block_only, pin_token_level, pin_zero_query_closed_form,
+        pin_group_map_and_ones, pin_entry_point_consistency, pin_bf16_storage_widening]
