@@ -1,0 +1,248 @@
+// msa_api.cpp -- the C ABI declared in include/msa.h: argument validation, workspace
+// sizing and kernel launches. Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "msa.h"
+#include "msa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return MSA_OK;
+}
+
+bool pow2_upto(int x, int hi) { return x >= 1 && x <= hi && (x & (x - 1)) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+long long n_blocks(const msa_shape &s) { return ((long long)s.n_k + s.block_size - 1) / s.block_size; }
+int cap_of(const msa_shape &s) { return s.kv_capacity ? s.kv_capacity : s.n_k; }
+
+// Checks shared by every entry point.
+int check_shape(const msa_shape *s) {
+  if (!s) return fail(MSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->n_q < 1 || s->n_k < 1 || s->q_start < 0)
+    return fail(MSA_ERR_INVALID_ARG, "batch, n_q, n_k must be >= 1 and q_start >= 0 (got %d, %d, %d, %d)",
+                s->batch, s->n_q, s->n_k, s->q_start);
+  if ((long long)s->q_start + s->n_q > s->n_k)
+    return fail(MSA_ERR_INVALID_ARG, "q_start + n_q (%lld) exceeds n_k (%d)",
+                (long long)s->q_start + s->n_q, s->n_k);
+  if (s->kv_capacity != 0 && s->kv_capacity < s->n_k)
+    return fail(MSA_ERR_INVALID_ARG, "kv_capacity (%d) is neither 0 nor >= n_k (%d)", s->kv_capacity, s->n_k);
+  if (s->h_kv < 1 || s->h_q < 1 || s->h_q % s->h_kv)
+    return fail(MSA_ERR_INVALID_ARG, "h_q (%d) must be a positive multiple of h_kv (%d)", s->h_q, s->h_kv);
+  if (s->top_k < 1) return fail(MSA_ERR_INVALID_ARG, "top_k must be >= 1 (got %d)", s->top_k);
+  if (s->block_size < 1) return fail(MSA_ERR_INVALID_ARG, "block_size must be >= 1");
+  if (s->dtype != MSA_F32 && s->dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "dtype %d is not MSA_F32 or MSA_BF16", s->dtype);
+  if (s->block_size != 32 && s->block_size != 64)
+    return fail(MSA_ERR_UNSUPPORTED, "block_size %d not in {32, 64}", s->block_size);
+  if (s->top_k > 64) return fail(MSA_ERR_UNSUPPORTED, "top_k %d > 64", s->top_k);
+  if (!pow2_upto(s->h_kv, 16)) return fail(MSA_ERR_UNSUPPORTED, "h_kv %d not in {1,2,4,8,16}", s->h_kv);
+  if (!pow2_upto(s->h_q / s->h_kv, 16))
+    return fail(MSA_ERR_UNSUPPORTED, "h_q / h_kv = %d not in {1,2,4,8,16}", s->h_q / s->h_kv);
+  return MSA_OK;
+}
+
+int topk_chunks(const msa_shape &s) {
+  if (s.top_k == 1) return 1;  // the local block alone: no ranking
+  // candidate blocks of the last row: its local block index
+  const long long last_local = ((long long)s.q_start + s.n_q - 1) / s.block_size;
+  const long long n = last_local < 1 ? 1 : (last_local + msa::TOPK_CHUNK - 1) / msa::TOPK_CHUNK;
+  return (int)n;
+}
+
+struct IndexWs {
+  size_t bmax, cand, total;
+};
+
+int index_ws(const msa_shape &s, bool with_bmax, IndexWs *w) {
+  const long long rows = (long long)s.batch * s.h_kv * s.n_q;
+  const int nch = topk_chunks(s);
+  if (nch > 1 && (long long)nch * (s.top_k - 1) > msa::TOPK_CHUNK)
+    return fail(MSA_ERR_UNSUPPORTED, "too many candidate blocks (%lld) for top_k %d",
+                ((long long)s.q_start + s.n_q - 1) / s.block_size, s.top_k);
+  w->bmax = with_bmax ? align_up((size_t)rows * (size_t)n_blocks(s) * sizeof(float)) : 0;
+  w->cand = nch > 1 ? align_up((size_t)rows * nch * (s.top_k - 1) * 4) : 0;
+  w->total = w->bmax + 2 * w->cand;
+  return MSA_OK;
+}
+
+int check_index_dims(const msa_shape &s) {
+  if (s.d_idx != 32 && s.d_idx != 64) return fail(MSA_ERR_UNSUPPORTED, "d_idx %d not in {32, 64}", s.d_idx);
+  return MSA_OK;
+}
+
+int check_attn_dims(const msa_shape &s) {
+  if (s.d_h != 64 && s.d_h != 128) return fail(MSA_ERR_UNSUPPORTED, "d_h %d not in {64, 128}", s.d_h);
+  return MSA_OK;
+}
+
+int decode_splits(const msa_shape &s) { return s.top_k; }  // one selected block per split
+
+size_t attn_decode_ws(const msa_shape &s) {
+  const size_t parts = (size_t)s.batch * s.h_q * decode_splits(s);
+  return align_up(parts * s.d_h * sizeof(float)) + align_up(parts * 2 * sizeof(float));
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int key_chunk_prefill(const msa_shape &s) {
+  const long long tq = 256 / s.h_kv;
+  const long long tiles = ((long long)s.n_q + tq - 1) / tq * s.batch;
+  const long long avg_keys = (long long)s.q_start + s.n_q / 2 + 1;
+  int kc = 8192;
+  while (kc > 512 && tiles * ((avg_keys + kc - 1) / kc) < 4096) kc /= 2;
+  return kc;
+}
+
+int key_chunk_decode(const msa_shape &s) {
+  const long long keys = (long long)s.q_start + 1;
+  int kc = 4096;
+  while (kc > 256 && s.batch * ((keys + kc - 1) / kc) < 2048) kc /= 2;
+  return kc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msa_abi_version(void) { return 1; }
+
+const char *msa_last_error(void) { return g_error.c_str(); }
+
+int msa_index_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_index_dims(*shape))) return rc;
+  if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  IndexWs w;
+  if ((rc = index_ws(*shape, true, &w))) return rc;
+  *bytes = w.total;
+  return ok();
+}
+
+int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx, int32_t *sel,
+                   float *block_scores, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if ((rc = check_index_dims(s))) return rc;
+  if (!q_idx || !k_idx || !sel) return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx and sel must be non-NULL");
+  IndexWs w;
+  if ((rc = index_ws(s, block_scores == nullptr, &w))) return rc;
+  if (w.total && (!workspace || workspace_bytes < w.total))
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
+  float *bmax = block_scores ? block_scores : reinterpret_cast<float *>(ws);
+  const long long rows = (long long)s.batch * s.h_kv * s.n_q;
+  hipError_t e;
+  if (block_scores) {
+    e = msa::launch_fill(block_scores, (size_t)rows * (size_t)n_blocks(s), -INFINITY, st);
+    if (e != hipSuccess) return hip_fail(e, "block score fill");
+  }
+  msa::IndexArgs ia{q_idx, k_idx, bmax, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
+                    (int)n_blocks(s), cap_of(s), 0};
+  if (s.n_q == 1) {
+    ia.key_chunk = key_chunk_decode(s);
+    e = msa::launch_index_decode(ia, s.dtype, s.d_idx, s.block_size, st);
+  } else {
+    ia.key_chunk = key_chunk_prefill(s);
+    e = msa::launch_index_prefill(ia, s.dtype, s.d_idx, s.block_size, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "index kernel launch");
+  msa::TopkArgs ta{bmax, sel,
+                   reinterpret_cast<uint32_t *>(ws + w.bmax),
+                   reinterpret_cast<int32_t *>(ws + w.bmax + w.cand),
+                   s.batch, s.n_q, s.q_start, s.h_kv, (int)n_blocks(s), s.block_size, s.top_k,
+                   topk_chunks(s)};
+  e = msa::launch_topk(ta, st);
+  if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+  return ok();
+}
+
+int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_attn_dims(*shape))) return rc;
+  if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  const bool decode = shape->n_q == 1 && shape->q_start == shape->n_k - 1;
+  *bytes = decode ? attn_decode_ws(*shape) : 0;
+  return ok();
+}
+
+int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k, const void *v,
+                            const int32_t *sel, void *o, float *lse, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if ((rc = check_attn_dims(s))) return rc;
+  if (!q || !k || !v || !sel || !o) return fail(MSA_ERR_INVALID_ARG, "q, k, v, sel and o must be non-NULL");
+  const int G = s.h_q / s.h_kv;
+  if (s.top_k * (16 / G) > 128)
+    return fail(MSA_ERR_UNSUPPORTED, "top_k * (16 / (h_q / h_kv)) = %d exceeds 128", s.top_k * (16 / G));
+  msa::AttnArgs a{q, k, v, sel, o, lse, nullptr, nullptr, s.batch, s.n_q, s.n_k, s.q_start,
+                  s.h_q, s.h_kv, s.block_size, s.top_k, cap_of(s), 0, 0,
+                  (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};
+  hipError_t e = msa::launch_attn_prefill(a, s.dtype, s.d_h, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  return ok();
+}
+
+int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *sel, void *o, float *lse,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if ((rc = check_attn_dims(s))) return rc;
+  if (s.n_q != 1 || s.q_start != s.n_k - 1)
+    return fail(MSA_ERR_INVALID_ARG, "decode needs n_q == 1 and q_start == n_k - 1 (got %d, %d, n_k %d)",
+                s.n_q, s.q_start, s.n_k);
+  if (!q || !k_cache || !v_cache || !sel || !o)
+    return fail(MSA_ERR_INVALID_ARG, "q, k_cache, v_cache, sel and o must be non-NULL");
+  const size_t need = attn_decode_ws(s);
+  if (!workspace || workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const int S = decode_splits(s);
+  const size_t parts = (size_t)s.batch * s.h_q * S;
+  unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
+  msa::AttnArgs a{q, k_cache, v_cache, sel, o, lse,
+                  reinterpret_cast<float *>(ws),
+                  reinterpret_cast<float *>(ws + align_up(parts * s.d_h * sizeof(float))),
+                  s.batch, 1, s.n_k, s.q_start, s.h_q, s.h_kv, s.block_size, s.top_k, cap_of(s),
+                  S, (s.top_k + S - 1) / S,
+                  (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};
+  hipError_t e = msa::launch_attn_decode(a, s.dtype, s.d_h, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  return ok();
+}
+
+}  // extern "C"

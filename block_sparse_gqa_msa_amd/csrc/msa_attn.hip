@@ -1,0 +1,399 @@
+// msa_attn.hip -- main branch: exact softmax attention over the selected blocks.
+//
+// Definition ("MiniMax-M3: MSA 技术报告速读", section 核心机制, main-branch equation):
+// O^(h)_t = softmax(q_h k_T^T / sqrt(d_h)) v_T, T = visible tokens (j <= p) of the blocks
+// the row's group selected; every head of a group shares the group's selection.
+//
+// A wave owns 16 (query, head) rows: 16/G consecutive queries x the G heads of one group.
+// It walks the union of its queries' selections in ascending block order; rows whose query
+// did not pick the current block are masked out of it. Per block:
+//   S^T = K_blk Q^T            (keys down the accumulator rows, one row per lane column)
+//   online softmax in the log2 domain (per-lane row = lane % 16, reductions over 4 groups)
+//   O^T += V_blk^T P^T         (P^T comes straight from the S^T accumulators: lane group g
+//                               feeds keys {4g..4g+3} of two adjacent 16-key tiles, and the
+//                               V^T fragment is read from LDS with the same key order)
+// V is staged transposed in a wave-private LDS region; K fragments are read directly.
+//
+// Decode splits the selected blocks of one (sequence, group) over several waves, each
+// writing (unnormalised O, running max, running sum); a second kernel merges them with
+// log-sum-exp weights. The split is fixed on the host, so no atomics are used.
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+template <typename E, int DH, int BS>
+struct VStage {
+  static constexpr int ES = (int)sizeof(E);
+  static constexpr int ROW = BS * ES + (ES == 2 ? 8 : 16);  // bytes per d-row of V^T
+  static constexpr int BYTES = DH * ROW;
+};
+
+template <typename E, int DH, int BS>
+struct RowState {
+  static constexpr int DT = DH / 16;
+  f32x4 o[DT];
+  float m;  // running max, log2 units
+  float l;  // running sum of 2^(z - m)
+};
+
+// Stage V rows [kb, kb+BS) transposed into LDS: vt[d][key]. bf16 packs key pairs into dwords.
+template <int DH, int BS>
+__device__ __forceinline__ void stage_v(const bf16_t *vp, long kb, int n_k, unsigned char *vt) {
+  constexpr int PAIRS = BS / 2, SEGS = 64 / PAIRS, DSEG = DH / SEGS, PIECES = DSEG / 8;
+  constexpr int ROW = VStage<bf16_t, DH, BS>::ROW;
+  const int lane = lane_id(), kp = lane % PAIRS, seg = lane / PAIRS;
+  const long j0 = kb + 2 * kp, j1 = j0 + 1;
+  u32x4 a[PIECES], b[PIECES];
+#pragma unroll
+  for (int i = 0; i < PIECES; ++i) {
+    const int d0 = seg * DSEG + i * 8;
+    a[i] = j0 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
+    b[i] = j1 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < PIECES; ++i) {
+    const int d0 = seg * DSEG + i * 8;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t x = a[i][e], y = b[i][e];
+      // element 2e is the low half, 2e+1 the high half of dword e
+      *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e) * ROW + kp * 4) = (x & 0xffffu) | (y << 16);
+      *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e + 1) * ROW + kp * 4) = (x >> 16) | (y & 0xffff0000u);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+template <int DH, int BS>
+__device__ __forceinline__ void stage_v(const float *vp, long kb, int n_k, unsigned char *vt) {
+  constexpr int SEGS = 64 / BS, DSEG = DH / SEGS, PIECES = DSEG / 4;
+  constexpr int ROW = VStage<float, DH, BS>::ROW;
+  const int lane = lane_id(), key = lane % BS, seg = lane / BS;
+  const long j = kb + key;
+  f32x4 a[PIECES];
+#pragma unroll
+  for (int i = 0; i < PIECES; ++i)
+    a[i] = j < n_k ? *reinterpret_cast<const f32x4 *>(vp + j * DH + seg * DSEG + i * 4)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < PIECES; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      *reinterpret_cast<float *>(vt + (seg * DSEG + i * 4 + e) * ROW + key * 4) = a[i][e];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// V^T fragment for d-row d and 32-key step ks: keys 32ks+4g+0..3 then 32ks+16+4g+0..3.
+__device__ __forceinline__ bf16x8 vt_frag(const unsigned char *row, int ks, int g, const bf16_t *) {
+  const u32x2 lo = *reinterpret_cast<const u32x2 *>(row + (32 * ks + 4 * g) * 2);
+  const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + (32 * ks + 16 + 4 * g) * 2);
+  return __builtin_bit_cast(bf16x8, (u32x4{lo[0], lo[1], hi[0], hi[1]}));
+}
+__device__ __forceinline__ f32x8 vt_frag(const unsigned char *row, int ks, int g, const float *) {
+  const f32x4 lo = *reinterpret_cast<const f32x4 *>(row + (32 * ks + 4 * g) * 4);
+  const f32x4 hi = *reinterpret_cast<const f32x4 *>(row + (32 * ks + 16 + 4 * g) * 4);
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// P^T fragment for key step ks from the probability tiles 2ks and 2ks+1.
+__device__ __forceinline__ bf16x8 pt_frag(f32x4 a, f32x4 b, const bf16_t *) {
+  return __builtin_bit_cast(bf16x8, (u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                           pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])}));
+}
+__device__ __forceinline__ f32x8 pt_frag(f32x4 a, f32x4 b, const float *) {
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// One selected block for the wave's 16 rows. `active`: this lane's row takes part;
+// p_row: its absolute position.
+template <typename E, int DH, int BS>
+__device__ __forceinline__ void attend_block(RowState<E, DH, BS> &st,
+                                             const typename Frag<E>::type (&bq)[DH / 32],
+                                             const E *kp, const E *vp, long kb, int n_k,
+                                             bool active, long p_row, float scale_log2,
+                                             unsigned char *vt) {
+  using F = typename Frag<E>::type;
+  constexpr int DC = DH / 32, KTN = BS / 16, DT = DH / 16;
+  const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
+
+  f32x4 s[KTN];
+#pragma unroll
+  for (int kt = 0; kt < KTN; ++kt) {
+    const long j = kb + kt * 16 + c16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      const F a = j < n_k ? load_frag(kp + j * DH + dc * 32 + g * 8) : zero_frag(kp);
+      acc = mfma_chunk(a, bq[dc], acc);
+    }
+    s[kt] = acc;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < KTN; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long j = kb + kt * 16 + g * 4 + i;
+      const float z = (active && j <= p_row) ? s[kt][i] * scale_log2 : -INFINITY;
+      s[kt][i] = z;
+      mx = fmaxf(mx, z);
+    }
+  mx = max_groups(mx);
+  const float m_new = fmaxf(st.m, mx);
+  const float msub = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2f(st.m - msub);
+  float rs = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < KTN; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pz = exp2f(s[kt][i] - msub);
+      s[kt][i] = pz;
+      rs += pz;
+    }
+  rs = sum_groups(rs);
+  st.l = st.l * alpha + rs;
+  st.m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.o[dt] *= alpha;
+
+  stage_v<DH, BS>(vp, kb, n_k, vt);
+  constexpr int ROW = VStage<E, DH, BS>::ROW;
+#pragma unroll
+  for (int ks = 0; ks < BS / 32; ++ks) {
+    const F b = pt_frag(s[2 * ks], s[2 * ks + 1], kp);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const F a = vt_frag(vt + (dt * 16 + c16) * ROW, ks, g, kp);
+      st.o[dt] = mfma_chunk(a, b, st.o[dt]);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+template <typename E>
+__device__ __forceinline__ void store4(E *dst, f32x4 v, float scale);
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t *dst, f32x4 v, float scale) {
+  *reinterpret_cast<u32x2 *>(dst) =
+      u32x2{pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale)};
+}
+template <>
+__device__ __forceinline__ void store4<float>(float *dst, f32x4 v, float scale) {
+  *reinterpret_cast<f32x4 *>(dst) = v * scale;
+}
+
+// Prefill. Grid: x = groups of 4 waves over (b, r, query group); block = 256 threads.
+template <typename E, int DH, int BS>
+__global__ __launch_bounds__(256) void attn_prefill(AttnArgs a, int log2g) {
+  using F = typename Frag<E>::type;
+  using VS = VStage<E, DH, BS>;
+  constexpr int DC = DH / 32, DT = DH / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char s_vt[4][VS::BYTES];
+  __shared__ int32_t s_sel[4][128];
+
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int G = 1 << log2g, QPW = 16 >> log2g, R = a.h_kv, k = a.top_k;
+  const int n_qg = (a.n_q + QPW - 1) / QPW;
+  const long wid = (long)blockIdx.x * 4 + w;
+  if (wid >= (long)a.batch * R * n_qg) return;
+  const int qg = (int)(wid % n_qg);
+  const int r = (int)((wid / n_qg) % R);
+  const int b = (int)(wid / ((long)n_qg * R));
+
+  const int qrow = c16 >> log2g, h = r * G + (c16 & (G - 1));
+  const int t = qg * QPW + qrow;
+  const bool row_valid = (c16 < QPW * G) && t < a.n_q;
+  const long p_row = (long)a.q_start + t;
+
+  const E *q = reinterpret_cast<const E *>(a.q);
+  F bq[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    bq[dc] = row_valid ? load_frag(q + (((long)b * a.h_q + h) * a.n_q + t) * DH + dc * 32 + g * 8)
+                       : zero_frag(q);
+  const int32_t *selp = a.sel + (((long)b * R + r) * a.n_q + (long)qg * QPW) * k;
+  for (int e = lane; e < QPW * k; e += 64)
+    s_sel[w][e] = (qg * QPW + e / k < a.n_q) ? selp[e] : -1;
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+  const long plane = ((long)b * R + r) * (long)a.cap * DH;
+  const E *kp = reinterpret_cast<const E *>(a.k) + plane;
+  const E *vp = reinterpret_cast<const E *>(a.v) + plane;
+  RowState<E, DH, BS> st;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  int ptr = 0;  // lanes < QPW: cursor into their query's (ascending) selection
+  for (;;) {
+    int cur = 0x7fffffff;
+    if (lane < QPW && ptr < k) {
+      const int v = s_sel[w][lane * k + ptr];
+      if (v >= 0) cur = v;
+    }
+    const int c = wave_min_i32(cur);
+    if (c == 0x7fffffff) break;
+    const bool mine = lane < QPW && cur == c;
+    const uint64_t act = ballot(mine);
+    if (mine) ++ptr;
+    const bool active = row_valid && ((act >> qrow) & 1ull);
+    attend_block<E, DH, BS>(st, bq, kp, vp, (long)c * BS, a.n_k, active, p_row, a.scale_log2,
+                            s_vt[w]);
+  }
+  if (row_valid) {
+    const float inv = 1.f / st.l;
+    E *o = reinterpret_cast<E *>(a.o) + (((long)b * a.h_q + h) * a.n_q + t) * DH;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) store4<E>(o + dt * 16 + g * 4, st.o[dt], inv);
+    if (a.lse && g == 0)
+      a.lse[((long)b * a.h_q + h) * a.n_q + t] = (st.m + __log2f(st.l)) * 0.69314718055994531f;
+  }
+}
+
+// Decode, split pass. Grid: x = groups of 4 waves over (b, r, split).
+template <typename E, int DH, int BS>
+__global__ __launch_bounds__(256) void attn_decode_split(AttnArgs a, int log2g) {
+  using F = typename Frag<E>::type;
+  using VS = VStage<E, DH, BS>;
+  constexpr int DC = DH / 32, DT = DH / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char s_vt[4][VS::BYTES];
+
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int G = 1 << log2g, R = a.h_kv, S = a.splits;
+  const long wid = (long)blockIdx.x * 4 + w;
+  if (wid >= (long)a.batch * R * S) return;
+  const int sp = (int)(wid % S);
+  const int r = (int)((wid / S) % R);
+  const int b = (int)(wid / ((long)S * R));
+  const bool row_valid = c16 < G;
+  const int h = r * G + (c16 & (G - 1));
+  const long p_row = (long)a.q_start;
+
+  const E *q = reinterpret_cast<const E *>(a.q);
+  F bq[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    bq[dc] = row_valid ? load_frag(q + ((long)b * a.h_q + h) * DH + dc * 32 + g * 8) : zero_frag(q);
+  const long plane = ((long)b * R + r) * (long)a.cap * DH;
+  const E *kp = reinterpret_cast<const E *>(a.k) + plane;
+  const E *vp = reinterpret_cast<const E *>(a.v) + plane;
+  const int32_t *selp = a.sel + ((long)b * R + r) * a.top_k;
+  RowState<E, DH, BS> st;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const int e0 = sp * a.blocks_per_split, e1 = min(e0 + a.blocks_per_split, a.top_k);
+  for (int e = e0; e < e1; ++e) {
+    const int c = selp[e];
+    if (c < 0) continue;  // wave-uniform
+    attend_block<E, DH, BS>(st, bq, kp, vp, (long)c * BS, a.n_k, row_valid, p_row, a.scale_log2,
+                            s_vt[w]);
+  }
+  if (row_valid) {
+    const long pr = ((long)b * a.h_q + h) * S + sp;
+    float *po = a.part_o + pr * DH;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4 *>(po + dt * 16 + g * 4) = st.o[dt];
+    if (g == 0) {
+      a.part_ml[pr * 2] = st.m;
+      a.part_ml[pr * 2 + 1] = st.l;
+    }
+  }
+}
+
+// Decode, merge pass: one wave per (b, h); lanes cover d.
+template <typename E, int DH>
+__global__ __launch_bounds__(256) void attn_decode_merge(AttnArgs a) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long bh = (long)blockIdx.x * 4 + w;
+  if (bh >= (long)a.batch * a.h_q) return;
+  const int S = a.splits;
+  const float *ml = a.part_ml + bh * S * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f;
+  constexpr int PER = DH / 64;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float ms = ml[2 * s];
+    if (ms == -INFINITY) continue;
+    const float wgt = exp2f(ms - M);
+    L += wgt * ml[2 * s + 1];
+    const float *po = a.part_o + (bh * S + s) * DH;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += wgt * po[lane + 64 * i];
+  }
+  const float inv = 1.f / L;
+  E *o = reinterpret_cast<E *>(a.o) + bh * DH;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const float x = acc[i] * inv;
+    if constexpr (sizeof(E) == 2) {
+      reinterpret_cast<uint16_t *>(o)[lane + 64 * i] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+    } else {
+      reinterpret_cast<float *>(o)[lane + 64 * i] = x;
+    }
+  }
+  if (a.lse && lane == 0) a.lse[bh] = (M + __log2f(L)) * 0.69314718055994531f;
+}
+
+template <typename E, int DH>
+hipError_t prefill_t(const AttnArgs &a, int bs, int log2g, hipStream_t s) {
+  const int QPW = 16 >> log2g;
+  const long waves = (long)a.batch * a.h_kv * ((a.n_q + QPW - 1) / QPW);
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (bs == 32)
+    hipLaunchKernelGGL((attn_prefill<E, DH, 32>), grid, dim3(256), 0, s, a, log2g);
+  else
+    hipLaunchKernelGGL((attn_prefill<E, DH, 64>), grid, dim3(256), 0, s, a, log2g);
+  return hipGetLastError();
+}
+
+template <typename E, int DH>
+hipError_t decode_t(const AttnArgs &a, int bs, int log2g, hipStream_t s) {
+  const long waves = (long)a.batch * a.h_kv * a.splits;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  if (bs == 32)
+    hipLaunchKernelGGL((attn_decode_split<E, DH, 32>), grid, dim3(256), 0, s, a, log2g);
+  else
+    hipLaunchKernelGGL((attn_decode_split<E, DH, 64>), grid, dim3(256), 0, s, a, log2g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long mw = (long)a.batch * a.h_q;
+  hipLaunchKernelGGL((attn_decode_merge<E, DH>), dim3((unsigned)((mw + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+int ilog2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill(const AttnArgs &a, int dtype, int d_h, hipStream_t s) {
+  const int lg = ilog2(a.h_q / a.h_kv);
+  if (dtype == 0) return d_h == 64 ? prefill_t<float, 64>(a, a.block_size, lg, s)
+                                   : prefill_t<float, 128>(a, a.block_size, lg, s);
+  return d_h == 64 ? prefill_t<bf16_t, 64>(a, a.block_size, lg, s)
+                   : prefill_t<bf16_t, 128>(a, a.block_size, lg, s);
+}
+
+hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s) {
+  const int lg = ilog2(a.h_q / a.h_kv);
+  if (dtype == 0) return d_h == 64 ? decode_t<float, 64>(a, a.block_size, lg, s)
+                                   : decode_t<float, 128>(a, a.block_size, lg, s);
+  return d_h == 64 ? decode_t<bf16_t, 64>(a, a.block_size, lg, s)
+                   : decode_t<bf16_t, 128>(a, a.block_size, lg, s);
+}
+
+}  // namespace msa

@@ -1,0 +1,263 @@
+// msa_index.hip -- index branch: token scores q_idx . k_idx on the matrix cores with the
+// causal block max-pool fused into the epilogue.
+//
+// Definition ("MiniMax-M3: MSA 技术报告速读", section 核心机制, index-branch score and
+// max-pool equation): M[b,r,t,c] = max over keys j of block c with j <= p(t) of
+// q_idx[b,r,t,:] . k_idx[b,j,:]. The 1/sqrt(d_idx) factor is positive and left out.
+//
+// The product is computed transposed, S^T = K_idx * Q_idx^T, so that the keys of a block
+// run down the accumulator rows each lane holds: pooling is an in-lane max over the
+// lane's rows followed by two lane-group swaps, not a shuffle reduction over keys.
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+constexpr int KT = 64;        // keys per key tile: four 16-row MFMA tiles
+constexpr int WG_COLS = 256;  // (group, query) columns per prefill workgroup: 4 waves x 64
+
+template <typename E, int DI>
+struct KTile {
+  static constexpr int ROW = DI * (int)sizeof(E) + 16;          // padded LDS row (bytes)
+  static constexpr int PER_ROW = DI * (int)sizeof(E) / 16;      // 16-byte pieces per key
+  static constexpr int PIECES = KT * PER_ROW;
+  static constexpr int PER_THREAD = PIECES / 256;
+};
+
+__global__ void fill_kernel(float *p, size_t n, float value) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+// Prefill / chunked prefill. Grid: x = key chunk, y = query tile, z = sequence.
+// A workgroup owns TQ = 256 / R query rows for all R groups (256 columns; wave w takes
+// columns 64w..64w+63 as four 16-column N-tiles) and one chunk of keys. The k_idx tile
+// is staged once in LDS (double-buffered) and feeds every group: the index key is shared.
+template <typename E, int DI, int BS>
+__global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
+  using L = KTile<E, DI>;
+  using F = typename Frag<E>::type;
+  constexpr int DC = DI / 32;
+  constexpr int BPT = KT / BS;  // blocks per key tile
+  constexpr int MPB = BS / 16;  // 16-key row tiles per block
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][KT * L::ROW];
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int R = a.h_kv, TQ = WG_COLS / R;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * TQ;
+  const int t_last = min(t0 + TQ, a.n_q) - 1;
+  const long p_first = (long)a.q_start + t0, p_last = (long)a.q_start + t_last;
+  const long k_begin = (long)blockIdx.x * a.key_chunk;
+  if (k_begin > p_last) return;  // uniform over the workgroup
+  const long k_end = min(k_begin + (long)a.key_chunk, p_last + 1);
+  const int n_tiles = (int)((k_end - k_begin + KT - 1) / KT);
+
+  // B operand: q_idx of this lane's four columns (column = lane % 16 of each N-tile).
+  const E *qi = reinterpret_cast<const E *>(a.q_idx);
+  F bq[4][DC];
+  long pcol[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int col = w * 64 + nt * 16 + c16, r = col / TQ, t = t0 + col % TQ;
+    pcol[nt] = (long)a.q_start + t;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      bq[nt][dc] = (t < a.n_q)
+                       ? load_frag(qi + (((long)b * R + r) * a.n_q + t) * DI + dc * 32 + g * 8)
+                       : zero_frag(qi);
+  }
+  // This lane writes the pooled value of column (nt = g, c16).
+  const int col_out = w * 64 + g * 16 + c16;
+  const int r_out = col_out / TQ, t_out = t0 + col_out % TQ;
+  float *out_row = a.bmax + (((long)b * R + r_out) * a.n_q + t_out) * (long)a.n_blocks;
+  const bool out_ok = t_out < a.n_q;
+
+  const unsigned char *kbase =
+      reinterpret_cast<const unsigned char *>(a.k_idx) + (long)b * a.cap * DI * (long)sizeof(E);
+  u32x4 pre[L::PER_THREAD];
+  auto fetch = [&](int tile) {
+    const long k0 = k_begin + (long)tile * KT;
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i) {
+      const int pc = tid + i * 256, key = pc / L::PER_ROW, off = pc % L::PER_ROW;
+      const long j = k0 + key;
+      pre[i] = (j < a.n_k) ? *reinterpret_cast<const u32x4 *>(kbase + j * DI * (long)sizeof(E) + off * 16)
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i) {
+      const int pc = tid + i * 256, key = pc / L::PER_ROW, off = pc % L::PER_ROW;
+      *reinterpret_cast<u32x4 *>(&lds[buf][key * L::ROW + off * 16]) = pre[i];
+    }
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < n_tiles) fetch(tile + 1);
+    const long k0 = k_begin + (long)tile * KT;
+    const bool need_mask = k0 + KT - 1 > p_first;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      F af[DC];
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        af[dc] = load_frag(reinterpret_cast<const E *>(
+            &lds[buf][(mt * 16 + c16) * L::ROW + (dc * 32 + g * 8) * (int)sizeof(E)]));
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) c = mfma_chunk(af[dc], bq[nt][dc], c);
+        acc[mt][nt] = c;
+      }
+    }
+#pragma unroll
+    for (int blk = 0; blk < BPT; ++blk) {
+      float outv = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int mm = 0; mm < MPB; ++mm) {
+          const int mt = blk * MPB + mm;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float s = acc[mt][nt][i];
+            if (need_mask && k0 + mt * 16 + g * 4 + i > pcol[nt]) s = -INFINITY;
+            m = fmaxf(m, s);
+          }
+        }
+        m = max_groups(m);
+        outv = (g == nt) ? m : outv;
+      }
+      const long c = k0 / BS + blk;
+      if (out_ok && c < a.n_blocks) out_row[c] = outv;
+    }
+    if (tile + 1 < n_tiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// Decode: one query row per sequence (all R groups in one 16-column N-tile). Each wave
+// streams its own run of keys straight from HBM; the sequence's keys are split over many
+// workgroups so the stream fills the chip. Grid: x = key chunk, z = sequence.
+template <typename E, int DI, int BS>
+__global__ __launch_bounds__(256) void index_pool_decode(IndexArgs a) {
+  using F = typename Frag<E>::type;
+  constexpr int DC = DI / 32;
+  constexpr int BPT = KT / BS;
+  constexpr int MPB = BS / 16;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int R = a.h_kv, b = blockIdx.z;
+  const long p = a.q_start;
+  const int sub = a.key_chunk / 4;
+  const long k_begin = (long)blockIdx.x * a.key_chunk + (long)w * sub;
+  if (k_begin > p) return;  // per wave; this kernel has no barrier
+  const long k_end = min(k_begin + (long)sub, p + 1);
+
+  const E *qi = reinterpret_cast<const E *>(a.q_idx);
+  const E *ki = reinterpret_cast<const E *>(a.k_idx) + (long)b * a.cap * DI;
+  F bq[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    bq[dc] = (c16 < R) ? load_frag(qi + (((long)b * R + c16) * a.n_q) * DI + dc * 32 + g * 8)
+                       : zero_frag(qi);
+  float *out_row = a.bmax + ((long)b * R + c16) * a.n_q * (long)a.n_blocks;
+
+  for (long k0 = k_begin; k0 < k_end; k0 += KT) {
+    F af[4][DC];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const long j = k0 + mt * 16 + c16;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        af[mt][dc] = (j < a.n_k) ? load_frag(ki + j * DI + dc * 32 + g * 8) : zero_frag(ki);
+    }
+    const bool need_mask = k0 + KT - 1 > p;
+#pragma unroll
+    for (int blk = 0; blk < BPT; ++blk) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int mm = 0; mm < MPB; ++mm) {
+        const int mt = blk * MPB + mm;
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) c = mfma_chunk(af[mt][dc], bq[dc], c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = c[i];
+          if (need_mask && k0 + mt * 16 + g * 4 + i > p) s = -INFINITY;
+          m = fmaxf(m, s);
+        }
+      }
+      m = max_groups(m);
+      const long cb = k0 / BS + blk;
+      if (g == 0 && c16 < R && cb < a.n_blocks) out_row[cb] = m;
+    }
+  }
+}
+
+template <typename E, int DI, int BS>
+hipError_t launch_prefill_t(const IndexArgs &a, hipStream_t s) {
+  const int TQ = WG_COLS / a.h_kv;
+  const long keys = (long)a.q_start + a.n_q;  // last position + 1
+  dim3 grid((unsigned)((keys + a.key_chunk - 1) / a.key_chunk), (unsigned)((a.n_q + TQ - 1) / TQ),
+            (unsigned)a.batch);
+  hipLaunchKernelGGL((index_pool_prefill<E, DI, BS>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename E, int DI, int BS>
+hipError_t launch_decode_t(const IndexArgs &a, hipStream_t s) {
+  const long keys = (long)a.q_start + 1;
+  dim3 grid((unsigned)((keys + a.key_chunk - 1) / a.key_chunk), 1, (unsigned)a.batch);
+  hipLaunchKernelGGL((index_pool_decode<E, DI, BS>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t pick(const IndexArgs &a, int d_idx, int bs, bool decode, hipStream_t s) {
+#define MSA_CASE(DI, BS)                                                             \
+  if (d_idx == DI && bs == BS)                                                       \
+    return decode ? launch_decode_t<E, DI, BS>(a, s) : launch_prefill_t<E, DI, BS>(a, s);
+  MSA_CASE(32, 32)
+  MSA_CASE(32, 64)
+  MSA_CASE(64, 32)
+  MSA_CASE(64, 64)
+#undef MSA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fill(float *p, size_t n, float value, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_prefill(const IndexArgs &a, int dtype, int d_idx, int block_size,
+                                hipStream_t s) {
+  return dtype == 0 ? pick<float>(a, d_idx, block_size, false, s)
+                    : pick<bf16_t>(a, d_idx, block_size, false, s);
+}
+
+hipError_t launch_index_decode(const IndexArgs &a, int dtype, int d_idx, int block_size,
+                               hipStream_t s) {
+  return dtype == 0 ? pick<float>(a, d_idx, block_size, true, s)
+                    : pick<bf16_t>(a, d_idx, block_size, true, s);
+}
+
+}  // namespace msa

@@ -1,0 +1,54 @@
+// msa_internal.hpp -- launchers shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct IndexArgs {
+  const void *q_idx;  // [B, R, n_q, DI]
+  const void *k_idx;  // [B, cap, DI]
+  float *bmax;        // [B, R, n_q, n_blocks]
+  int batch, n_q, n_k, q_start, h_kv, n_blocks, cap;
+  int key_chunk;      // keys per workgroup (multiple of 64)
+};
+
+struct TopkArgs {
+  const float *bmax;   // [B, R, n_q, n_blocks]
+  int32_t *sel;        // [B, R, n_q, k]
+  uint32_t *cand_key;  // [problems, n_chunks, k-1]  (two-level path only)
+  int32_t *cand_idx;   // [problems, n_chunks, k-1]
+  int batch, n_q, q_start, h_kv, n_blocks, block_size, top_k;
+  int n_chunks;        // chunks of TOPK_CHUNK blocks for the largest problem
+};
+
+struct AttnArgs {
+  const void *q;       // [B, H, n_q, DH]
+  const void *k;       // [B, R, cap, DH]
+  const void *v;       // [B, R, cap, DH]
+  const int32_t *sel;  // [B, R, n_q, top_k]
+  void *o;             // [B, H, n_q, DH]
+  float *lse;          // [B, H, n_q] or null
+  float *part_o;       // decode partials [B, H, S, DH]
+  float *part_ml;      // decode partials [B, H, S, 2] (max in log2 units, sum)
+  int batch, n_q, n_k, q_start, h_q, h_kv, block_size, top_k, cap;
+  int splits;          // decode: number of splits S
+  int blocks_per_split;
+  float scale_log2;    // log2(e) / sqrt(DH)
+};
+
+constexpr int TOPK_CHUNK = 2048;  // candidate blocks one wave ranks at a time
+
+// Each launcher validates nothing (the C-ABI layer did) and returns the launch status.
+hipError_t launch_fill(float *p, size_t n, float value, hipStream_t s);
+hipError_t launch_index_prefill(const IndexArgs &a, int dtype, int d_idx, int block_size,
+                                hipStream_t s);
+hipError_t launch_index_decode(const IndexArgs &a, int dtype, int d_idx, int block_size,
+                               hipStream_t s);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+hipError_t launch_attn_prefill(const AttnArgs &a, int dtype, int d_h, hipStream_t s);
+hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s);
+
+}  // namespace msa

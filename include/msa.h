@@ -1,0 +1,138 @@
+/*
+ * msa.h -- C ABI of libmsa.so, the MI355X (gfx950) MiniMax Sparse Attention hot path.
+ *
+ * The operations are those of the page "MiniMax-M3: MSA 技术报告速读"
+ * (mloasisblog.com/blog/ML/minimax-m3-msa-tech-report), section 核心机制:
+ *   index branch (索引分支): token scores S^idx = Q_idx K_idx^T / sqrt(d_idx) for
+ *     visible keys, causal max-pool into fixed-size key blocks (M^idx), and a
+ *     per-GQA-group TopK over blocks with the query's own block always kept;
+ *   main branch (主分支): softmax(Q K[I]^T / sqrt(d_h)) V[I] over the visible
+ *     tokens of the selected blocks I, all query heads of a group sharing the
+ *     group's selection.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers to dense, contiguous, row-major buffers
+ *     owned by the caller. The library keeps no pointer after a call returns,
+ *     never allocates, frees or synchronises, and enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL is the default stream).
+ *   - A query row t (0 <= t < n_q) sits at absolute position p = q_start + t and
+ *     sees keys j <= p. Head h belongs to group r = h / (h_q / h_kv).
+ *     Block c covers keys [c*block_size, (c+1)*block_size); n_blocks =
+ *     ceil(n_k / block_size); the local block of row t is floor(p / block_size).
+ *   - Layouts (K, V and K_idx have a token stride of kv_capacity, n_k of which
+ *     are valid):
+ *       q      [batch, h_q,  n_q, d_h]          k, v   [batch, h_kv, kv_capacity, d_h]
+ *       q_idx  [batch, h_kv, n_q, d_idx]        k_idx  [batch, kv_capacity, d_idx]
+ *       sel    [batch, h_kv, n_q, top_k] int32  o      [batch, h_q, n_q, d_h]
+ *       lse    [batch, h_q, n_q] float32        block_scores [batch, h_kv, n_q, n_blocks] float32
+ *     q, k, v, q_idx, k_idx and o share the element type `dtype`.
+ *   - Errors: a call validates everything it can on the host first; on any
+ *     error it returns a negative code, enqueues nothing and sets the text
+ *     returned by msa_last_error(). Launch failures return MSA_ERR_HIP.
+ *
+ * Supported set: dtype F32 or BF16; d_h in {64, 128}; d_idx in {32, 64};
+ * block_size in {32, 64}; 1 <= top_k <= 64; h_kv and h_q / h_kv in
+ * {1, 2, 4, 8, 16}; top_k * (16 / (h_q / h_kv)) <= 128 for prefill; at most
+ * 2048 * 2048 / (top_k - 1) candidate blocks before the last row's own block.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, range or divisibility */
+  MSA_ERR_UNSUPPORTED = -2, /* a dtype / d_h / d_idx / block_size / top_k combination with no kernel */
+  MSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_size reports */
+  MSA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+typedef struct {
+  int32_t batch;       /* sequences, >= 1 */
+  int32_t n_q;         /* query rows per sequence, >= 1 */
+  int32_t n_k;         /* valid keys per sequence; q_start + n_q <= n_k */
+  int32_t q_start;     /* absolute position of row 0, >= 0 */
+  int32_t h_q;         /* query heads */
+  int32_t h_kv;        /* KV heads = GQA groups = index heads */
+  int32_t d_h;         /* head dim of q, k, v, o */
+  int32_t d_idx;       /* head dim of q_idx, k_idx */
+  int32_t block_size;  /* tokens per key block */
+  int32_t top_k;       /* blocks selected per (row, group), counting the local block */
+  int32_t dtype;       /* msa_dtype */
+  int32_t kv_capacity; /* token stride of k, v, k_idx; 0 means n_k; else >= n_k */
+} msa_shape;
+
+/*
+ * Workspace bytes msa_index_topk needs for `shape` (block maxima and top-k
+ * candidates). Returns MSA_OK and writes *bytes, or an error code.
+ */
+int msa_index_topk_workspace_size(const msa_shape *shape, size_t *bytes);
+
+/*
+ * Index branch: block selection (S^idx, causal block max-pool M^idx and TopK of
+ * the index-branch equations, with the local block forced).
+ *   q_idx, k_idx  inputs (layouts above)
+ *   sel           out: for each (b, group, row) the selected blocks in ascending
+ *                 order, -1 padded. Selection: the local block, plus the top_k-1
+ *                 earlier blocks with the highest block score, equal scores going
+ *                 to the lower block index; a row that sees top_k blocks or fewer
+ *                 selects all of them. The positive 1/sqrt(d_idx) factor does not
+ *                 change the order and is not applied.
+ *   block_scores  optional out (NULL to skip): raw block maxima of q_idx . k_idx
+ *                 over visible keys, -inf for blocks after the local block.
+ *   workspace     device scratch of at least msa_index_topk_workspace_size bytes.
+ * Scores accumulate in fp32 from exact products of the inputs.
+ */
+int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx, int32_t *sel,
+                   float *block_scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes the attention entry points need for `shape` (split partials
+ * of the decode path; 0 for prefill). Returns MSA_OK and writes *bytes.
+ */
+int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes);
+
+/*
+ * Main branch, prefill or chunked prefill (any n_q, q_start): for every head h of
+ * group r and row t, o = softmax(q k_T^T / sqrt(d_h)) v_T over T = the visible
+ * tokens (j <= p) of the blocks listed in sel[b, r, t, :] (entries < 0 ignored).
+ *   q, k, v  inputs; sel as produced by msa_index_topk (ascending, -1 padded; each
+ *            valid entry must be a block whose first key is <= p)
+ *   o        out, dtype of q; rounded to nearest even for bf16
+ *   lse      optional out (NULL to skip): natural-log sum of exp of the scaled scores
+ *   workspace unused (pass NULL, 0).
+ */
+int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k, const void *v,
+                            const int32_t *sel, void *o, float *lse, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * Main branch, single-token decode: n_q == 1 and q_start == n_k - 1 (the new
+ * token's k, v and k_idx are already in the caches at position n_k - 1). Same
+ * result as msa_sparse_attn_prefill for that row, computed by a split over the
+ * selected blocks and a log-sum-exp merge (pre-scheduled, no atomics). Any n_k.
+ *   workspace  at least msa_sparse_attn_workspace_size bytes.
+ */
+int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *sel, void *o, float *lse,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Text of the last error on the calling thread (empty after a successful call). */
+const char *msa_last_error(void);
+
+/* ABI version of this header: 1. */
+int msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,146 @@
+"""Host-side checks of libmsa.so (no GPU needed): it loads, exports every function that
+include/msa.h declares, sizes workspaces, and rejects bad arguments with the documented
+code and a message before anything reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_gqa_msa_amd import binding as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return msa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(msa.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"libmsa.so does not export {n}"
+
+
+def test_header_struct_matches_binding():
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct {"):text.index("} msa_shape;")]
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [n for n, _ in msa.MsaShape._fields_]
+
+
+def test_abi_version(lib):
+    assert msa.msa_abi_version() == 1
+
+
+def good(**kw):
+    f = dict(batch=1, n_q=128, n_k=128, q_start=0, h_q=32, h_kv=4, d_h=128, d_idx=64,
+             block_size=64, top_k=8, dtype="bf16")
+    f.update(kw)
+    return msa.make_shape(**f)
+
+
+def test_workspace_sizes(lib):
+    s = good(batch=2, n_q=1000, n_k=1000)
+    nb = -(-1000 // 64)
+    assert msa.msa_index_topk_workspace_size(s) >= 2 * 4 * 1000 * nb * 4
+    assert msa.msa_sparse_attn_workspace_size(s) == 0           # prefill needs none
+    d = good(batch=4, n_q=1, n_k=1 << 20, q_start=(1 << 20) - 1, top_k=32)
+    # decode partials: (b, h, split) x (d_h + 2) floats
+    assert msa.msa_sparse_attn_workspace_size(d) >= 4 * 32 * 32 * 130 * 4
+    # chunked prefill at 1M keys needs the two-level candidate buffers
+    c = good(n_q=8192, n_k=1 << 20, q_start=(1 << 20) - 8192, top_k=32)
+    rows = 4 * 8192
+    assert msa.msa_index_topk_workspace_size(c) >= rows * (1 << 14) * 4 + 2 * rows * 8 * 31 * 4
+
+
+BAD = [
+    (dict(batch=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(n_q=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(q_start=-1), msa.MSA_ERR_INVALID_ARG),
+    (dict(n_q=100, n_k=120, q_start=30), msa.MSA_ERR_INVALID_ARG),   # q_start + n_q > n_k
+    (dict(h_q=30), msa.MSA_ERR_INVALID_ARG),                        # not a multiple of h_kv
+    (dict(top_k=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(kv_capacity=64), msa.MSA_ERR_INVALID_ARG),                # below n_k
+    (dict(dtype=7), msa.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=16), msa.MSA_ERR_UNSUPPORTED),
+    (dict(top_k=65), msa.MSA_ERR_UNSUPPORTED),
+    (dict(h_q=24, h_kv=3), msa.MSA_ERR_UNSUPPORTED),
+    (dict(h_q=96, h_kv=4), msa.MSA_ERR_UNSUPPORTED),                # 24 heads per group
+    (dict(d_idx=48), msa.MSA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_index_topk_rejects(lib, kw, code):
+    s = good(**kw)
+    dummy = 1 << 20  # never dereferenced: validation fails first
+    rc = lib.msa_index_topk(ctypes.byref(s), dummy, dummy, dummy, None, dummy, 1 << 40, None)
+    assert rc == code
+    assert msa.msa_last_error() != ""
+
+
+def test_attention_rejects(lib):
+    dummy = 1 << 20
+    s = good(d_h=96)
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(s), dummy, dummy, dummy, dummy, dummy, None,
+                                       None, 0, None) == msa.MSA_ERR_UNSUPPORTED
+    s = good()
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(s), None, dummy, dummy, dummy, dummy, None,
+                                       None, 0, None) == msa.MSA_ERR_INVALID_ARG
+    assert "non-NULL" in msa.msa_last_error()
+    # decode needs n_q == 1 at the last position
+    assert lib.msa_sparse_attn_decode(ctypes.byref(s), dummy, dummy, dummy, dummy, dummy, None,
+                                      dummy, 1 << 30, None) == msa.MSA_ERR_INVALID_ARG
+    d = good(n_q=1, n_k=5000, q_start=4999)
+    assert lib.msa_sparse_attn_decode(ctypes.byref(d), dummy, dummy, dummy, dummy, dummy, None,
+                                      dummy, 16, None) == msa.MSA_ERR_WORKSPACE
+    # G = 1 with top_k 16: 16 queries per wave x 16 entries > 128
+    g = good(h_q=4, h_kv=4, top_k=16)
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(g), dummy, dummy, dummy, dummy, dummy, None,
+                                       None, 0, None) == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_index_workspace_too_small(lib):
+    s = good()
+    need = msa.msa_index_topk_workspace_size(s)
+    dummy = 1 << 20
+    rc = lib.msa_index_topk(ctypes.byref(s), dummy, dummy, dummy, None, dummy, need - 1, None)
+    assert rc == msa.MSA_ERR_WORKSPACE
+    rc = lib.msa_index_topk(ctypes.byref(s), dummy, dummy, dummy, None, None, need, None)
+    assert rc == msa.MSA_ERR_WORKSPACE
+
+
+def test_null_shape_and_bytes(lib):
+    assert lib.msa_index_topk(None, 1, 1, 1, None, None, 0, None) == msa.MSA_ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert lib.msa_index_topk_workspace_size(None, ctypes.byref(n)) == msa.MSA_ERR_INVALID_ARG
+    s = good()
+    assert lib.msa_sparse_attn_workspace_size(ctypes.byref(s), None) == msa.MSA_ERR_INVALID_ARG
+
+
+def test_too_many_candidate_blocks(lib):
+    # 2^30 keys in blocks of 32 with k = 64: more chunk winners than one merge pass takes
+    s = good(n_q=1, n_k=(1 << 30), q_start=(1 << 30) - 1, block_size=32, top_k=64)
+    with pytest.raises(msa.MsaError) as e:
+        msa.msa_index_topk_workspace_size(s)
+    assert e.value.code == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(msa.MsaLibraryMissing):
+        msa._lib_saved = msa._lib
+        try:
+            msa._lib = None
+            msa.load_library(str(tmp_path / "nope.so"))
+        finally:
+            msa._lib = msa._lib_saved

@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same input bits.
+
+Block selections (and block scores, when requested) must match bit for bit: index
+inputs are integers, so every fp32 score is exact. O must be within 1e-5 max-abs
+(fp32) or 2e-2 max-abs and 1e-2 mean-abs (bf16); LSE within 1e-5 (fp32) / 1e-3 (bf16).
+Small shapes are compared in full; the six workloads run at full size with sampled
+rows (sampled sequences for decode) checked against the oracle and selection
+invariants checked on every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_gqa_msa_amd import binding as msa
+from block_sparse_gqa_msa_amd.inputs import WORKLOADS, Workload, generate
+from gpu_cases import (check_selection_invariants, compare, log, oracle_run, run_gpu,
+                       sample_rows, to_cpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    msa.load_library()  # raises if libmsa.so is missing: no fallback
+
+
+def W(name, dtype="bf16", batch=1, n_q=256, n_k=256, q_start=0, h_q=32, h_kv=4, d_h=128,
+      d_idx=64, block_size=64, top_k=8, idx_range=4, qkv_scale=0.5, needles=0, seed=7):
+    return Workload(name, dtype, batch, n_q, n_k, q_start, h_q, h_kv, d_h, d_idx, block_size,
+                    top_k, idx_range, qkv_scale, needles, seed)
+
+
+SMALL = [
+    WORKLOADS["prefill_512_f32"],
+    W("ragged_tail_bf16", batch=2, n_q=1000, n_k=1000, top_k=8, needles=4),
+    W("chunk_unaligned_g4", n_q=300, n_k=1500, q_start=1200, h_q=8, h_kv=2, d_h=64, d_idx=32,
+      block_size=32, top_k=5, needles=3),
+    W("g1_r8_f32", dtype="f32", n_q=700, n_k=700, h_q=8, h_kv=8, d_h=64, d_idx=64, top_k=3,
+      idx_range=3, qkv_scale=1.0),
+    W("g16_r1", n_q=520, n_k=520, h_q=16, h_kv=1, d_h=128, d_idx=32, block_size=32, top_k=4),
+    W("g2_r16_f32", dtype="f32", n_q=300, n_k=300, h_q=32, h_kv=16, d_h=64, d_idx=64,
+      block_size=32, top_k=6, idx_range=3, qkv_scale=1.0),
+    W("k64_near_dense", n_q=4200, n_k=4200, top_k=64, needles=8),
+    W("k1_local_only", n_q=777, n_k=777, top_k=1, block_size=32),
+    W("f32_d128_bs64", dtype="f32", n_q=640, n_k=640, h_q=8, h_kv=2, d_h=128, d_idx=64,
+      top_k=4, idx_range=3, qkv_scale=1.0),
+    W("prefill_two_level_topk", n_q=64, n_k=70064, q_start=70000, block_size=32, d_idx=32,
+      top_k=32, needles=16),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_full_oracle(w):
+    log(f"case {w.name}: {w}")
+    inp = generate(w, device="cuda")
+    buf = run_gpu(w, inp, block_scores=True)
+    check_selection_invariants(w, buf.sel)
+    ref = oracle_run(w, to_cpu(inp), block_scores=True)
+    bs_gpu = buf.block_scores.cpu().numpy().astype(np.float64)
+    assert np.array_equal(bs_gpu, ref["block_scores"]), "block scores differ"
+    compare(w, buf, ref, label=w.name)
+
+
+def test_heavy_ties_use_exact_fallback():
+    """All index keys zero: every block score is 0, so the tie-break alone decides
+    (lowest blocks first) and the wide-tie path of the top-k kernel runs."""
+    w = W("all_ties", n_q=3000, n_k=3000, block_size=32, d_idx=32, top_k=16)
+    inp = generate(w, device="cuda")
+    inp["k_idx"].zero_()
+    buf = run_gpu(w, inp)
+    ref = oracle_run(w, to_cpu(inp))
+    compare(w, buf, ref, label=w.name)
+
+
+def test_few_distinct_scores():
+    """Index values in {0, 1}: many ties at the threshold but a short candidate list."""
+    w = W("few_values", n_q=2500, n_k=2500, block_size=32, d_idx=32, top_k=12, idx_range=1)
+    inp = generate(w, device="cuda")
+    inp["q_idx"].abs_()
+    inp["k_idx"].abs_()
+    buf = run_gpu(w, inp)
+    ref = oracle_run(w, to_cpu(inp))
+    compare(w, buf, ref, label=w.name)
+
+
+DECODE_SMALL = [
+    W("decode_ragged_bf16", batch=3, n_q=1, n_k=5000, q_start=4999, top_k=16, needles=4),
+    W("decode_f32_g2", dtype="f32", batch=2, n_q=1, n_k=3001, q_start=3000, h_q=8, h_kv=4,
+      d_h=64, d_idx=32, block_size=32, top_k=4, idx_range=3, qkv_scale=1.0),
+    W("decode_two_level_topk", batch=2, n_q=1, n_k=140000, q_start=139999, block_size=32,
+      top_k=32, needles=8),
+    W("decode_few_blocks", batch=2, n_q=1, n_k=200, q_start=199, top_k=8),
+]
+
+
+@pytest.mark.parametrize("w", DECODE_SMALL, ids=lambda w: w.name)
+def test_decode_full_oracle(w):
+    log(f"case {w.name}: {w}")
+    inp = generate(w, device="cuda")
+    buf = run_gpu(w, inp, block_scores=True)
+    check_selection_invariants(w, buf.sel)
+    ref = oracle_run(w, to_cpu(inp), block_scores=True)
+    assert np.array_equal(buf.block_scores.cpu().numpy().astype(np.float64), ref["block_scores"])
+    compare(w, buf, ref, label=w.name)
+
+
+def test_kv_capacity_stride():
+    """Caches allocated longer than the valid length (kv_capacity > n_k), prefill and decode."""
+    for w in (W("cap_prefill", n_q=200, n_k=400, q_start=200, top_k=4),
+              W("cap_decode", batch=2, n_q=1, n_k=900, q_start=899, top_k=6)):
+        inp = generate(w, device="cuda")
+        cap = w.n_k + 136
+        big = {}
+        for key in ("k", "v"):
+            x = torch.zeros(w.batch, w.h_kv, cap, w.d_h, dtype=inp[key].dtype, device="cuda")
+            x[:, :, : w.n_k] = inp[key]
+            big[key] = x
+        x = torch.full((w.batch, cap, w.d_idx), 3.0, dtype=inp["k_idx"].dtype, device="cuda")
+        x[:, : w.n_k] = inp["k_idx"]
+        big["k_idx"] = x
+        big["q"], big["q_idx"] = inp["q"], inp["q_idx"]
+        buf = run_gpu(w, big, kv_capacity=cap)
+        ref = oracle_run(w, to_cpu(inp))
+        compare(w, buf, ref, label=w.name)
+
+
+def test_decode_equals_prefill_last_row():
+    """The split decode path and the prefill path agree on the same row."""
+    w = W("consistency", batch=2, n_q=1, n_k=4096 + 77, q_start=4096 + 76, top_k=16, needles=4)
+    inp = generate(w, device="cuda")
+    dec = run_gpu(w, inp)
+    s = msa.shape_of(w)
+    buf = msa.Buffers(s)
+    msa.msa_index_topk(s, inp["q_idx"], inp["k_idx"], buf.sel, None, buf.ws_index)
+    msa.msa_sparse_attn_prefill(s, inp["q"], inp["k"], inp["v"], buf.sel, buf.o, buf.lse)
+    torch.cuda.synchronize()
+    assert torch.equal(dec.sel, buf.sel)
+    assert (dec.o.float() - buf.o.float()).abs().max().item() <= 1e-2
+    assert (dec.lse - buf.lse).abs().max().item() <= 1e-4
+
+
+def test_chunked_equals_full_rows():
+    """A chunk at q_start > 0 gives the same selections as the matching rows of a full prefill."""
+    w = W("full", n_q=2000, n_k=2000, top_k=8, needles=6)
+    inp = generate(w, device="cuda")
+    full = run_gpu(w, inp)
+    start = 1333
+    wc = w.replace(name="chunk", n_q=w.n_q - start, q_start=start)
+    ic = dict(inp)
+    ic["q"] = inp["q"][:, :, start:].contiguous()
+    ic["q_idx"] = inp["q_idx"][:, :, start:].contiguous()
+    part = run_gpu(wc, ic)
+    assert torch.equal(part.sel, full.sel[:, :, start:])
+    assert torch.equal(part.o, full.o[:, :, start:])
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", ["prefill_8k", "prefill_128k", "chunk_1m"])
+def test_prefill_workload_full_size(name):
+    w = WORKLOADS[name]
+    log(f"case {name}: {w}")
+    inp = generate(w, device="cuda")
+    buf = run_gpu(w, inp)
+    check_selection_invariants(w, buf.sel)
+    rows = sample_rows(w, n_random=64 if w.n_q > 10000 else 128)
+    ref = oracle_run(w, to_cpu(inp), rows=rows)
+    compare(w, buf, ref, rows=rows, label=name)
+    if name == "prefill_8k":  # every row's selection (index branch only)
+        import oracle
+        full = oracle.get().run(w, to_cpu(inp, ("q_idx", "k_idx")), attention=False)
+        assert np.array_equal(buf.sel.cpu().numpy(), full["sel"]), "selections differ"
+
+
+@pytest.mark.parametrize("name,seqs", [("decode_256k_b32", [0, 13, 31]),
+                                       ("decode_1m_b4", [0, 3])])
+def test_decode_workload_full_size(name, seqs):
+    w = WORKLOADS[name]
+    log(f"case {name}: {w}")
+    inp = generate(w, device="cuda")
+    buf = run_gpu(w, inp)
+    check_selection_invariants(w, buf.sel)
+    import oracle
+    orc = oracle.get()
+    outs = []
+    for b in seqs:
+        wb = w.replace(batch=1)
+        cb = {k: inp[k][b:b + 1].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
+        outs.append(orc.run(wb, cb))
+        log(f"  oracle sequence {b} done")
+    ref = {k: np.concatenate([o[k] for o in outs], axis=0) for k in ("sel", "o", "lse")}
+    compare(w, buf, ref, seqs=torch.as_tensor(seqs, device="cuda"), label=name)
