@@ -1,0 +1,250 @@
+"""Benchmark of the MSA hot path on one MI355X; prints ONE JSON line.
+
+Headline (``value``): causal prefill tokens/s at N = 131072 (32 query heads / 4 KV
+groups, d_h 128, index d_idx 64, blocks of 64, top_k 32, bf16): one step is the index
+branch (block scores, top-k) plus the sparse prefill attention over all 131072 rows.
+The same line carries the 1M-token decode result (batch 4, one new token each, same
+heads) under ``decode``, each with the roofline of its dominant kernel and the fp64
+oracle timed on a bounded sample on the host cores.
+
+Inputs are seeded synthetic tensors already resident in HBM when timing starts. Kernel
+durations come from HIP events recorded on the stream the library launches on.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps KD] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MSA attn: prefill tok/s @128K, decode tok/s @1M; % of MFMA/HBM roofline"
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E
+
+
+# ------------------------------------------------------------------ algorithmic work
+
+def prefill_work(w):
+    """Algorithmic FLOPs of one step: index scores R*(p+1)*2*d_idx per row plus main
+    branch H_q*T_p*4*d_h, T_p = visible tokens of the selected blocks."""
+    p = w.q_start + np.arange(w.n_q, dtype=np.int64)
+    b = p // w.block_size
+    t_p = (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
+    index = float(w.batch * w.h_kv * np.sum(p + 1) * 2 * w.d_idx)
+    main = float(w.batch * w.h_q * np.sum(t_p) * 4 * w.d_h)
+    return index, main
+
+
+def decode_work(w):
+    """Algorithmic HBM bytes of one decode step: the whole k_idx cache, the selected K/V
+    blocks, q, q_idx, o and sel (block-score scratch and split partials excluded)."""
+    L, e = w.n_k, 2
+    nb = -(-L // w.block_size)
+    sel_blocks = min(w.top_k, nb)
+    kv_tokens = (sel_blocks - 1) * w.block_size + (L - (nb - 1) * w.block_size)
+    k_idx = L * w.d_idx * e
+    kv = w.h_kv * kv_tokens * w.d_h * e * 2
+    small = (w.h_q * w.d_h * e * 2) + (w.h_kv * w.d_idx * e) + (w.h_kv * w.top_k * 4)
+    per_seq = dict(k_idx=k_idx, kv=kv, small=small)
+    index_kernel = w.batch * (k_idx + w.h_kv * w.d_idx * e)
+    return w.batch * (k_idx + kv + small), index_kernel, per_seq
+
+
+# ------------------------------------------------------------------ GPU timing
+
+def time_step(w, inputs, steps, warmup, decode):
+    import torch
+    from block_sparse_gqa_msa_amd import binding as msa
+
+    s = msa.shape_of(w)
+    R, n = w.h_kv, w.n_q
+    nb = -(-w.n_k // w.block_size)
+    scores = torch.empty((w.batch, R, n, nb), dtype=torch.float32, device="cuda")
+    sel = torch.empty((w.batch, R, n, w.top_k), dtype=torch.int32, device="cuda")
+    o = torch.empty((w.batch, w.h_q, n, w.d_h), dtype=inputs["q"].dtype, device="cuda")
+    lse = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device="cuda")
+    ws_topk = torch.empty(max(1, msa.msa_topk_workspace_size(s)), dtype=torch.uint8, device="cuda")
+    ws_attn = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(s)), dtype=torch.uint8,
+                          device="cuda")
+    attn = msa.msa_sparse_attn_decode if decode else msa.msa_sparse_attn_prefill
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        msa.msa_index_block_scores(s, inputs["q_idx"], inputs["k_idx"], scores)
+        if ev:
+            ev[1].record(stream)
+        msa.msa_topk_from_block_scores(s, scores, sel, ws_topk)
+        if ev:
+            ev[2].record(stream)
+        attn(s, inputs["q"], inputs["k"], inputs["v"], sel, o, lse, ws_attn)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    k_index = np.mean([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
+    k_topk = np.mean([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
+    k_attn = np.mean([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
+    return wall, dict(index_scores=k_index, topk=k_topk, attention=k_attn)
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline_prefill(w, inputs, target_s=12.0, seed=0):
+    import oracle
+    orc = oracle.get()
+    cpu = {k: inputs[k].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
+    rng = np.random.default_rng(seed)
+    probe = np.sort(rng.choice(w.n_q, size=16, replace=False))
+    t0 = time.perf_counter()
+    orc.run(w, cpu, rows=probe)
+    dt = time.perf_counter() - t0
+    n = int(min(w.n_q, max(16, 16 * target_s / max(dt, 1e-3))))
+    rows = np.sort(rng.choice(w.n_q, size=n, replace=False))
+    t0 = time.perf_counter()
+    orc.run(w, cpu, rows=rows)
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+                sample=f"{n} query rows drawn uniformly (seed {seed}) from the {w.n_q}-row "
+                       f"prefill, all {w.h_kv} groups and {w.h_q} heads; {dt:.1f} s")
+
+
+def cpu_baseline_decode(w, inputs):
+    import oracle
+    orc = oracle.get()
+    wb = w.replace(batch=1)
+    cpu = {k: inputs[k][0:1].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
+    t0 = time.perf_counter()
+    orc.run(wb, cpu)
+    dt = time.perf_counter() - t0
+    return dict(value=1.0 / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+                sample=f"1 of {w.batch} sequences (one decode token over {w.n_k} cached "
+                       f"tokens); {dt:.1f} s")
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--prefill", default="prefill_128k")
+    ap.add_argument("--decode", default="decode_1m_b4")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this MSA build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_gqa_msa_amd import binding as msa
+    from block_sparse_gqa_msa_amd.inputs import WORKLOADS, generate
+
+    msa.load_library()
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+
+    # ---- prefill at 128K
+    wp = WORKLOADS[args.prefill]
+    inp = generate(wp, device="cuda")
+    log(f"[bench] prefill {wp.name}: warmup {args.warmup}, steps {args.steps}")
+    wall, kt = time_step(wp, inp, args.steps, args.warmup, decode=False)
+    f_index, f_main = prefill_work(wp)
+    tok_s = wp.batch * wp.n_q / wall
+    cand = {
+        "index_scores": dict(kernel="index_pool_prefill", flops=f_index, t=kt["index_scores"]),
+        "attention": dict(kernel="attn_prefill", flops=f_main, t=kt["attention"]),
+    }
+    dom = max(cand.values(), key=lambda c: c["t"])
+    roof = dict(kernel=dom["kernel"], bound="mfma", achieved=dom["flops"] / dom["t"] / 1e12,
+                peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                frac=dom["flops"] / dom["t"] / PEAK_BF16_FLOPS, traffic=None,
+                per_launch_flops=dom["flops"], avg_launch_ms=dom["t"] * 1e3)
+    path = dict(flops=f_index + f_main, tflops=(f_index + f_main) / wall / 1e12,
+                mfma_frac=(f_index + f_main) / wall / PEAK_BF16_FLOPS)
+    log(f"[bench] prefill {wall * 1e3:.2f} ms/step, kernels (ms): "
+        + ", ".join(f"{k} {v * 1e3:.3f}" for k, v in kt.items()))
+    cpu_p = None
+    if not args.no_cpu:
+        log("[bench] oracle CPU baseline (prefill sample)")
+        cpu_p = cpu_baseline_prefill(wp, inp)
+    del inp
+    torch.cuda.empty_cache()
+
+    # ---- decode at 1M
+    wd = WORKLOADS[args.decode]
+    inp = generate(wd, device="cuda")
+    log(f"[bench] decode {wd.name}: warmup {args.warmup}, steps {args.decode_steps}")
+    dwall, dkt = time_step(wd, inp, args.decode_steps, args.warmup, decode=True)
+    d_bytes, d_index_bytes, _ = decode_work(wd)
+    droof = dict(kernel="index_pool_decode", bound="hbm",
+                 achieved=d_index_bytes / dkt["index_scores"] / 1e9, peak=PEAK_HBM_BYTES / 1e9,
+                 unit="GB/s", frac=d_index_bytes / dkt["index_scores"] / PEAK_HBM_BYTES,
+                 traffic=None, per_launch_bytes=d_index_bytes,
+                 avg_launch_ms=dkt["index_scores"] * 1e3)
+    log(f"[bench] decode {dwall * 1e6:.1f} us/step, kernels (us): "
+        + ", ".join(f"{k} {v * 1e6:.1f}" for k, v in dkt.items()))
+    cpu_d = None
+    if not args.no_cpu:
+        log("[bench] oracle CPU baseline (decode sample)")
+        cpu_d = cpu_baseline_decode(wd, inp)
+
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wp.name, "batch": wp.batch, "seq_len": wp.n_q, "h_q": wp.h_q,
+                   "h_kv": wp.h_kv, "d_h": wp.d_h, "d_idx": wp.d_idx,
+                   "block_size": wp.block_size, "top_k": wp.top_k, "parallelism": "none"},
+        "roofline": roof,
+        "path_mfma": path,
+        "kernel_ms": {k: v * 1e3 for k, v in kt.items()},
+        "cpu_baseline": cpu_p,
+        "decode": {
+            "workload": wd.name, "value": wd.batch / dwall, "unit": "tok/s",
+            "steps": args.decode_steps, "ms_per_step": dwall * 1e3,
+            "config": {"batch": wd.batch, "kv_len": wd.n_k, "h_q": wd.h_q, "h_kv": wd.h_kv,
+                       "d_h": wd.d_h, "d_idx": wd.d_idx, "block_size": wd.block_size,
+                       "top_k": wd.top_k},
+            "roofline": droof,
+            "path_hbm": dict(bytes=d_bytes, gbs=d_bytes / dwall / 1e9,
+                             hbm_frac=d_bytes / dwall / PEAK_HBM_BYTES),
+            "kernel_ms": {k: v * 1e3 for k, v in dkt.items()},
+            "cpu_baseline": cpu_d,
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

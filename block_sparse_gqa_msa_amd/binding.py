@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(PKG, "libmsa.so")
 
 MSA_F32, MSA_BF16 = 0, 1
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
-EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_sparse_attn_workspace_size",
-           "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_last_error",
-           "msa_abi_version")
+EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_scores",
+           "msa_topk_workspace_size", "msa_topk_from_block_scores",
+           "msa_sparse_attn_workspace_size", "msa_sparse_attn_prefill", "msa_sparse_attn_decode",
+           "msa_last_error", "msa_abi_version")
 
 
 class MsaShape(ctypes.Structure):
@@ -60,11 +61,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sz = ctypes.POINTER(ctypes.c_size_t)
     lib.msa_index_topk_workspace_size.argtypes = [S, sz]
     lib.msa_sparse_attn_workspace_size.argtypes = [S, sz]
+    lib.msa_topk_workspace_size.argtypes = [S, sz]
+    lib.msa_index_block_scores.argtypes = [S, P, P, P, P]
+    lib.msa_topk_from_block_scores.argtypes = [S, P, P, P, ctypes.c_size_t, P]
     lib.msa_index_topk.argtypes = [S, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_prefill.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_decode.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-    for f in ("msa_index_topk_workspace_size", "msa_sparse_attn_workspace_size", "msa_index_topk",
-              "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_abi_version"):
+    for f in EXPORTS:
+        if f == "msa_last_error":
+            continue
         getattr(lib, f).restype = I
     lib.msa_last_error.restype = ctypes.c_char_p
     lib.msa_last_error.argtypes = []
@@ -162,6 +167,29 @@ def msa_index_topk(shape: MsaShape, q_idx, k_idx, sel, block_scores=None, worksp
         ctypes.byref(shape), _ptr(q_idx, et, "q_idx"), _ptr(k_idx, et, "k_idx"),
         _ptr(sel, torch.int32, "sel"), _ptr(block_scores, torch.float32, "block_scores"),
         wp, wn, _stream(stream, sel)))
+
+
+def msa_index_block_scores(shape: MsaShape, q_idx, k_idx, block_scores, stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    _check(load_library().msa_index_block_scores(
+        ctypes.byref(shape), _ptr(q_idx, et, "q_idx"), _ptr(k_idx, et, "k_idx"),
+        _ptr(block_scores, torch.float32, "block_scores"), _stream(stream, block_scores)))
+
+
+def msa_topk_workspace_size(shape: MsaShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_topk_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return int(n.value)
+
+
+def msa_topk_from_block_scores(shape: MsaShape, block_scores, sel, workspace=None,
+                               stream=None) -> None:
+    import torch
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_topk_from_block_scores(
+        ctypes.byref(shape), _ptr(block_scores, torch.float32, "block_scores"),
+        _ptr(sel, torch.int32, "sel"), wp, wn, _stream(stream, sel)))
 
 
 def msa_sparse_attn_prefill(shape: MsaShape, q, k, v, sel, o, lse=None, workspace=None,

@@ -143,6 +143,31 @@ int msa_index_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
   return ok();
 }
 
+// Shared by msa_index_topk and the two split calls.
+static int launch_scores(const msa_shape &s, const void *q_idx, const void *k_idx, float *bmax,
+                         hipStream_t st) {
+  msa::IndexArgs ia{q_idx, k_idx, bmax, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
+                    (int)n_blocks(s), cap_of(s), 0};
+  hipError_t e;
+  if (s.n_q == 1) {
+    ia.key_chunk = key_chunk_decode(s);
+    e = msa::launch_index_decode(ia, s.dtype, s.d_idx, s.block_size, st);
+  } else {
+    ia.key_chunk = key_chunk_prefill(s);
+    e = msa::launch_index_prefill(ia, s.dtype, s.d_idx, s.block_size, st);
+  }
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "index kernel launch");
+}
+
+static int launch_select(const msa_shape &s, const float *bmax, int32_t *sel, unsigned char *cand,
+                         size_t cand_bytes, hipStream_t st) {
+  msa::TopkArgs ta{bmax, sel, reinterpret_cast<uint32_t *>(cand),
+                   reinterpret_cast<int32_t *>(cand + cand_bytes), s.batch, s.n_q, s.q_start,
+                   s.h_kv, (int)n_blocks(s), s.block_size, s.top_k, topk_chunks(s)};
+  hipError_t e = msa::launch_topk(ta, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "top-k kernel launch");
+}
+
 int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx, int32_t *sel,
                    float *block_scores, void *workspace, size_t workspace_bytes, void *stream) {
   int rc = check_shape(shape);
@@ -158,29 +183,53 @@ int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
   float *bmax = block_scores ? block_scores : reinterpret_cast<float *>(ws);
-  const long long rows = (long long)s.batch * s.h_kv * s.n_q;
-  hipError_t e;
   if (block_scores) {
-    e = msa::launch_fill(block_scores, (size_t)rows * (size_t)n_blocks(s), -INFINITY, st);
+    const long long rows = (long long)s.batch * s.h_kv * s.n_q;
+    hipError_t e = msa::launch_fill(block_scores, (size_t)rows * (size_t)n_blocks(s), -INFINITY, st);
     if (e != hipSuccess) return hip_fail(e, "block score fill");
   }
-  msa::IndexArgs ia{q_idx, k_idx, bmax, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
-                    (int)n_blocks(s), cap_of(s), 0};
-  if (s.n_q == 1) {
-    ia.key_chunk = key_chunk_decode(s);
-    e = msa::launch_index_decode(ia, s.dtype, s.d_idx, s.block_size, st);
-  } else {
-    ia.key_chunk = key_chunk_prefill(s);
-    e = msa::launch_index_prefill(ia, s.dtype, s.d_idx, s.block_size, st);
-  }
-  if (e != hipSuccess) return hip_fail(e, "index kernel launch");
-  msa::TopkArgs ta{bmax, sel,
-                   reinterpret_cast<uint32_t *>(ws + w.bmax),
-                   reinterpret_cast<int32_t *>(ws + w.bmax + w.cand),
-                   s.batch, s.n_q, s.q_start, s.h_kv, (int)n_blocks(s), s.block_size, s.top_k,
-                   topk_chunks(s)};
-  e = msa::launch_topk(ta, st);
-  if (e != hipSuccess) return hip_fail(e, "top-k kernel launch");
+  if ((rc = launch_scores(s, q_idx, k_idx, bmax, st))) return rc;
+  if ((rc = launch_select(s, bmax, sel, ws + w.bmax, w.cand, st))) return rc;
+  return ok();
+}
+
+int msa_index_block_scores(const msa_shape *shape, const void *q_idx, const void *k_idx,
+                           float *block_scores, void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if ((rc = check_index_dims(s))) return rc;
+  if (!q_idx || !k_idx || !block_scores)
+    return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx and block_scores must be non-NULL");
+  if ((rc = launch_scores(s, q_idx, k_idx, block_scores, reinterpret_cast<hipStream_t>(stream))))
+    return rc;
+  return ok();
+}
+
+int msa_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  IndexWs w;
+  if ((rc = index_ws(*shape, false, &w))) return rc;
+  *bytes = w.total;
+  return ok();
+}
+
+int msa_topk_from_block_scores(const msa_shape *shape, const float *block_scores, int32_t *sel,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if (!block_scores || !sel) return fail(MSA_ERR_INVALID_ARG, "block_scores and sel must be non-NULL");
+  IndexWs w;
+  if ((rc = index_ws(s, false, &w))) return rc;
+  if (w.total && (!workspace || workspace_bytes < w.total))
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((rc = launch_select(s, block_scores, sel, reinterpret_cast<unsigned char *>(workspace),
+                          w.cand, reinterpret_cast<hipStream_t>(stream))))
+    return rc;
   return ok();
 }
 

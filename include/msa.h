@@ -95,6 +95,31 @@ int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx,
                    float *block_scores, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The index branch in two calls, for callers that want the block scores (the
+ * same kernels msa_index_topk runs, one launch each):
+ *
+ * msa_index_block_scores: token scores and causal block max-pool only. Writes,
+ *   for every (b, group, row), the raw block maxima of q_idx . k_idx over the
+ *   visible keys of every block up to the row's local block; entries after the
+ *   local block are -inf or left unwritten (pre-fill the buffer if they matter).
+ *   block_scores [batch, h_kv, n_q, n_blocks] float32, caller-owned.
+ */
+int msa_index_block_scores(const msa_shape *shape, const void *q_idx, const void *k_idx,
+                           float *block_scores, void *stream);
+
+/* Workspace bytes msa_topk_from_block_scores needs (top-k chunk candidates). */
+int msa_topk_workspace_size(const msa_shape *shape, size_t *bytes);
+
+/*
+ * msa_topk_from_block_scores: the TopK step with the local block forced, from
+ *   block scores as written by msa_index_block_scores (only entries before each
+ *   row's local block are read). Output `sel` as for msa_index_topk. d_idx is
+ *   not used.
+ */
+int msa_topk_from_block_scores(const msa_shape *shape, const float *block_scores, int32_t *sel,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Workspace bytes the attention entry points need for `shape` (split partials
  * of the decode path; 0 for prefill). Returns MSA_OK and writes *bytes.
  */

@@ -191,3 +191,25 @@ def test_decode_workload_full_size(name, seqs):
         log(f"  oracle sequence {b} done")
     ref = {k: np.concatenate([o[k] for o in outs], axis=0) for k in ("sel", "o", "lse")}
     compare(w, buf, ref, seqs=torch.as_tensor(seqs, device="cuda"), label=name)
+
+
+def test_split_index_calls_equal_fused():
+    """msa_index_block_scores + msa_topk_from_block_scores select exactly what
+    msa_index_topk selects, and the block scores agree on every visible block."""
+    for w in (W("split_prefill", n_q=3000, n_k=3000, top_k=16, needles=6),
+              W("split_decode", batch=2, n_q=1, n_k=150000, q_start=149999, block_size=32,
+                top_k=32, needles=8)):
+        inp = generate(w, device="cuda")
+        fused = run_gpu(w, inp, block_scores=True)
+        s = msa.shape_of(w)
+        nb = -(-w.n_k // w.block_size)
+        scores = torch.full((w.batch, w.h_kv, w.n_q, nb), float("nan"), device="cuda")
+        sel = torch.empty_like(fused.sel)
+        ws = torch.empty(max(1, msa.msa_topk_workspace_size(s)), dtype=torch.uint8, device="cuda")
+        msa.msa_index_block_scores(s, inp["q_idx"], inp["k_idx"], scores)
+        msa.msa_topk_from_block_scores(s, scores, sel, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, fused.sel), w.name
+        local = (w.q_start + torch.arange(w.n_q, device="cuda")) // w.block_size
+        vis = torch.arange(nb, device="cuda")[None, :] <= local[:, None]
+        assert torch.equal(scores[..., vis], fused.block_scores[..., vis]), w.name
