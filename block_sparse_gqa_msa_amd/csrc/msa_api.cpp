@@ -99,6 +99,28 @@ int check_attn_dims(const msa_shape &s) {
 
 int decode_splits(const msa_shape &s) { return s.top_k; }  // one selected block per split
 
+bool is_decode(const msa_shape &s) { return s.n_q == 1 && s.q_start == s.n_k - 1; }
+
+size_t attn_prefill_ws(const msa_shape &s, msa::KvLayout *lay) {
+  return msa::kv_workspace_bytes(s.batch, s.h_kv, s.n_q, s.top_k, n_blocks(s), s.h_q / s.h_kv,
+                                 s.d_h, s.dtype == MSA_F32 ? 4 : 2, lay);
+}
+
+int kv_seg_rows(const msa_shape &s) {
+  return msa::kv_segment_rows(s.batch, s.h_kv, s.n_q, s.top_k, s.h_q / s.h_kv, s.d_h,
+                              s.dtype == MSA_F32 ? 4 : 2);
+}
+
+int check_prefill_limits(const msa_shape &s) {
+  const long long entries = (long long)s.batch * s.h_kv * s.n_q * s.top_k;
+  const long long n_seg = (s.n_q + kv_seg_rows(s) - 1) / kv_seg_rows(s);
+  if (entries >= (1LL << 31) || s.n_q >= (1 << 25) ||
+      n_seg * s.batch * s.h_kv * n_blocks(s) >= (1LL << 30))
+    return fail(MSA_ERR_UNSUPPORTED, "prefill too large for one call (%lld selection entries); "
+                "split the query rows over several calls", entries);
+  return MSA_OK;
+}
+
 size_t attn_decode_ws(const msa_shape &s) {
   const size_t parts = (size_t)s.batch * s.h_q * decode_splits(s);
   return align_up(parts * s.d_h * sizeof(float)) + align_up(parts * 2 * sizeof(float));
@@ -238,28 +260,42 @@ int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes) {
   if (rc) return rc;
   if ((rc = check_attn_dims(*shape))) return rc;
   if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
-  const bool decode = shape->n_q == 1 && shape->q_start == shape->n_k - 1;
-  *bytes = decode ? attn_decode_ws(*shape) : 0;
+  if ((rc = check_prefill_limits(*shape))) return rc;
+  *bytes = attn_prefill_ws(*shape, nullptr);
+  if (is_decode(*shape)) {  // either entry point may be called for a decode shape
+    const size_t d = attn_decode_ws(*shape);
+    if (d > *bytes) *bytes = d;
+  }
   return ok();
 }
 
 int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k, const void *v,
                             const int32_t *sel, void *o, float *lse, void *workspace,
                             size_t workspace_bytes, void *stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int rc = check_shape(shape);
   if (rc) return rc;
   const msa_shape &s = *shape;
   if ((rc = check_attn_dims(s))) return rc;
   if (!q || !k || !v || !sel || !o) return fail(MSA_ERR_INVALID_ARG, "q, k, v, sel and o must be non-NULL");
-  const int G = s.h_q / s.h_kv;
-  if (s.top_k * (16 / G) > 128)
-    return fail(MSA_ERR_UNSUPPORTED, "top_k * (16 / (h_q / h_kv)) = %d exceeds 128", s.top_k * (16 / G));
-  msa::AttnArgs a{q, k, v, sel, o, lse, nullptr, nullptr, s.batch, s.n_q, s.n_k, s.q_start,
-                  s.h_q, s.h_kv, s.block_size, s.top_k, cap_of(s), 0, 0,
-                  (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};
-  hipError_t e = msa::launch_attn_prefill(a, s.dtype, s.d_h, reinterpret_cast<hipStream_t>(stream));
+  if ((rc = check_prefill_limits(s))) return rc;
+  msa::KvLayout lay;
+  const size_t need = attn_prefill_ws(s, &lay);
+  if (!workspace || workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
+  const int seg_rows = kv_seg_rows(s);
+  const int n_seg = (s.n_q + seg_rows - 1) / seg_rows;
+  const long long NB = (long long)n_seg * s.batch * s.h_kv * n_blocks(s);
+  int32_t *cnt = reinterpret_cast<int32_t *>(ws + lay.cnt);
+  msa::KvArgs a{q, k, v, sel, o, lse, cnt, cnt + NB,
+                reinterpret_cast<int32_t *>(ws + lay.boff), reinterpret_cast<int32_t *>(ws + lay.coff),
+                reinterpret_cast<int32_t *>(ws + lay.list), reinterpret_cast<int32_t *>(ws + lay.cmap),
+                ws + lay.part_o,
+                reinterpret_cast<float *>(ws + lay.part_ml), s.batch, s.n_q, s.n_k, s.q_start,
+                s.h_q, s.h_kv, s.block_size, s.top_k, cap_of(s), (int)n_blocks(s), seg_rows,
+                n_seg, (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};
+  hipError_t e = msa::launch_attn_prefill_kv(a, s.dtype, s.d_h, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   return ok();
 }

@@ -1,12 +1,12 @@
-// msa_attn.hip -- main branch: exact softmax attention over the selected blocks.
+// msa_attn.hip -- main branch for single-token decode: exact softmax attention over the
+// selected blocks, split over the blocks and merged by log-sum-exp.
 //
 // Definition ("MiniMax-M3: MSA 技术报告速读", section 核心机制, main-branch equation):
 // O^(h)_t = softmax(q_h k_T^T / sqrt(d_h)) v_T, T = visible tokens (j <= p) of the blocks
 // the row's group selected; every head of a group shares the group's selection.
 //
-// A wave owns 16 (query, head) rows: 16/G consecutive queries x the G heads of one group.
-// It walks the union of its queries' selections in ascending block order; rows whose query
-// did not pick the current block are masked out of it. Per block:
+// A wave owns the G heads of one (sequence, group) (rows of a 16-row tile) and a fixed share
+// of the selected blocks. Per block:
 //   S^T = K_blk Q^T            (keys down the accumulator rows, one row per lane column)
 //   online softmax in the log2 domain (per-lane row = lane % 16, reductions over 4 groups)
 //   O^T += V_blk^T P^T         (P^T comes straight from the S^T accumulators: lane group g
@@ -186,75 +186,6 @@ __device__ __forceinline__ void store4<float>(float *dst, f32x4 v, float scale) 
   *reinterpret_cast<f32x4 *>(dst) = v * scale;
 }
 
-// Prefill. Grid: x = groups of 4 waves over (b, r, query group); block = 256 threads.
-template <typename E, int DH, int BS>
-__global__ __launch_bounds__(256) void attn_prefill(AttnArgs a, int log2g) {
-  using F = typename Frag<E>::type;
-  using VS = VStage<E, DH, BS>;
-  constexpr int DC = DH / 32, DT = DH / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char s_vt[4][VS::BYTES];
-  __shared__ int32_t s_sel[4][128];
-
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
-  const int G = 1 << log2g, QPW = 16 >> log2g, R = a.h_kv, k = a.top_k;
-  const int n_qg = (a.n_q + QPW - 1) / QPW;
-  const long wid = (long)blockIdx.x * 4 + w;
-  if (wid >= (long)a.batch * R * n_qg) return;
-  const int qg = (int)(wid % n_qg);
-  const int r = (int)((wid / n_qg) % R);
-  const int b = (int)(wid / ((long)n_qg * R));
-
-  const int qrow = c16 >> log2g, h = r * G + (c16 & (G - 1));
-  const int t = qg * QPW + qrow;
-  const bool row_valid = (c16 < QPW * G) && t < a.n_q;
-  const long p_row = (long)a.q_start + t;
-
-  const E *q = reinterpret_cast<const E *>(a.q);
-  F bq[DC];
-#pragma unroll
-  for (int dc = 0; dc < DC; ++dc)
-    bq[dc] = row_valid ? load_frag(q + (((long)b * a.h_q + h) * a.n_q + t) * DH + dc * 32 + g * 8)
-                       : zero_frag(q);
-  const int32_t *selp = a.sel + (((long)b * R + r) * a.n_q + (long)qg * QPW) * k;
-  for (int e = lane; e < QPW * k; e += 64)
-    s_sel[w][e] = (qg * QPW + e / k < a.n_q) ? selp[e] : -1;
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-
-  const long plane = ((long)b * R + r) * (long)a.cap * DH;
-  const E *kp = reinterpret_cast<const E *>(a.k) + plane;
-  const E *vp = reinterpret_cast<const E *>(a.v) + plane;
-  RowState<E, DH, BS> st;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
-
-  int ptr = 0;  // lanes < QPW: cursor into their query's (ascending) selection
-  for (;;) {
-    int cur = 0x7fffffff;
-    if (lane < QPW && ptr < k) {
-      const int v = s_sel[w][lane * k + ptr];
-      if (v >= 0) cur = v;
-    }
-    const int c = wave_min_i32(cur);
-    if (c == 0x7fffffff) break;
-    const bool mine = lane < QPW && cur == c;
-    const uint64_t act = ballot(mine);
-    if (mine) ++ptr;
-    const bool active = row_valid && ((act >> qrow) & 1ull);
-    attend_block<E, DH, BS>(st, bq, kp, vp, (long)c * BS, a.n_k, active, p_row, a.scale_log2,
-                            s_vt[w]);
-  }
-  if (row_valid) {
-    const float inv = 1.f / st.l;
-    E *o = reinterpret_cast<E *>(a.o) + (((long)b * a.h_q + h) * a.n_q + t) * DH;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) store4<E>(o + dt * 16 + g * 4, st.o[dt], inv);
-    if (a.lse && g == 0)
-      a.lse[((long)b * a.h_q + h) * a.n_q + t] = (st.m + __log2f(st.l)) * 0.69314718055994531f;
-  }
-}
-
 // Decode, split pass. Grid: x = groups of 4 waves over (b, r, split).
 template <typename E, int DH, int BS>
 __global__ __launch_bounds__(256) void attn_decode_split(AttnArgs a, int log2g) {
@@ -346,18 +277,6 @@ __global__ __launch_bounds__(256) void attn_decode_merge(AttnArgs a) {
 }
 
 template <typename E, int DH>
-hipError_t prefill_t(const AttnArgs &a, int bs, int log2g, hipStream_t s) {
-  const int QPW = 16 >> log2g;
-  const long waves = (long)a.batch * a.h_kv * ((a.n_q + QPW - 1) / QPW);
-  const dim3 grid((unsigned)((waves + 3) / 4));
-  if (bs == 32)
-    hipLaunchKernelGGL((attn_prefill<E, DH, 32>), grid, dim3(256), 0, s, a, log2g);
-  else
-    hipLaunchKernelGGL((attn_prefill<E, DH, 64>), grid, dim3(256), 0, s, a, log2g);
-  return hipGetLastError();
-}
-
-template <typename E, int DH>
 hipError_t decode_t(const AttnArgs &a, int bs, int log2g, hipStream_t s) {
   const long waves = (long)a.batch * a.h_kv * a.splits;
   const dim3 grid((unsigned)((waves + 3) / 4));
@@ -379,14 +298,6 @@ int ilog2(int x) {
 }
 
 }  // namespace
-
-hipError_t launch_attn_prefill(const AttnArgs &a, int dtype, int d_h, hipStream_t s) {
-  const int lg = ilog2(a.h_q / a.h_kv);
-  if (dtype == 0) return d_h == 64 ? prefill_t<float, 64>(a, a.block_size, lg, s)
-                                   : prefill_t<float, 128>(a, a.block_size, lg, s);
-  return d_h == 64 ? prefill_t<bf16_t, 64>(a, a.block_size, lg, s)
-                   : prefill_t<bf16_t, 128>(a, a.block_size, lg, s);
-}
 
 hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s) {
   const int lg = ilog2(a.h_q / a.h_kv);

@@ -75,6 +75,29 @@ __device__ __forceinline__ float sum_xor16(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Transposing max-reduction over the four lane groups: given per-lane values v0..v3 (one
+// per 16-column N-tile), returns in lane group g the maximum of v_g over all four groups.
+// Uses v_permlane32_swap (x <-> upper half of the other operand) then v_permlane16_swap.
+__device__ __forceinline__ float max_groups_transpose(float v0, float v1, float v2, float v3) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+  const float t0 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));  // N-tile 0 (lo) / 2 (hi)
+  const float t1 = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));  // N-tile 1 (lo) / 3 (hi)
+  auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(t0), __float_as_uint(t1), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// Max of N values as a chain of three-input maxima (v_max3_f32).
+template <int N>
+__device__ __forceinline__ float max_chain(const float (&v)[N]) {
+  static_assert(N >= 2, "max_chain needs two values");
+  float m = fmaxf(v[0], v[1]);
+#pragma unroll
+  for (int i = 2; i + 1 < N; i += 2) m = fmaxf(fmaxf(m, v[i]), v[i + 1]);
+  if constexpr (N % 2 == 1) m = fmaxf(m, v[N - 1]);
+  return m;
+}
+
 // Reduce over the four lane groups (l % 16 fixed).
 __device__ __forceinline__ float max_groups(float v) { return max_xor32(max_xor16(v)); }
 __device__ __forceinline__ float sum_groups(float v) { return sum_xor32(sum_xor16(v)); }

@@ -11,6 +11,8 @@
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
+#include <type_traits>
+
 namespace msa {
 namespace {
 
@@ -35,6 +37,10 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 // A workgroup owns TQ = 256 / R query rows for all R groups (256 columns; wave w takes
 // columns 64w..64w+63 as four 16-column N-tiles) and one chunk of keys. The k_idx tile
 // is staged once in LDS (double-buffered) and feeds every group: the index key is shared.
+// Pooled maxima are collected in LDS for OUT_RUN consecutive blocks and written as
+// contiguous runs of each output row.
+constexpr int OUT_RUN = 16;
+
 template <typename E, int DI, int BS>
 __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
   using L = KTile<E, DI>;
@@ -43,6 +49,7 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
   constexpr int BPT = KT / BS;  // blocks per key tile
   constexpr int MPB = BS / 16;  // 16-key row tiles per block
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][KT * L::ROW];
+  __shared__ float s_out[WG_COLS][OUT_RUN + 1];  // padded: conflict-free column writes
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int R = a.h_kv, TQ = WG_COLS / R;
@@ -54,26 +61,22 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
   if (k_begin > p_last) return;  // uniform over the workgroup
   const long k_end = min(k_begin + (long)a.key_chunk, p_last + 1);
   const int n_tiles = (int)((k_end - k_begin + KT - 1) / KT);
+  const long c_begin = k_begin / BS;  // first block of the chunk (a multiple of OUT_RUN)
 
   // B operand: q_idx of this lane's four columns (column = lane % 16 of each N-tile).
   const E *qi = reinterpret_cast<const E *>(a.q_idx);
   F bq[4][DC];
-  long pcol[4];
+  int prel[4];  // column position minus the chunk's first key (clamped to int range)
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int col = w * 64 + nt * 16 + c16, r = col / TQ, t = t0 + col % TQ;
-    pcol[nt] = (long)a.q_start + t;
+    prel[nt] = (int)min((long)a.q_start + t - k_begin, (long)0x3fffffff);
 #pragma unroll
     for (int dc = 0; dc < DC; ++dc)
       bq[nt][dc] = (t < a.n_q)
                        ? load_frag(qi + (((long)b * R + r) * a.n_q + t) * DI + dc * 32 + g * 8)
                        : zero_frag(qi);
   }
-  // This lane writes the pooled value of column (nt = g, c16).
-  const int col_out = w * 64 + g * 16 + c16;
-  const int r_out = col_out / TQ, t_out = t0 + col_out % TQ;
-  float *out_row = a.bmax + (((long)b * R + r_out) * a.n_q + t_out) * (long)a.n_blocks;
-  const bool out_ok = t_out < a.n_q;
 
   const unsigned char *kbase =
       reinterpret_cast<const unsigned char *>(a.k_idx) + (long)b * a.cap * DI * (long)sizeof(E);
@@ -95,56 +98,91 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
       *reinterpret_cast<u32x4 *>(&lds[buf][key * L::ROW + off * 16]) = pre[i];
     }
   };
+  // Write s_out's first n blocks of every column to block columns [c0, c0 + n) of the rows:
+  // four threads per column, 16 columns per wave per pass.
+  auto flush = [&](long c0, int n) {
+    const int j0 = (tid & 3) * 4;
+    for (int col = tid >> 2; col < WG_COLS; col += 64) {
+      const int r = col / TQ, t = t0 + col % TQ;
+      if (t >= a.n_q) continue;
+      const long base = (((long)b * R + r) * a.n_q + t) * (long)a.n_blocks + c0;
+      if (n >= j0 + 4 && c0 + j0 + 4 <= a.n_blocks && ((base + j0) & 3) == 0) {
+        *reinterpret_cast<f32x4 *>(a.bmax + base + j0) =
+            f32x4{s_out[col][j0], s_out[col][j0 + 1], s_out[col][j0 + 2], s_out[col][j0 + 3]};
+      } else {
+        for (int j = j0; j < min(n, j0 + 4); ++j)
+          if (c0 + j < a.n_blocks) a.bmax[base + j] = s_out[col][j];
+      }
+    }
+  };
 
+  const int my_col = w * 64 + g * 16 + c16;  // the column whose pooled value this lane holds
   fetch(0);
   stash(0);
   __syncthreads();
+  int run = 0;  // blocks collected in s_out
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
     if (tile + 1 < n_tiles) fetch(tile + 1);
     const long k0 = k_begin + (long)tile * KT;
+    const int krel = tile * KT;  // k0 - k_begin
     const bool need_mask = k0 + KT - 1 > p_first;
 
-    f32x4 acc[4][4];
+    F af[4][DC];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      F af[DC];
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
-        af[dc] = load_frag(reinterpret_cast<const E *>(
+        af[mt][dc] = load_frag(reinterpret_cast<const E *>(
             &lds[buf][(mt * 16 + c16) * L::ROW + (dc * 32 + g * 8) * (int)sizeof(E)]));
+    f32x4 acc[4][4];  // [mt][nt]: S^T tile of 16 keys x 16 columns
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) c = mfma_chunk(af[dc], bq[nt][dc], c);
+        for (int dc = 0; dc < DC; ++dc) c = mfma_chunk(af[mt][dc], bq[nt][dc], c);
         acc[mt][nt] = c;
       }
-    }
+    // Pool each block: max over its keys (rows), then over the four lane groups.
+    auto pool = [&](auto masked) {
 #pragma unroll
-    for (int blk = 0; blk < BPT; ++blk) {
-      float outv = -INFINITY;
+      for (int blk = 0; blk < BPT; ++blk) {
+        float m[4];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        float m = -INFINITY;
+        for (int nt = 0; nt < 4; ++nt) {
+          float v[4 * MPB];
 #pragma unroll
-        for (int mm = 0; mm < MPB; ++mm) {
-          const int mt = blk * MPB + mm;
+          for (int mm = 0; mm < MPB; ++mm) {
+            const int mt = blk * MPB + mm;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float s = acc[mt][nt][i];
-            if (need_mask && k0 + mt * 16 + g * 4 + i > pcol[nt]) s = -INFINITY;
-            m = fmaxf(m, s);
+            for (int i = 0; i < 4; ++i) v[mm * 4 + i] = acc[mt][nt][i];
+            if constexpr (decltype(masked)::value) {
+              // key offset (mt*16 + g*4 + i) is visible iff it is <= lim
+              const int lim = prel[nt] - krel - (mt * 16 + g * 4);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[mm * 4 + i] = (i <= lim) ? v[mm * 4 + i] : -INFINITY;
+            }
           }
+          m[nt] = max_chain<4 * MPB>(v);
         }
-        m = max_groups(m);
-        outv = (g == nt) ? m : outv;
+        s_out[my_col][run + blk] = max_groups_transpose(m[0], m[1], m[2], m[3]);
       }
-      const long c = k0 / BS + blk;
-      if (out_ok && c < a.n_blocks) out_row[c] = outv;
-    }
+    };
+    if (need_mask)
+      pool(std::true_type{});
+    else
+      pool(std::false_type{});
+    run += BPT;
     if (tile + 1 < n_tiles) stash(buf ^ 1);
     __syncthreads();
+    if (run == OUT_RUN || tile + 1 == n_tiles) {
+      const long c0 = c_begin + (long)(tile + 1) * BPT - run;
+      flush(c0, run);
+      run = 0;
+      __syncthreads();
+    }
   }
 }
 

@@ -39,6 +39,35 @@ struct AttnArgs {
   float scale_log2;    // log2(e) / sqrt(DH)
 };
 
+struct KvArgs {          // KV-outer prefill attention
+  const void *q, *k, *v;
+  const int32_t *sel;
+  void *o;
+  float *lse;
+  int32_t *cnt;          // [NB] entries per (b, r, block); cursor follows it: [NB]
+  int32_t *cursor;
+  int32_t *boff;         // [NB + 1] first entry of each block's list
+  int32_t *coff;         // [NB + 1] first chunk of each block
+  int32_t *list;         // [entries] row * 64 + slot, grouped by block
+  int32_t *cmap;         // [chunks] list index of each chunk
+  void *part_o;          // [B*R*n_q*top_k][G][DH] unnormalised partial outputs (dtype)
+  float *part_ml;        // [B*R*n_q*top_k][G][2] (max in log2 units, sum)
+  int batch, n_q, n_k, q_start, h_q, h_kv, block_size, top_k, cap, n_blocks;
+  int seg_rows;          // lists are keyed (row segment, b, r, block), segment-major
+  int n_seg;
+  float scale_log2;
+};
+
+struct KvLayout {
+  size_t cnt, boff, coff, cmap, list, part_o, part_ml, total;
+};
+
+// Rows per list segment for a prefill of this size (a multiple of the list-build tile).
+int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long group, long d_h,
+                    long elem_bytes);
+size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
+                          long d_h, long elem_bytes, KvLayout *lay);
+
 constexpr int TOPK_CHUNK = 2048;  // candidate blocks one wave ranks at a time
 
 // Each launcher validates nothing (the C-ABI layer did) and returns the launch status.
@@ -48,7 +77,7 @@ hipError_t launch_index_prefill(const IndexArgs &a, int dtype, int d_idx, int bl
 hipError_t launch_index_decode(const IndexArgs &a, int dtype, int d_idx, int block_size,
                                hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
-hipError_t launch_attn_prefill(const AttnArgs &a, int dtype, int d_h, hipStream_t s);
+hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s);
 
 }  // namespace msa

@@ -1,0 +1,607 @@
+// msa_kvouter.hip -- main branch for prefill, organised KV-block-outer.
+//
+// The attention itself is the main-branch equation of "MiniMax-M3: MSA 技术报告速读"
+// (section 核心机制): each head h of group r attends, for row t, to the visible tokens of
+// the blocks in sel[b, r, t, :]. The organisation follows the kernel notes of the same
+// page (section Kernel): every selected KV block gathers the query rows that chose it so
+// the matrix cores see full tiles, and a fixed split with a second merge stage replaces
+// atomic accumulation.
+//
+//   1. The list build inverts sel into per-(row segment, b, r, block) lists of
+//      (row, slot) entries: per-workgroup LDS histograms, one workgroup's exclusive scan,
+//      then a fill. Integer atomics only place entries; their order inside a list does not
+//      change any result. Lists are keyed segment-major so that chunks processed at the
+//      same time share a row segment: a small slice of Q and of the partial buffers.
+//   2. kv_attend (persistent): a workgroup takes chunks of up to CHUNK entries of one list,
+//      stages the block's K (row-major) and V (transposed) in LDS once, and each wave keeps
+//      the block's K and V^T fragments in registers while it runs 16-row tiles (16/G rows
+//      x the G heads of the group): S^T = K Q^T, a softmax over the block, O^T = V^T P^T.
+//      It writes, for every (row, slot, head), the block's unnormalised output sum_j p_j v_j
+//      and (m, l) with p_j = 2^(z_j - m), l = sum_j p_j (log2 units).
+//   3. kv_merge: one wave per (b, r, row) combines the row's partials in slot order with
+//      weights 2^(m_s - M): O = sum_s w_s o_s / sum_s w_s l_s, LSE = (M + log2 L) ln 2.
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+
+#include <algorithm>
+
+namespace msa {
+namespace {
+
+constexpr int CHUNK = 128;                // entries per kv_attend work item
+constexpr int HIST_ROWS_ENTRIES = 32768;  // entries per list-build workgroup
+constexpr int HIST_MAX_BLOCKS = 32768;    // LDS histogram capacity (128 KiB)
+
+__global__ void fill_i32(int32_t *p, long n, int32_t v) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// List index of (b, r, row t, block c): segment-major.
+__device__ __forceinline__ long list_index(const KvArgs &a, long br, int t, int c) {
+  const long seg = t / a.seg_rows;
+  return (seg * ((long)a.batch * a.h_kv) + br) * a.n_blocks + c;
+}
+
+// ---------------------------------------------------------------- list build
+
+// Fallback for more blocks than an LDS histogram holds: one counter update per entry.
+__global__ __launch_bounds__(256) void kv_count(KvArgs a) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)a.batch * a.h_kv * a.n_q * a.top_k;
+  if (e >= total) return;
+  const int c = a.sel[e];
+  if (c < 0 || c >= a.n_blocks) return;
+  const long row = e / a.top_k;
+  atomicAdd(&a.cnt[list_index(a, row / a.n_q, (int)(row % a.n_q), c)], 1);
+}
+
+__global__ __launch_bounds__(256) void kv_fill(KvArgs a) {
+  const long e = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)a.batch * a.h_kv * a.n_q * a.top_k;
+  if (e >= total) return;
+  const int c = a.sel[e];
+  if (c < 0 || c >= a.n_blocks) return;
+  const long row = e / a.top_k;
+  const int t = (int)(row % a.n_q);
+  const long i = list_index(a, row / a.n_q, t, c);
+  const int pos = a.boff[i] + atomicAdd(&a.cursor[i], 1);
+  a.list[pos] = t * 64 + (int)(e % a.top_k);
+}
+
+__device__ __forceinline__ long hist_rows_per_wg(int top_k) { return max(1, HIST_ROWS_ENTRIES / top_k); }
+
+// Rows of this list-build workgroup (they lie in one row segment); `base` is the list
+// index of block 0 for them.
+__device__ __forceinline__ void hist_rows(const KvArgs &a, long &e_begin, long &e_end, long &base) {
+  const long rows_per_wg = hist_rows_per_wg(a.top_k);
+  const long tiles_per_br = (a.n_q + rows_per_wg - 1) / rows_per_wg;
+  const long br = blockIdx.x / tiles_per_br;
+  const long r0 = (blockIdx.x % tiles_per_br) * rows_per_wg;
+  const long r1 = min((long)a.n_q, r0 + rows_per_wg);
+  e_begin = (br * a.n_q + r0) * a.top_k;
+  e_end = (br * a.n_q + r1) * a.top_k;
+  base = list_index(a, br, (int)r0, 0);
+}
+
+__global__ __launch_bounds__(1024) void kv_count_hist(KvArgs a) {
+  extern __shared__ int32_t s_hist[];
+  long e0, e1, base;
+  hist_rows(a, e0, e1, base);
+  for (int c = threadIdx.x; c < a.n_blocks; c += 1024) s_hist[c] = 0;
+  __syncthreads();
+  for (long e = e0 + threadIdx.x; e < e1; e += 1024) {
+    const int c = a.sel[e];
+    if (c >= 0 && c < a.n_blocks) atomicAdd(&s_hist[c], 1);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.n_blocks; c += 1024)
+    if (s_hist[c]) atomicAdd(&a.cnt[base + c], s_hist[c]);
+}
+
+__global__ __launch_bounds__(1024) void kv_fill_hist(KvArgs a) {
+  extern __shared__ int32_t s_hist[];
+  long e0, e1, base;
+  hist_rows(a, e0, e1, base);
+  for (int c = threadIdx.x; c < a.n_blocks; c += 1024) s_hist[c] = 0;
+  __syncthreads();
+  for (long e = e0 + threadIdx.x; e < e1; e += 1024) {
+    const int c = a.sel[e];
+    if (c >= 0 && c < a.n_blocks) atomicAdd(&s_hist[c], 1);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.n_blocks; c += 1024) {  // reserve this workgroup's ranges
+    const int n = s_hist[c];
+    if (n) s_hist[c] = a.boff[base + c] + atomicAdd(&a.cursor[base + c], n);
+  }
+  __syncthreads();
+  for (long e = e0 + threadIdx.x; e < e1; e += 1024) {
+    const int c = a.sel[e];
+    if (c >= 0 && c < a.n_blocks) {
+      const int pos = atomicAdd(&s_hist[c], 1);
+      a.list[pos] = (int)((e / a.top_k) % a.n_q) * 64 + (int)(e % a.top_k);
+    }
+  }
+}
+
+// Exclusive scans of the per-list entry counts and chunk counts, and the chunk -> list
+// map (one workgroup; each thread owns a contiguous run of lists, read four at a time).
+__global__ __launch_bounds__(1024) void kv_scan(KvArgs a) {
+  __shared__ long s_pairs[1024];
+  __shared__ long s_chunks[1024];
+  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
+  const int tid = threadIdx.x;
+  const long seg = ((NB + 1023) / 1024 + 3) / 4 * 4;  // a multiple of 4: aligned int4 reads
+  const long i0 = min(NB, tid * seg), i1 = min(NB, i0 + seg);
+  long sp = 0, sc = 0;
+  for (long i = i0; i < i1; i += 4) {
+    if (i + 4 <= i1) {
+      const int4 n = *reinterpret_cast<const int4 *>(a.cnt + i);
+      sp += (long)n.x + n.y + n.z + n.w;
+      sc += (n.x + CHUNK - 1) / CHUNK + (n.y + CHUNK - 1) / CHUNK + (n.z + CHUNK - 1) / CHUNK +
+            (n.w + CHUNK - 1) / CHUNK;
+    } else {
+      for (long j = i; j < i1; ++j) {
+        sp += a.cnt[j];
+        sc += (a.cnt[j] + CHUNK - 1) / CHUNK;
+      }
+    }
+  }
+  s_pairs[tid] = sp;
+  s_chunks[tid] = sc;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const long vp = tid >= off ? s_pairs[tid - off] : 0;
+    const long vc = tid >= off ? s_chunks[tid - off] : 0;
+    __syncthreads();
+    s_pairs[tid] += vp;
+    s_chunks[tid] += vc;
+    __syncthreads();
+  }
+  long rp = s_pairs[tid] - sp, rc = s_chunks[tid] - sc;
+  for (long i = i0; i < i1; ++i) {
+    const int n = a.cnt[i];
+    const int nc = (n + CHUNK - 1) / CHUNK;
+    a.boff[i] = (int32_t)rp;
+    a.coff[i] = (int32_t)rc;
+    for (int j = 0; j < nc; ++j) a.cmap[rc + j] = (int32_t)i;
+    rp += n;
+    rc += nc;
+  }
+  if (tid == 1023) {
+    a.boff[NB] = (int32_t)s_pairs[1023];
+    a.coff[NB] = (int32_t)s_chunks[1023];
+  }
+}
+
+// ---------------------------------------------------------------- attention per block
+
+template <typename E, int DH, int BS>
+struct KvLds {
+  static constexpr int ES = (int)sizeof(E);
+  static constexpr int KROW = DH * ES + 16;                  // K row-major, padded rows
+  static constexpr int VROW = BS * ES + (ES == 2 ? 8 : 16);  // V^T rows (one per d)
+  static constexpr int K_BYTES = BS * KROW;
+  static constexpr int V_BYTES = DH * VROW;
+};
+
+// Stage block rows [kb, kb+BS) of K (row-major) and V (transposed) into LDS, 256 threads.
+template <typename E, int DH, int BS>
+__device__ __forceinline__ void stage_block(const E *kp, const E *vp, long kb, int n_k,
+                                            unsigned char *ks, unsigned char *vt) {
+  using L = KvLds<E, DH, BS>;
+  const int tid = threadIdx.x;
+  constexpr int KPIECES = BS * DH * L::ES / 16;
+  constexpr int PER_ROW = DH * L::ES / 16;
+  for (int pc = tid; pc < KPIECES; pc += 256) {
+    const int key = pc / PER_ROW, off = pc % PER_ROW;
+    const long j = kb + key;
+    const u32x4 x = j < n_k ? *reinterpret_cast<const u32x4 *>(
+                                  reinterpret_cast<const unsigned char *>(kp + j * DH) + off * 16)
+                            : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4 *>(ks + key * L::KROW + off * 16) = x;
+  }
+  if constexpr (L::ES == 2) {
+    constexpr int PAIRS = BS / 2, VPIECES = PAIRS * (DH / 8);
+    for (int pc = tid; pc < VPIECES; pc += 256) {
+      const int kpair = pc % PAIRS, d0 = (pc / PAIRS) * 8;
+      const long j0 = kb + 2 * kpair, j1 = j0 + 1;
+      const u32x4 x = j0 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 y = j1 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e) * L::VROW + kpair * 4) =
+            (x[e] & 0xffffu) | (y[e] << 16);
+        *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e + 1) * L::VROW + kpair * 4) =
+            (x[e] >> 16) | (y[e] & 0xffff0000u);
+      }
+    }
+  } else {
+    constexpr int VPIECES = BS * (DH / 4);
+    for (int pc = tid; pc < VPIECES; pc += 256) {
+      const int key = pc % BS, d0 = (pc / BS) * 4;
+      const long j = kb + key;
+      const f32x4 x = j < n_k ? *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(vp) + j * DH + d0)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *reinterpret_cast<float *>(vt + (d0 + e) * L::VROW + key * 4) = x[e];
+    }
+  }
+}
+
+// V^T fragment for d-row `row` and 32-key step ks: keys 32ks+4g+0..3, then 32ks+16+4g+0..3
+// (the order in which the S^T accumulators hold P^T).
+__device__ __forceinline__ bf16x8 vt_frag(const unsigned char *row, int ks, int g, const bf16_t *) {
+  const u32x2 lo = *reinterpret_cast<const u32x2 *>(row + (32 * ks + 4 * g) * 2);
+  const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + (32 * ks + 16 + 4 * g) * 2);
+  return __builtin_bit_cast(bf16x8, (u32x4{lo[0], lo[1], hi[0], hi[1]}));
+}
+__device__ __forceinline__ f32x8 vt_frag(const unsigned char *row, int ks, int g, const float *) {
+  const f32x4 lo = *reinterpret_cast<const f32x4 *>(row + (32 * ks + 4 * g) * 4);
+  const f32x4 hi = *reinterpret_cast<const f32x4 *>(row + (32 * ks + 16 + 4 * g) * 4);
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ bf16x8 pt_frag(f32x4 a, f32x4 b, const bf16_t *) {
+  return __builtin_bit_cast(bf16x8, (u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                           pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])}));
+}
+__device__ __forceinline__ f32x8 pt_frag(f32x4 a, f32x4 b, const float *) {
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void store4(bf16_t *dst, f32x4 v) {
+  *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void store4(float *dst, f32x4 v) { *reinterpret_cast<f32x4 *>(dst) = v; }
+
+// REG_KV: keep the block's K and V^T fragments in registers across tiles (fewer LDS reads,
+// fewer resident waves) instead of re-reading them from LDS per tile.
+template <typename E, int DH, int BS, bool REG_KV>
+__global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
+  using F = typename Frag<E>::type;
+  using L = KvLds<E, DH, BS>;
+  constexpr int DC = DH / 32, KTN = BS / 16, DT = DH / 16, KS = BS / 32;
+  constexpr int OROW = DH * L::ES + 16;  // one output row in the store-staging buffer
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[L::K_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[L::V_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char s_o[4][16 * OROW];  // per wave
+  __shared__ int32_t s_list[CHUNK];
+
+  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
+  const int n_chunks = a.coff[NB];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int G = 1 << log2g, QPT = 16 >> log2g;
+  const int qi = c16 >> log2g, hd = c16 & (G - 1);
+  const E *q = reinterpret_cast<const E *>(a.q);
+  const float cs = a.scale_log2;
+
+  for (int chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {  // uniform loop
+    const long i = a.cmap[chunk];
+    const int c = (int)(i % a.n_blocks);
+    const long br = (i / a.n_blocks) % ((long)a.batch * a.h_kv);
+    const int r = (int)(br % a.h_kv), b = (int)(br / a.h_kv);
+    const int e0 = a.boff[i] + (chunk - a.coff[i]) * CHUNK;
+    const int n_e = min(e0 + CHUNK, a.boff[i + 1]) - e0;
+    const long plane = ((long)b * a.h_kv + r) * (long)a.cap * DH;
+    const E *kp = reinterpret_cast<const E *>(a.k) + plane;
+    const E *vp = reinterpret_cast<const E *>(a.v) + plane;
+    const long kb = (long)c * BS;
+    const int h = r * G + hd;
+
+    __syncthreads();  // the previous chunk is done with the LDS buffers
+    if (tid < n_e) s_list[tid] = a.list[e0 + tid];
+    stage_block<E, DH, BS>(kp, vp, kb, a.n_k, s_k, s_v);
+    __syncthreads();
+
+    F kf[REG_KV ? KTN : 1][REG_KV ? DC : 1];
+    F vf[REG_KV ? DT : 1][REG_KV ? KS : 1];
+    if constexpr (REG_KV) {
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt)
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc)
+          kf[kt][dc] = load_frag(reinterpret_cast<const E *>(s_k + (kt * 16 + c16) * L::KROW +
+                                                            (dc * 32 + g * 8) * L::ES));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) vf[dt][ks] = vt_frag(s_v + (dt * 16 + c16) * L::VROW, ks, g, kp);
+    }
+
+    const int n_tiles = (n_e + QPT - 1) / QPT;
+    auto load_q = [&](int tt, F (&dst)[DC]) {
+      const int e = tt * QPT + qi;
+      const bool ok = tt < n_tiles && e < n_e;
+      const int t = ok ? (s_list[e] >> 6) : 0;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        dst[dc] = ok ? load_frag(q + (((long)b * a.h_q + h) * a.n_q + t) * DH + dc * 32 + g * 8)
+                     : zero_frag(q);
+    };
+    F bq[DC], bq_next[DC];
+    load_q(w, bq);
+    for (int tt = w; tt < n_tiles; tt += 4) {
+      load_q(tt + 4, bq_next);  // in flight while this tile computes
+      const int e = tt * QPT + qi;
+      const bool valid = e < n_e;
+      const int ent = valid ? s_list[e] : 0;
+      const int t = ent >> 6, slot = ent & 63;
+      const long p = (long)a.q_start + t;
+
+      f32x4 s[KTN];
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) {
+          F af;
+          if constexpr (REG_KV)
+            af = kf[kt][dc];
+          else
+            af = load_frag(reinterpret_cast<const E *>(s_k + (kt * 16 + c16) * L::KROW +
+                                                      (dc * 32 + g * 8) * L::ES));
+          acc = mfma_chunk(af, bq[dc], acc);
+        }
+        s[kt] = acc;
+      }
+      // Rows that need masking (their own block, or no entry) are rare: one uniform test.
+      const bool fix = !valid || kb + BS - 1 > p;
+      if (ballot(fix)) {
+        const int lim = valid ? (int)min(p - kb, (long)BS) : -1;  // key offset visible iff <= lim
+#pragma unroll
+        for (int kt = 0; kt < KTN; ++kt)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            if (kt * 16 + g * 4 + ii > lim) s[kt][ii] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt) mx = fmaxf(mx, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
+      mx = max_groups(mx);
+      const float m = mx == -INFINITY ? 0.f : mx * cs;  // log2 units
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float pz = __builtin_amdgcn_exp2f(fmaf(s[kt][ii], cs, -m));  // exp2(-inf) = 0
+          s[kt][ii] = pz;
+          rs += pz;
+        }
+      rs = sum_groups(rs);
+      f32x4 o[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const F bp = pt_frag(s[2 * ks], s[2 * ks + 1], kp);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          F av;
+          if constexpr (REG_KV)
+            av = vf[dt][ks];
+          else
+            av = vt_frag(s_v + (dt * 16 + c16) * L::VROW, ks, g, kp);
+          o[dt] = mfma_chunk(av, bp, o[dt]);
+        }
+      }
+      // Stage the tile's 16 output rows in LDS, then write each entry's G x DH block with
+      // contiguous 16-byte pieces (consecutive lanes, consecutive addresses).
+      unsigned char *so = s_o[w];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) store4(reinterpret_cast<E *>(so + c16 * OROW) + dt * 16 + g * 4, o[dt]);
+      if (valid && g == 0) {
+        const long ps = ((((long)b * a.h_kv + r) * a.n_q + t) * a.top_k + slot) * G + hd;
+        reinterpret_cast<float2 *>(a.part_ml)[ps] = make_float2(rs > 0.f ? m : -INFINITY, rs);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // wave-private buffer: in-order LDS
+      {
+        constexpr int PIECES_ROW = DH * L::ES / 16;  // 16-byte pieces per output row
+        const int pieces = 16 * PIECES_ROW;          // the whole tile
+        for (int pc = lane; pc < pieces; pc += 64) {
+          const int row = pc / PIECES_ROW, off = pc % PIECES_ROW;
+          const int qq = row >> log2g, hh = row & (G - 1);
+          const int ee = tt * QPT + qq;
+          if (ee < n_e) {
+            const int en = s_list[ee];
+            const long pss = ((((long)b * a.h_kv + r) * a.n_q + (en >> 6)) * a.top_k + (en & 63)) * G + hh;
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.part_o) + pss * DH * L::ES + off * 16) =
+                *reinterpret_cast<const u32x4 *>(so + row * OROW + off * 16);
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) bq[dc] = bq_next[dc];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- merge
+
+template <typename E>
+__device__ __forceinline__ void load8(const E *p, float (&x)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t *p, float (&x)[8]) {
+  const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(v[e] << 16);
+    x[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, float (&x)[8]) {
+  const f32x4 u = *reinterpret_cast<const f32x4 *>(p), v = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = u[e];
+    x[4 + e] = v[e];
+  }
+}
+
+// One wave per (b, r, row): lane covers EPL consecutive outputs of one head,
+// EPL = max(8, G * DH / 64).
+template <typename E, int DH, int EPL>
+__global__ __launch_bounds__(256) void kv_merge(KvArgs a, int log2g) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + w;  // (b, r, t)
+  if (row >= (long)a.batch * a.h_kv * a.n_q) return;
+  const int G = 1 << log2g;
+  if (lane * EPL >= G * DH) return;  // idle lanes (no cross-lane work below)
+  const int hd = (lane * EPL) / DH;
+  const int d0 = (lane * EPL) % DH;
+  const int t = (int)(row % a.n_q);
+  const long br = row / a.n_q;
+  const int r = (int)(br % a.h_kv), b = (int)(br / a.h_kv);
+  const int32_t *sel = a.sel + row * a.top_k;
+  uint64_t valid = 0;  // valid slots as a bit mask (top_k <= 64)
+  for (int s = 0; s < a.top_k; ++s) {
+    const int c = sel[s];
+    if (c >= 0 && c < a.n_blocks) valid |= 1ull << s;
+  }
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row * a.top_k * G + hd;
+  const E *pbase = reinterpret_cast<const E *>(a.part_o) + (row * a.top_k * G + hd) * DH + d0;
+  float acc[EPL];
+#pragma unroll
+  for (int x = 0; x < EPL; ++x) acc[x] = 0.f;
+  float M = -INFINITY, Ls = 0.f;
+  constexpr int U = 8;  // slots whose loads are in flight together
+  uint64_t v = valid;
+  while (v) {
+    int sl[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      sl[u] = v ? __builtin_ctzll(v) : -1;
+      v &= v - 1;  // no-op once v is 0
+    }
+    float2 mls[U];
+    float part[U][EPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      mls[u] = sl[u] >= 0 ? ml[(long)sl[u] * G] : make_float2(-INFINITY, 0.f);
+      if (sl[u] >= 0) {
+        const E *po = pbase + (long)sl[u] * G * DH;
+#pragma unroll
+        for (int x8 = 0; x8 < EPL; x8 += 8) {
+          float tmp[8];
+          load8<E>(po + x8, tmp);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part[u][x8 + e] = tmp[e];
+        }
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (mls[u].y > 0.f) Mb = fmaxf(Mb, mls[u].x);
+    const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);  // rescale earlier slots
+    Ls *= sc;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) acc[x] *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (mls[u].y > 0.f) {
+        const float wgt = __builtin_amdgcn_exp2f(mls[u].x - Mb);
+        Ls += wgt * mls[u].y;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) acc[x] += wgt * part[u][x];
+      }
+    }
+    M = Mb;
+  }
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  E *o = reinterpret_cast<E *>(a.o) + (((long)b * a.h_q + r * G + hd) * a.n_q + t) * DH + d0;
+#pragma unroll
+  for (int x4 = 0; x4 < EPL; x4 += 4) {
+    const f32x4 v4 = {acc[x4] * inv, acc[x4 + 1] * inv, acc[x4 + 2] * inv, acc[x4 + 3] * inv};
+    store4(o + x4, v4);
+  }
+  if (a.lse && d0 == 0)
+    a.lse[((long)b * a.h_q + r * G + hd) * a.n_q + t] = (M + __log2f(Ls)) * 0.69314718055994531f;
+}
+
+template <typename E, int DH, int BS>
+hipError_t run_kv(const KvArgs &a, int log2g, hipStream_t s) {
+  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
+  const long entries = (long)a.batch * a.h_kv * a.n_q * a.top_k;
+  hipLaunchKernelGGL(fill_i32, dim3((unsigned)std::min(4096L, (2 * NB + 255) / 256)), dim3(256), 0, s,
+                     a.cnt, 2 * NB, 0);  // cnt and cursor are adjacent
+  if (a.n_blocks <= HIST_MAX_BLOCKS) {
+    const long rows_per_wg = std::max(1, HIST_ROWS_ENTRIES / a.top_k);  // divides seg_rows
+    const unsigned wgs = (unsigned)((long)a.batch * a.h_kv * ((a.n_q + rows_per_wg - 1) / rows_per_wg));
+    const size_t lds = (size_t)a.n_blocks * sizeof(int32_t);
+    hipLaunchKernelGGL(kv_count_hist, dim3(wgs), dim3(1024), lds, s, a);
+    hipLaunchKernelGGL(kv_scan, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(kv_fill_hist, dim3(wgs), dim3(1024), lds, s, a);
+  } else {
+    const unsigned eg = (unsigned)((entries + 255) / 256);
+    hipLaunchKernelGGL(kv_count, dim3(eg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(kv_scan, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(kv_fill, dim3(eg), dim3(256), 0, s, a);
+  }
+  // persistent: a few workgroups per CU loop over the chunks
+  const long max_chunks = (entries + CHUNK - 1) / CHUNK + NB;
+  const unsigned grid = (unsigned)std::min(max_chunks, 256L * 8);
+  hipLaunchKernelGGL((kv_attend<E, DH, BS, false>), dim3(grid), dim3(256), 0, s, a, log2g);
+  const long rows = (long)a.batch * a.h_kv * a.n_q;
+  const dim3 mg((unsigned)((rows + 3) / 4));
+  const int epl = std::max(8, (DH << log2g) >> 6);
+  if (epl == 8)
+    hipLaunchKernelGGL((kv_merge<E, DH, 8>), mg, dim3(256), 0, s, a, log2g);
+  else if (epl == 16)
+    hipLaunchKernelGGL((kv_merge<E, DH, 16>), mg, dim3(256), 0, s, a, log2g);
+  else
+    hipLaunchKernelGGL((kv_merge<E, DH, 32>), mg, dim3(256), 0, s, a, log2g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long group, long d_h,
+                    long elem_bytes) {
+  // about 1 GiB of partial outputs per segment, in whole list-build tiles
+  const long tile = std::max(1, HIST_ROWS_ENTRIES / (int)top_k);
+  const long per_row = batch * h_kv * top_k * group * d_h * elem_bytes;
+  long rows = std::max(1L, (1L << 30) / per_row);
+  rows = std::max(tile, rows / tile * tile);
+  return (int)std::min(rows, ((n_q + tile - 1) / tile) * tile);
+}
+
+size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
+                          long d_h, long elem_bytes, KvLayout *lay) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const long seg_rows = kv_segment_rows(batch, h_kv, n_q, top_k, group, d_h, elem_bytes);
+  const long n_seg = (n_q + seg_rows - 1) / seg_rows;
+  const size_t NB = (size_t)(n_seg * batch * h_kv * n_blocks);
+  const size_t slots = (size_t)(batch * h_kv * n_q * top_k);
+  const size_t max_chunks = (slots + CHUNK - 1) / CHUNK + NB;
+  KvLayout L;
+  size_t o = 0;
+  L.cnt = o;     o += al(2 * NB * 4);  // cnt, then cursor
+  L.boff = o;    o += al((NB + 1) * 4);
+  L.coff = o;    o += al((NB + 1) * 4);
+  L.cmap = o;    o += al(max_chunks * 4);
+  L.list = o;    o += al(slots * 4);
+  L.part_o = o;  o += al(slots * (size_t)group * (size_t)d_h * (size_t)elem_bytes);
+  L.part_ml = o; o += al(slots * (size_t)group * 8);
+  L.total = o;
+  if (lay) *lay = L;
+  return o;
+}
+
+hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, hipStream_t s) {
+  int lg = 0;
+  while ((1 << lg) < a.h_q / a.h_kv) ++lg;
+#define MSA_KV(E, DH)                                                             \
+  if (a.block_size == 32) return run_kv<E, DH, 32>(a, lg, s);                     \
+  return run_kv<E, DH, 64>(a, lg, s);
+  if (dtype == 0) {
+    if (d_h == 64) { MSA_KV(float, 64) }
+    MSA_KV(float, 128)
+  }
+  if (d_h == 64) { MSA_KV(bf16_t, 64) }
+  MSA_KV(bf16_t, 128)
+#undef MSA_KV
+}
+
+}  // namespace msa

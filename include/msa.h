@@ -32,8 +32,8 @@
  *
  * Supported set: dtype F32 or BF16; d_h in {64, 128}; d_idx in {32, 64};
  * block_size in {32, 64}; 1 <= top_k <= 64; h_kv and h_q / h_kv in
- * {1, 2, 4, 8, 16}; top_k * (16 / (h_q / h_kv)) <= 128 for prefill; at most
- * 2048 * 2048 / (top_k - 1) candidate blocks before the last row's own block.
+ * {1, 2, 4, 8, 16}; at most 2048 * 2048 / (top_k - 1) candidate blocks before the
+ * last row's own block.
  */
 #ifndef MSA_H
 #define MSA_H
@@ -120,8 +120,10 @@ int msa_topk_from_block_scores(const msa_shape *shape, const float *block_scores
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Workspace bytes the attention entry points need for `shape` (split partials
- * of the decode path; 0 for prefill). Returns MSA_OK and writes *bytes.
+ * Workspace bytes the attention entry points need for `shape`: the prefill lists
+ * and partials, or for a decode shape (n_q == 1, q_start == n_k - 1) the larger of
+ * that and the decode split partials, so either entry point can use it.
+ * Returns MSA_OK and writes *bytes.
  */
 int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes);
 
@@ -133,7 +135,12 @@ int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes);
  *            valid entry must be a block whose first key is <= p)
  *   o        out, dtype of q; rounded to nearest even for bf16
  *   lse      optional out (NULL to skip): natural-log sum of exp of the scaled scores
- *   workspace unused (pass NULL, 0).
+ *   workspace at least msa_sparse_attn_workspace_size bytes: the per-block query lists
+ *            and one normalised partial output per (row, group, selected block), i.e.
+ *            about batch * h_kv * n_q * top_k * (h_q / h_kv) * d_h * sizeof(dtype) bytes.
+ * Computed KV-block-outer: each selected block is staged once per chunk of the rows that
+ * chose it, and the partials are merged with log-sum-exp weights (no float atomics).
+ * At most 2^31 selection entries (batch * h_kv * n_q * top_k) and n_q < 2^25 per call.
  */
 int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k, const void *v,
                             const int32_t *sel, void *o, float *lse, void *workspace,

@@ -47,6 +47,9 @@ SMALL = [
       top_k=4, idx_range=3, qkv_scale=1.0),
     W("prefill_two_level_topk", n_q=64, n_k=70064, q_start=70000, block_size=32, d_idx=32,
       top_k=32, needles=16),
+    # more than 32768 key blocks: the list build falls back to per-entry counters
+    W("prefill_many_blocks", n_q=40, n_k=(1 << 20) + 96, q_start=(1 << 20) + 56, h_q=8,
+      h_kv=2, d_h=64, d_idx=32, block_size=32, top_k=16, needles=8),
 ]
 
 
@@ -133,7 +136,8 @@ def test_decode_equals_prefill_last_row():
     s = msa.shape_of(w)
     buf = msa.Buffers(s)
     msa.msa_index_topk(s, inp["q_idx"], inp["k_idx"], buf.sel, None, buf.ws_index)
-    msa.msa_sparse_attn_prefill(s, inp["q"], inp["k"], inp["v"], buf.sel, buf.o, buf.lse)
+    msa.msa_sparse_attn_prefill(s, inp["q"], inp["k"], inp["v"], buf.sel, buf.o, buf.lse,
+                                buf.ws_attn)
     torch.cuda.synchronize()
     assert torch.equal(dec.sel, buf.sel)
     assert (dec.o.float() - buf.o.float()).abs().max().item() <= 1e-2
