@@ -73,7 +73,19 @@ int topk_chunks(const msa_shape &s) {
 
 struct IndexWs {
   size_t bmax, cand, total;
+  size_t dec_cand;  // fused decode path: candidate pairs of every index-select workgroup
+  bool fused;       // the fused decode path applies
 };
+
+// Fused decode selection: one query row, its candidates fit one merge pass.
+int decode_select_wgs(const msa_shape &s) {
+  const long long blocks = (long long)s.q_start / s.block_size + 1;
+  return (int)((blocks + msa::SEL_NBLK - 1) / msa::SEL_NBLK);
+}
+bool fused_decode_ok(const msa_shape &s) {
+  return s.n_q == 1 && s.top_k > 1 &&
+         (long long)decode_select_wgs(s) * (s.top_k - 1) <= msa::TOPK_CHUNK;
+}
 
 int index_ws(const msa_shape &s, bool with_bmax, IndexWs *w) {
   const long long rows = (long long)s.batch * s.h_kv * s.n_q;
@@ -84,6 +96,9 @@ int index_ws(const msa_shape &s, bool with_bmax, IndexWs *w) {
   w->bmax = with_bmax ? align_up((size_t)rows * (size_t)n_blocks(s) * sizeof(float)) : 0;
   w->cand = nch > 1 ? align_up((size_t)rows * nch * (s.top_k - 1) * 4) : 0;
   w->total = w->bmax + 2 * w->cand;
+  w->fused = fused_decode_ok(s);
+  w->dec_cand = w->fused ? align_up((size_t)rows * decode_select_wgs(s) * (s.top_k - 1) * 4) : 0;
+  if (2 * w->dec_cand > w->total) w->total = 2 * w->dec_cand;
   return MSA_OK;
 }
 
@@ -169,7 +184,7 @@ int msa_index_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
 static int launch_scores(const msa_shape &s, const void *q_idx, const void *k_idx, float *bmax,
                          hipStream_t st) {
   msa::IndexArgs ia{q_idx, k_idx, bmax, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
-                    (int)n_blocks(s), cap_of(s), 0};
+                    (int)n_blocks(s), cap_of(s), 0, nullptr, nullptr, s.top_k};
   hipError_t e;
   if (s.n_q == 1) {
     ia.key_chunk = key_chunk_decode(s);
@@ -185,7 +200,8 @@ static int launch_select(const msa_shape &s, const float *bmax, int32_t *sel, un
                          size_t cand_bytes, hipStream_t st) {
   msa::TopkArgs ta{bmax, sel, reinterpret_cast<uint32_t *>(cand),
                    reinterpret_cast<int32_t *>(cand + cand_bytes), s.batch, s.n_q, s.q_start,
-                   s.h_kv, (int)n_blocks(s), s.block_size, s.top_k, topk_chunks(s)};
+                   s.h_kv, (int)n_blocks(s), s.block_size, s.top_k, topk_chunks(s),
+                   msa::TOPK_CHUNK, 0};
   hipError_t e = msa::launch_topk(ta, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e, "top-k kernel launch");
 }
@@ -204,6 +220,19 @@ int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx,
                 workspace ? workspace_bytes : (size_t)0);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
+  if (!block_scores && w.fused) {  // decode: first selection stage inside the index kernel
+    uint32_t *ck = reinterpret_cast<uint32_t *>(ws);
+    int32_t *ci = reinterpret_cast<int32_t *>(ws + w.dec_cand);
+    msa::IndexArgs ia{q_idx, k_idx, nullptr, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
+                      (int)n_blocks(s), cap_of(s), 0, ck, ci, s.top_k};
+    hipError_t e = msa::launch_index_select_decode(ia, s.dtype, s.d_idx, s.block_size, st);
+    if (e != hipSuccess) return hip_fail(e, "index-select kernel launch");
+    msa::TopkArgs ta{nullptr, sel, ck, ci, s.batch, s.n_q, s.q_start, s.h_kv, (int)n_blocks(s),
+                     s.block_size, s.top_k, decode_select_wgs(s), msa::SEL_NBLK, 1};
+    e = msa::launch_topk_final(ta, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k merge launch");
+    return ok();
+  }
   float *bmax = block_scores ? block_scores : reinterpret_cast<float *>(ws);
   if (block_scores) {
     const long long rows = (long long)s.batch * s.h_kv * s.n_q;
@@ -291,7 +320,7 @@ int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k
   msa::KvArgs a{q, k, v, sel, o, lse, cnt, cnt + NB,
                 reinterpret_cast<int32_t *>(ws + lay.boff), reinterpret_cast<int32_t *>(ws + lay.coff),
                 reinterpret_cast<int32_t *>(ws + lay.list), reinterpret_cast<int32_t *>(ws + lay.cmap),
-                ws + lay.part_o,
+                reinterpret_cast<long *>(ws + lay.tile_sum), ws + lay.part_o,
                 reinterpret_cast<float *>(ws + lay.part_ml), s.batch, s.n_q, s.n_k, s.q_start,
                 s.h_q, s.h_kv, s.block_size, s.top_k, cap_of(s), (int)n_blocks(s), seg_rows,
                 n_seg, (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};

@@ -38,54 +38,64 @@ struct RowState {
   float l;  // running sum of 2^(z - m)
 };
 
-// Stage V rows [kb, kb+BS) transposed into LDS: vt[d][key]. bf16 packs key pairs into dwords.
+// V rows [kb, kb+BS) for one wave: loaded into registers first (so the loads overlap the
+// score MFMAs), then written transposed into a wave-private LDS region vt[d][key].
+template <typename E, int DH, int BS>
+struct VRegs;
 template <int DH, int BS>
-__device__ __forceinline__ void stage_v(const bf16_t *vp, long kb, int n_k, unsigned char *vt) {
-  constexpr int PAIRS = BS / 2, SEGS = 64 / PAIRS, DSEG = DH / SEGS, PIECES = DSEG / 8;
-  constexpr int ROW = VStage<bf16_t, DH, BS>::ROW;
-  const int lane = lane_id(), kp = lane % PAIRS, seg = lane / PAIRS;
-  const long j0 = kb + 2 * kp, j1 = j0 + 1;
+struct VRegs<bf16_t, DH, BS> {  // key pairs packed into dwords
+  static constexpr int PAIRS = BS / 2, SEGS = 64 / PAIRS, DSEG = DH / SEGS, PIECES = DSEG / 8;
   u32x4 a[PIECES], b[PIECES];
+  __device__ __forceinline__ void load(const bf16_t *vp, long kb, int n_k) {
+    const int lane = lane_id(), kp = lane % PAIRS, seg = lane / PAIRS;
+    const long j0 = kb + 2 * kp, j1 = j0 + 1;
 #pragma unroll
-  for (int i = 0; i < PIECES; ++i) {
-    const int d0 = seg * DSEG + i * 8;
-    a[i] = j0 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
-    b[i] = j1 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < PIECES; ++i) {
-    const int d0 = seg * DSEG + i * 8;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t x = a[i][e], y = b[i][e];
-      // element 2e is the low half, 2e+1 the high half of dword e
-      *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e) * ROW + kp * 4) = (x & 0xffffu) | (y << 16);
-      *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e + 1) * ROW + kp * 4) = (x >> 16) | (y & 0xffff0000u);
+    for (int i = 0; i < PIECES; ++i) {
+      const int d0 = seg * DSEG + i * 8;
+      a[i] = j0 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
+      b[i] = j1 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
+  __device__ __forceinline__ void store_t(unsigned char *vt) const {
+    constexpr int ROW = VStage<bf16_t, DH, BS>::ROW;
+    const int lane = lane_id(), kp = lane % PAIRS, seg = lane / PAIRS;
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int d0 = seg * DSEG + i * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = a[i][e], y = b[i][e];
+        // element 2e is the low half, 2e+1 the high half of dword e
+        *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e) * ROW + kp * 4) = (x & 0xffffu) | (y << 16);
+        *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e + 1) * ROW + kp * 4) = (x >> 16) | (y & 0xffff0000u);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+};
 template <int DH, int BS>
-__device__ __forceinline__ void stage_v(const float *vp, long kb, int n_k, unsigned char *vt) {
-  constexpr int SEGS = 64 / BS, DSEG = DH / SEGS, PIECES = DSEG / 4;
-  constexpr int ROW = VStage<float, DH, BS>::ROW;
-  const int lane = lane_id(), key = lane % BS, seg = lane / BS;
-  const long j = kb + key;
+struct VRegs<float, DH, BS> {
+  static constexpr int SEGS = 64 / BS, DSEG = DH / SEGS, PIECES = DSEG / 4;
   f32x4 a[PIECES];
+  __device__ __forceinline__ void load(const float *vp, long kb, int n_k) {
+    const int lane = lane_id(), key = lane % BS, seg = lane / BS;
+    const long j = kb + key;
 #pragma unroll
-  for (int i = 0; i < PIECES; ++i)
-    a[i] = j < n_k ? *reinterpret_cast<const f32x4 *>(vp + j * DH + seg * DSEG + i * 4)
-                   : f32x4{0.f, 0.f, 0.f, 0.f};
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int i = 0; i < PIECES; ++i)
+      a[i] = j < n_k ? *reinterpret_cast<const f32x4 *>(vp + j * DH + seg * DSEG + i * 4)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void store_t(unsigned char *vt) const {
+    constexpr int ROW = VStage<float, DH, BS>::ROW;
+    const int lane = lane_id(), key = lane % BS, seg = lane / BS;
 #pragma unroll
-  for (int i = 0; i < PIECES; ++i)
+    for (int i = 0; i < PIECES; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      *reinterpret_cast<float *>(vt + (seg * DSEG + i * 4 + e) * ROW + key * 4) = a[i][e];
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<float *>(vt + (seg * DSEG + i * 4 + e) * ROW + key * 4) = a[i][e];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+};
 
 // V^T fragment for d-row d and 32-key step ks: keys 32ks+4g+0..3 then 32ks+16+4g+0..3.
 __device__ __forceinline__ bf16x8 vt_frag(const unsigned char *row, int ks, int g, const bf16_t *) {
@@ -119,6 +129,8 @@ __device__ __forceinline__ void attend_block(RowState<E, DH, BS> &st,
   constexpr int DC = DH / 32, KTN = BS / 16, DT = DH / 16;
   const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
 
+  VRegs<E, DH, BS> vr;
+  vr.load(vp, kb, n_k);  // in flight during the score MFMAs
   f32x4 s[KTN];
 #pragma unroll
   for (int kt = 0; kt < KTN; ++kt) {
@@ -160,7 +172,7 @@ __device__ __forceinline__ void attend_block(RowState<E, DH, BS> &st,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) st.o[dt] *= alpha;
 
-  stage_v<DH, BS>(vp, kb, n_k, vt);
+  vr.store_t(vt);
   constexpr int ROW = VStage<E, DH, BS>::ROW;
 #pragma unroll
   for (int ks = 0; ks < BS / 32; ++ks) {
@@ -244,23 +256,34 @@ __global__ __launch_bounds__(256) void attn_decode_merge(AttnArgs a) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long bh = (long)blockIdx.x * 4 + w;
   if (bh >= (long)a.batch * a.h_q) return;
-  const int S = a.splits;
-  const float *ml = a.part_ml + bh * S * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f;
+  const int S = a.splits;  // <= 64
+  const float2 mine = lane < S ? reinterpret_cast<const float2 *>(a.part_ml)[bh * S + lane]
+                               : make_float2(-INFINITY, 0.f);
+  float M = mine.y > 0.f ? mine.x : -INFINITY;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float wl = mine.y > 0.f ? __builtin_amdgcn_exp2f(mine.x - M) : 0.f;  // this split's weight
+  float L = wl * mine.y;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
   constexpr int PER = DH / 64;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ms = ml[2 * s];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
-    L += wgt * ml[2 * s + 1];
-    const float *po = a.part_o + (bh * S + s) * DH;
+  const float *pbase = a.part_o + bh * S * DH + lane;
+  for (int s0 = 0; s0 < S; s0 += 8) {  // eight splits' loads in flight together
+    float wv[8], pv[8][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += wgt * po[lane + 64 * i];
+    for (int u = 0; u < 8; ++u) {
+      const int sp = s0 + u;
+      wv[u] = __shfl(wl, sp & 63);  // 0 for splits past S (their lanes hold weight 0)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) pv[u][i] = (sp < S && wv[u] != 0.f) ? pbase[sp * DH + 64 * i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += wv[u] * pv[u][i];
   }
   const float inv = 1.f / L;
   E *o = reinterpret_cast<E *>(a.o) + bh * DH;

@@ -10,6 +10,7 @@
 // lane's rows followed by two lane-group swaps, not a shuffle reduction over keys.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
+#include "msa_select.hpp"
 
 #include <type_traits>
 
@@ -245,6 +246,126 @@ __global__ __launch_bounds__(256) void index_pool_decode(IndexArgs a) {
   }
 }
 
+// Decode with the first selection stage fused in. Grid: x = range of SEL_NBLK key blocks,
+// z = sequence; 512 threads. Each wave pools 32 blocks for all groups into LDS; then one
+// wave per group ranks the range's blocks before the local block and writes its best
+// top_k - 1 (key, block) pairs; a final merge pass picks the overall best.
+template <typename E, int DI, int BS>
+__global__ __launch_bounds__(512) void index_select_decode(IndexArgs a) {
+  using F = typename Frag<E>::type;
+  constexpr int DC = DI / 32;
+  constexpr int BPT = KT / BS;
+  constexpr int MPB = BS / 16;
+  constexpr int NBW = SEL_NBLK / 8;  // blocks per wave
+  __shared__ float s_m[16][SEL_NBLK];
+  __shared__ uint32_t s_key[8][SELECT_CAP + 1];
+  __shared__ int32_t s_idx[8][SELECT_CAP + 1];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int R = a.h_kv, b = blockIdx.z, wg = blockIdx.x;
+  const long p = a.q_start;
+  const int local = (int)(p / BS);
+  const int c0 = wg * SEL_NBLK;
+
+  for (int x = tid; x < 16 * SEL_NBLK; x += 512) (&s_m[0][0])[x] = -INFINITY;
+  __syncthreads();
+
+  const E *qi = reinterpret_cast<const E *>(a.q_idx);
+  const E *ki = reinterpret_cast<const E *>(a.k_idx) + (long)b * a.cap * DI;
+  F bq[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    bq[dc] = (c16 < R) ? load_frag(qi + (((long)b * R + c16) * a.n_q) * DI + dc * 32 + g * 8)
+                       : zero_frag(qi);
+  const long kw0 = (long)(c0 + w * NBW) * BS;  // this wave's first key
+  constexpr int NT = NBW * BS / KT;            // key tiles per wave
+  auto fetch = [&](int tile, F (&dst)[4][DC]) {
+    const long k0 = kw0 + (long)tile * KT;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const long j = k0 + mt * 16 + c16;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        dst[mt][dc] = (j < a.n_k && j <= p) ? load_frag(ki + j * DI + dc * 32 + g * 8) : zero_frag(ki);
+    }
+  };
+  auto pool = [&](int tile, const F (&cur)[4][DC]) {
+    const long k0 = kw0 + (long)tile * KT;
+    const bool need_mask = k0 + KT - 1 > p;
+#pragma unroll
+    for (int blk = 0; blk < BPT; ++blk) {
+      float v[4 * MPB];
+#pragma unroll
+      for (int mm = 0; mm < MPB; ++mm) {
+        const int mt = blk * MPB + mm;
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) c = mfma_chunk(cur[mt][dc], bq[dc], c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[mm * 4 + i] = (need_mask && k0 + mt * 16 + g * 4 + i > p) ? -INFINITY : c[i];
+      }
+      const float mx = max_groups(max_chain<4 * MPB>(v));
+      if (g == 0 && c16 < R) s_m[c16][w * NBW + tile * BPT + blk] = mx;
+    }
+  };
+  // double-buffered key tiles: the next tile's fragments load while this one computes
+  const int nt = (int)min((long)NT, (p - kw0) / KT + 1);  // tiles with a visible key
+  F fa[4][DC], fb[4][DC];
+  if (nt > 0) fetch(0, fa);
+  for (int tile = 0; tile < nt; tile += 2) {
+    if (tile + 1 < nt) fetch(tile + 1, fb);
+    pool(tile, fa);
+    if (tile + 1 < nt) {
+      if (tile + 2 < nt) fetch(tile + 2, fa);
+      pool(tile + 1, fb);
+    }
+  }
+  __syncthreads();
+
+  const int m = a.top_k - 1;
+  const int nv = max(0, min(SEL_NBLK, local - c0));  // candidates: blocks c0.. before `local`
+  const int n_wg = gridDim.x;
+  for (int r = w; r < R; r += 8) {  // one wave per group
+    if (m == 0) break;
+    uint32_t key[4];
+    int32_t idx[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int cl = s4 * 64 + lane;
+      idx[s4] = c0 + cl;
+      key[s4] = cl < nv ? order_key(s_m[r][cl]) : 0u;
+    }
+    uint32_t ks = 0;
+    int32_t is = 0x7fffffff;
+    if (nv > m) wave_threshold<4>(key, idx, m, s_key[w], s_idx[w], ks, is);
+    uint32_t *ck = a.cand_key + (((long)b * R + r) * n_wg + wg) * m;
+    int32_t *ci = a.cand_idx + (((long)b * R + r) * n_wg + wg) * m;
+    int pos = 0;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const bool pr = taken(key[s4], idx[s4], ks, is);
+      const uint64_t mk = ballot(pr);
+      if (pr) {
+        ck[pos + rank_below(mk)] = key[s4];
+        ci[pos + rank_below(mk)] = idx[s4];
+      }
+      pos += popc64(mk);
+    }
+    if (lane >= pos && lane < m) {  // fewer than m candidates in this range
+      ck[lane] = 0u;
+      ci[lane] = -1;
+    }
+  }
+}
+
+template <typename E, int DI, int BS>
+hipError_t launch_select_t(const IndexArgs &a, hipStream_t s) {
+  const long blocks = a.q_start / BS + 1;  // blocks 0 .. local
+  dim3 grid((unsigned)((blocks + SEL_NBLK - 1) / SEL_NBLK), 1, (unsigned)a.batch);
+  hipLaunchKernelGGL((index_select_decode<E, DI, BS>), grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename E, int DI, int BS>
 hipError_t launch_prefill_t(const IndexArgs &a, hipStream_t s) {
   const int TQ = WG_COLS / a.h_kv;
@@ -261,6 +382,18 @@ hipError_t launch_decode_t(const IndexArgs &a, hipStream_t s) {
   dim3 grid((unsigned)((keys + a.key_chunk - 1) / a.key_chunk), 1, (unsigned)a.batch);
   hipLaunchKernelGGL((index_pool_decode<E, DI, BS>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename E>
+hipError_t pick_select(const IndexArgs &a, int d_idx, int bs, hipStream_t s) {
+#define MSA_CASE(DI, BS) \
+  if (d_idx == DI && bs == BS) return launch_select_t<E, DI, BS>(a, s);
+  MSA_CASE(32, 32)
+  MSA_CASE(32, 64)
+  MSA_CASE(64, 32)
+  MSA_CASE(64, 64)
+#undef MSA_CASE
+  return hipErrorInvalidValue;
 }
 
 template <typename E>
@@ -290,6 +423,12 @@ hipError_t launch_index_prefill(const IndexArgs &a, int dtype, int d_idx, int bl
                                 hipStream_t s) {
   return dtype == 0 ? pick<float>(a, d_idx, block_size, false, s)
                     : pick<bf16_t>(a, d_idx, block_size, false, s);
+}
+
+hipError_t launch_index_select_decode(const IndexArgs &a, int dtype, int d_idx, int block_size,
+                                      hipStream_t s) {
+  return dtype == 0 ? pick_select<float>(a, d_idx, block_size, s)
+                    : pick_select<bf16_t>(a, d_idx, block_size, s);
 }
 
 hipError_t launch_index_decode(const IndexArgs &a, int dtype, int d_idx, int block_size,

@@ -13,7 +13,13 @@ struct IndexArgs {
   float *bmax;        // [B, R, n_q, n_blocks]
   int batch, n_q, n_k, q_start, h_kv, n_blocks, cap;
   int key_chunk;      // keys per workgroup (multiple of 64)
+  // decode selection fused into the index kernel (index_select_decode only):
+  uint32_t *cand_key;  // [B, R, n_wg, top_k - 1] best blocks of each workgroup's range
+  int32_t *cand_idx;
+  int top_k;
 };
+
+constexpr int SEL_NBLK = 256;  // key blocks per fused decode index-select workgroup
 
 struct TopkArgs {
   const float *bmax;   // [B, R, n_q, n_blocks]
@@ -21,7 +27,9 @@ struct TopkArgs {
   uint32_t *cand_key;  // [problems, n_chunks, k-1]  (two-level path only)
   int32_t *cand_idx;   // [problems, n_chunks, k-1]
   int batch, n_q, q_start, h_kv, n_blocks, block_size, top_k;
-  int n_chunks;        // chunks of TOPK_CHUNK blocks for the largest problem
+  int n_chunks;        // candidate chunks per problem (stride of cand_key / cand_idx)
+  int chunk_blocks;    // blocks per chunk (TOPK_CHUNK, or SEL_NBLK after the fused decode kernel)
+  int final_all;       // merge pass also writes problems with a single chunk (fused decode path)
 };
 
 struct AttnArgs {
@@ -50,6 +58,7 @@ struct KvArgs {          // KV-outer prefill attention
   int32_t *coff;         // [NB + 1] first chunk of each block
   int32_t *list;         // [entries] row * 64 + slot, grouped by block
   int32_t *cmap;         // [chunks] list index of each chunk
+  long *tile_sum;        // [2 * scan tiles] scan scratch
   void *part_o;          // [B*R*n_q*top_k][G][DH] unnormalised partial outputs (dtype)
   float *part_ml;        // [B*R*n_q*top_k][G][2] (max in log2 units, sum)
   int batch, n_q, n_k, q_start, h_q, h_kv, block_size, top_k, cap, n_blocks;
@@ -59,7 +68,7 @@ struct KvArgs {          // KV-outer prefill attention
 };
 
 struct KvLayout {
-  size_t cnt, boff, coff, cmap, list, part_o, part_ml, total;
+  size_t cnt, boff, coff, cmap, tile_sum, list, part_o, part_ml, total;
 };
 
 // Rows per list segment for a prefill of this size (a multiple of the list-build tile).
@@ -77,6 +86,9 @@ hipError_t launch_index_prefill(const IndexArgs &a, int dtype, int d_idx, int bl
 hipError_t launch_index_decode(const IndexArgs &a, int dtype, int d_idx, int block_size,
                                hipStream_t s);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
+hipError_t launch_topk_final(const TopkArgs &a, hipStream_t s);
+hipError_t launch_index_select_decode(const IndexArgs &a, int dtype, int d_idx, int block_size,
+                                      hipStream_t s);
 hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s);
 

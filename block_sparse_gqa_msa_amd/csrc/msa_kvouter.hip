@@ -124,54 +124,106 @@ __global__ __launch_bounds__(1024) void kv_fill_hist(KvArgs a) {
   }
 }
 
-// Exclusive scans of the per-list entry counts and chunk counts, and the chunk -> list
-// map (one workgroup; each thread owns a contiguous run of lists, read four at a time).
-__global__ __launch_bounds__(1024) void kv_scan(KvArgs a) {
-  __shared__ long s_pairs[1024];
-  __shared__ long s_chunks[1024];
-  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
-  const int tid = threadIdx.x;
-  const long seg = ((NB + 1023) / 1024 + 3) / 4 * 4;  // a multiple of 4: aligned int4 reads
-  const long i0 = min(NB, tid * seg), i1 = min(NB, i0 + seg);
-  long sp = 0, sc = 0;
-  for (long i = i0; i < i1; i += 4) {
-    if (i + 4 <= i1) {
-      const int4 n = *reinterpret_cast<const int4 *>(a.cnt + i);
-      sp += (long)n.x + n.y + n.z + n.w;
-      sc += (n.x + CHUNK - 1) / CHUNK + (n.y + CHUNK - 1) / CHUNK + (n.z + CHUNK - 1) / CHUNK +
-            (n.w + CHUNK - 1) / CHUNK;
-    } else {
-      for (long j = i; j < i1; ++j) {
-        sp += a.cnt[j];
-        sc += (a.cnt[j] + CHUNK - 1) / CHUNK;
-      }
-    }
+// Exclusive scans of the per-list entry counts and chunk counts, and the chunk -> list map,
+// in three parallel phases over tiles of SCAN_TILE lists: tile sums, one scan of the tile
+// sums, then each tile's own scan with its offset.
+constexpr int SCAN_TILE = 1024;  // lists per scan workgroup (256 threads x 4)
+
+__device__ __forceinline__ int chunks_of(int n) { return (n + CHUNK - 1) / CHUNK; }
+
+// Block-wide exclusive scan of one value per thread (256 threads); returns the total.
+__device__ __forceinline__ long block_excl_scan(long v, long &excl, long *s_w) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  long incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
-  s_pairs[tid] = sp;
-  s_chunks[tid] = sc;
+  if (lane == 63) s_w[w] = incl;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
-    const long vp = tid >= off ? s_pairs[tid - off] : 0;
-    const long vc = tid >= off ? s_chunks[tid - off] : 0;
-    __syncthreads();
-    s_pairs[tid] += vp;
-    s_chunks[tid] += vc;
-    __syncthreads();
+  long base = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) base += s_w[i];
+    total += s_w[i];
   }
-  long rp = s_pairs[tid] - sp, rc = s_chunks[tid] - sc;
-  for (long i = i0; i < i1; ++i) {
-    const int n = a.cnt[i];
-    const int nc = (n + CHUNK - 1) / CHUNK;
-    a.boff[i] = (int32_t)rp;
-    a.coff[i] = (int32_t)rc;
-    for (int j = 0; j < nc; ++j) a.cmap[rc + j] = (int32_t)i;
-    rp += n;
-    rc += nc;
+  __syncthreads();
+  excl = base + incl - v;
+  return total;
+}
+
+__global__ __launch_bounds__(256) void kv_scan_tiles(KvArgs a) {
+  __shared__ long s_w[2][4];
+  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
+  const long i0 = (long)blockIdx.x * SCAN_TILE + threadIdx.x * 4;
+  long sp = 0, sc = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (i0 + u < NB) {
+      const int n = a.cnt[i0 + u];
+      sp += n;
+      sc += chunks_of(n);
+    }
+  long ep, ec;
+  const long tp = block_excl_scan(sp, ep, s_w[0]);
+  const long tc = block_excl_scan(sc, ec, s_w[1]);
+  if (threadIdx.x == 0) {
+    a.tile_sum[2 * blockIdx.x] = tp;
+    a.tile_sum[2 * blockIdx.x + 1] = tc;
   }
-  if (tid == 1023) {
-    a.boff[NB] = (int32_t)s_pairs[1023];
-    a.coff[NB] = (int32_t)s_chunks[1023];
+}
+
+// One workgroup: exclusive scan of the tile sums in place; writes the totals.
+__global__ __launch_bounds__(256) void kv_scan_top(KvArgs a) {
+  __shared__ long s_w[2][4];
+  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
+  const long n_tiles = (NB + SCAN_TILE - 1) / SCAN_TILE;
+  long carry_p = 0, carry_c = 0;
+  for (long base = 0; base < n_tiles; base += 256) {
+    const long i = base + threadIdx.x;
+    const long vp = i < n_tiles ? a.tile_sum[2 * i] : 0, vc = i < n_tiles ? a.tile_sum[2 * i + 1] : 0;
+    long ep, ec;
+    const long tp = block_excl_scan(vp, ep, s_w[0]);
+    const long tc = block_excl_scan(vc, ec, s_w[1]);
+    if (i < n_tiles) {
+      a.tile_sum[2 * i] = carry_p + ep;
+      a.tile_sum[2 * i + 1] = carry_c + ec;
+    }
+    carry_p += tp;
+    carry_c += tc;
   }
+  if (threadIdx.x == 0) {
+    a.boff[NB] = (int32_t)carry_p;
+    a.coff[NB] = (int32_t)carry_c;
+  }
+}
+
+__global__ __launch_bounds__(256) void kv_scan_apply(KvArgs a) {
+  __shared__ long s_w[2][4];
+  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
+  const long i0 = (long)blockIdx.x * SCAN_TILE + threadIdx.x * 4;
+  int n[4];
+  long sp = 0, sc = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    n[u] = i0 + u < NB ? a.cnt[i0 + u] : 0;
+    sp += n[u];
+    sc += chunks_of(n[u]);
+  }
+  long ep, ec;
+  block_excl_scan(sp, ep, s_w[0]);
+  block_excl_scan(sc, ec, s_w[1]);
+  long rp = a.tile_sum[2 * blockIdx.x] + ep, rc = a.tile_sum[2 * blockIdx.x + 1] + ec;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (i0 + u < NB) {
+      a.boff[i0 + u] = (int32_t)rp;
+      a.coff[i0 + u] = (int32_t)rc;
+      for (int j = 0; j < chunks_of(n[u]); ++j) a.cmap[rc + j] = (int32_t)(i0 + u);
+      rp += n[u];
+      rc += chunks_of(n[u]);
+    }
 }
 
 // ---------------------------------------------------------------- attention per block
@@ -447,18 +499,14 @@ __global__ __launch_bounds__(256) void kv_merge(KvArgs a, int log2g) {
   const long row = (long)blockIdx.x * 4 + w;  // (b, r, t)
   if (row >= (long)a.batch * a.h_kv * a.n_q) return;
   const int G = 1 << log2g;
+  const int cl = lane < a.top_k ? a.sel[row * a.top_k + lane] : -1;
+  const uint64_t valid = ballot(cl >= 0 && cl < a.n_blocks);  // valid slots (top_k <= 64)
   if (lane * EPL >= G * DH) return;  // idle lanes (no cross-lane work below)
   const int hd = (lane * EPL) / DH;
   const int d0 = (lane * EPL) % DH;
   const int t = (int)(row % a.n_q);
   const long br = row / a.n_q;
   const int r = (int)(br % a.h_kv), b = (int)(br / a.h_kv);
-  const int32_t *sel = a.sel + row * a.top_k;
-  uint64_t valid = 0;  // valid slots as a bit mask (top_k <= 64)
-  for (int s = 0; s < a.top_k; ++s) {
-    const int c = sel[s];
-    if (c >= 0 && c < a.n_blocks) valid |= 1ull << s;
-  }
   const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row * a.top_k * G + hd;
   const E *pbase = reinterpret_cast<const E *>(a.part_o) + (row * a.top_k * G + hd) * DH + d0;
   float acc[EPL];
@@ -520,6 +568,13 @@ __global__ __launch_bounds__(256) void kv_merge(KvArgs a, int log2g) {
     a.lse[((long)b * a.h_q + r * G + hd) * a.n_q + t] = (M + __log2f(Ls)) * 0.69314718055994531f;
 }
 
+void scan(const KvArgs &a, long NB, hipStream_t s) {
+  const unsigned tiles = (unsigned)((NB + SCAN_TILE - 1) / SCAN_TILE);
+  hipLaunchKernelGGL(kv_scan_tiles, dim3(tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(kv_scan_top, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(kv_scan_apply, dim3(tiles), dim3(256), 0, s, a);
+}
+
 template <typename E, int DH, int BS>
 hipError_t run_kv(const KvArgs &a, int log2g, hipStream_t s) {
   const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
@@ -531,12 +586,12 @@ hipError_t run_kv(const KvArgs &a, int log2g, hipStream_t s) {
     const unsigned wgs = (unsigned)((long)a.batch * a.h_kv * ((a.n_q + rows_per_wg - 1) / rows_per_wg));
     const size_t lds = (size_t)a.n_blocks * sizeof(int32_t);
     hipLaunchKernelGGL(kv_count_hist, dim3(wgs), dim3(1024), lds, s, a);
-    hipLaunchKernelGGL(kv_scan, dim3(1), dim3(1024), 0, s, a);
+    scan(a, NB, s);
     hipLaunchKernelGGL(kv_fill_hist, dim3(wgs), dim3(1024), lds, s, a);
   } else {
     const unsigned eg = (unsigned)((entries + 255) / 256);
     hipLaunchKernelGGL(kv_count, dim3(eg), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(kv_scan, dim3(1), dim3(1024), 0, s, a);
+    scan(a, NB, s);
     hipLaunchKernelGGL(kv_fill, dim3(eg), dim3(256), 0, s, a);
   }
   // persistent: a few workgroups per CU loop over the chunks
@@ -581,6 +636,7 @@ size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_bl
   L.boff = o;    o += al((NB + 1) * 4);
   L.coff = o;    o += al((NB + 1) * 4);
   L.cmap = o;    o += al(max_chunks * 4);
+  L.tile_sum = o; o += al(2 * ((NB + SCAN_TILE - 1) / SCAN_TILE) * 8);
   L.list = o;    o += al(slots * 4);
   L.part_o = o;  o += al(slots * (size_t)group * (size_t)d_h * (size_t)elem_bytes);
   L.part_ml = o; o += al(slots * (size_t)group * 8);

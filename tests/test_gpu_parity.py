@@ -94,18 +94,26 @@ DECODE_SMALL = [
     W("decode_two_level_topk", batch=2, n_q=1, n_k=140000, q_start=139999, block_size=32,
       top_k=32, needles=8),
     W("decode_few_blocks", batch=2, n_q=1, n_k=200, q_start=199, top_k=8),
+    W("decode_k1", batch=2, n_q=1, n_k=3000, q_start=2999, top_k=1),
+    W("decode_ties", batch=2, n_q=1, n_k=70000, q_start=69999, d_idx=32, top_k=32,
+      idx_range=0),  # all index scores equal: lowest blocks win every tie
 ]
 
 
 @pytest.mark.parametrize("w", DECODE_SMALL, ids=lambda w: w.name)
 def test_decode_full_oracle(w):
+    """Both decode selection paths: with block scores requested (index kernel, then top-k
+    passes over the scores) and without (selection fused into the index kernel)."""
     log(f"case {w.name}: {w}")
     inp = generate(w, device="cuda")
-    buf = run_gpu(w, inp, block_scores=True)
-    check_selection_invariants(w, buf.sel)
     ref = oracle_run(w, to_cpu(inp), block_scores=True)
-    assert np.array_equal(buf.block_scores.cpu().numpy().astype(np.float64), ref["block_scores"])
-    compare(w, buf, ref, label=w.name)
+    for want_scores in (True, False):
+        buf = run_gpu(w, inp, block_scores=want_scores)
+        check_selection_invariants(w, buf.sel)
+        if want_scores:
+            assert np.array_equal(buf.block_scores.cpu().numpy().astype(np.float64),
+                                  ref["block_scores"])
+        compare(w, buf, ref, label=f"{w.name} (block scores {want_scores})")
 
 
 def test_kv_capacity_stride():
