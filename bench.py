@@ -81,39 +81,49 @@ def time_step(w, inputs, steps, warmup, decode):
     ws_index = torch.empty(max(1, msa.msa_index_topk_workspace_size(s)), dtype=torch.uint8,
                            device="cuda")
 
+    if decode:
+        # msa_index_topk runs the first selection stage inside the index kernel
+        # (index_select_decode) and merges the per-range winners in topk_pass2
+        stages = [
+            ("index_topk", lambda: msa.msa_index_topk(s, inputs["q_idx"], inputs["k_idx"], sel,
+                                                       None, ws_index)),
+            ("attention", lambda: msa.msa_sparse_attn_decode(s, inputs["q"], inputs["k"],
+                                                             inputs["v"], sel, o, lse, ws_attn)),
+        ]
+    else:
+        # prefill: every stage is its own call so each kernel is timed alone
+        stages = [
+            ("index_scores", lambda: msa.msa_index_block_scores(s, inputs["q_idx"],
+                                                                inputs["k_idx"], scores)),
+            ("topk", lambda: msa.msa_topk_from_block_scores(s, scores, sel, ws_topk)),
+            ("attn_plan", lambda: msa.msa_sparse_attn_prefill_plan(s, sel, ws_attn)),
+            ("attn_partials", lambda: msa.msa_sparse_attn_prefill_partials(
+                s, inputs["q"], inputs["k"], inputs["v"], ws_attn)),
+            ("attn_merge", lambda: msa.msa_sparse_attn_prefill_merge(s, sel, o, lse, ws_attn)),
+        ]
+
     def step(ev=None):
-        # prefill: the index kernel and the top-k pass as two calls so each is timed alone;
-        # decode: msa_index_topk, whose first selection stage runs inside the index kernel
+        for i, (_, call) in enumerate(stages):
+            if ev:
+                ev[i].record(stream)
+            call()
         if ev:
-            ev[0].record(stream)
-        if decode:
-            msa.msa_index_topk(s, inputs["q_idx"], inputs["k_idx"], sel, None, ws_index)
-        else:
-            msa.msa_index_block_scores(s, inputs["q_idx"], inputs["k_idx"], scores)
-        if ev:
-            ev[1].record(stream)
-        if not decode:
-            msa.msa_topk_from_block_scores(s, scores, sel, ws_topk)
-        if ev:
-            ev[2].record(stream)
-        attn(s, inputs["q"], inputs["k"], inputs["v"], sel, o, lse, ws_attn)
-        if ev:
-            ev[3].record(stream)
+            ev[-1].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    n_ev = len(stages) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    k_index = np.mean([e[0].elapsed_time(e[1]) for e in events]) * 1e-3
-    k_topk = np.mean([e[1].elapsed_time(e[2]) for e in events]) * 1e-3
-    k_attn = np.mean([e[2].elapsed_time(e[3]) for e in events]) * 1e-3
-    return wall, dict(index_scores=k_index, topk=k_topk, attention=k_attn)
+    times = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) * 1e-3
+             for i, (name, _) in enumerate(stages)}
+    return wall, times
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -154,6 +164,46 @@ def cpu_baseline_decode(w, inputs, target_s=6.0):
                        f"{n} repetitions in {dt:.1f} s")
 
 
+# ------------------------------------------------------------------ counters
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the FETCH_SIZE / WRITE_SIZE
+    counter runs recorded in profiles/traffic.json (each scaled by what the counter
+    reads for a plain copy of known size), or None when there is no record or the
+    kernel's sources have changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)["kernels"][f"{kernel}@{workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if source_digest(rec["sources"]) != rec["source_digest"]:
+        return None
+    return rec["traffic_bytes"]
+
+
+def copy_calibration(n_bytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes, "reps": reps}))
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -165,11 +215,17 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--prefill", default="prefill_128k")
     ap.add_argument("--decode", default="decode_1m_b4")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (to scale the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this MSA build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the MSA library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        copy_calibration()
+        return
 
     import torch
     from block_sparse_gqa_msa_amd import binding as msa
@@ -185,15 +241,16 @@ def main():
     wall, kt = time_step(wp, inp, args.steps, args.warmup, decode=False)
     f_index, f_main = prefill_work(wp)
     tok_s = wp.batch * wp.n_q / wall
-    cand = {
-        "index_scores": dict(kernel="index_pool_prefill", flops=f_index, t=kt["index_scores"]),
-        "attention": dict(kernel="attn_prefill", flops=f_main, t=kt["attention"]),
-    }
-    dom = max(cand.values(), key=lambda c: c["t"])
-    roof = dict(kernel=dom["kernel"], bound="mfma", achieved=dom["flops"] / dom["t"] / 1e12,
+    # dominant kernel by time: the index kernel (index FLOPs) or kv_attend (main-branch FLOPs)
+    cand = [dict(kernel="index_pool_prefill", stage="index_scores", flops=f_index),
+            dict(kernel="kv_attend", stage="attn_partials", flops=f_main)]
+    dom = max(cand, key=lambda c: kt[c["stage"]])
+    t_dom = kt[dom["stage"]]
+    roof = dict(kernel=dom["kernel"], bound="mfma", achieved=dom["flops"] / t_dom / 1e12,
                 peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                frac=dom["flops"] / dom["t"] / PEAK_BF16_FLOPS, traffic=None,
-                per_launch_flops=dom["flops"], avg_launch_ms=dom["t"] * 1e3)
+                frac=dom["flops"] / t_dom / PEAK_BF16_FLOPS,
+                traffic=measured_traffic(dom["kernel"], wp.name),
+                per_launch_flops=dom["flops"], avg_launch_ms=t_dom * 1e3)
     path = dict(flops=f_index + f_main, tflops=(f_index + f_main) / wall / 1e12,
                 mfma_frac=(f_index + f_main) / wall / PEAK_BF16_FLOPS)
     log(f"[bench] prefill {wall * 1e3:.2f} ms/step, kernels (ms): "
@@ -211,11 +268,12 @@ def main():
     log(f"[bench] decode {wd.name}: warmup {args.warmup}, steps {args.decode_steps}")
     dwall, dkt = time_step(wd, inp, args.decode_steps, args.warmup, decode=True)
     d_bytes, d_index_bytes, _ = decode_work(wd)
-    droof = dict(kernel="index_select_decode+topk_pass2 (msa_index_topk)", bound="hbm",
-                 achieved=d_index_bytes / dkt["index_scores"] / 1e9, peak=PEAK_HBM_BYTES / 1e9,
-                 unit="GB/s", frac=d_index_bytes / dkt["index_scores"] / PEAK_HBM_BYTES,
-                 traffic=None, per_launch_bytes=d_index_bytes,
-                 avg_launch_ms=dkt["index_scores"] * 1e3)
+    t_idx = dkt["index_topk"]
+    droof = dict(kernel="index_select_decode+topk_pass2", bound="hbm",
+                 achieved=d_index_bytes / t_idx / 1e9, peak=PEAK_HBM_BYTES / 1e9,
+                 unit="GB/s", frac=d_index_bytes / t_idx / PEAK_HBM_BYTES,
+                 traffic=measured_traffic("index_select_decode", wd.name),
+                 per_launch_bytes=d_index_bytes, avg_launch_ms=t_idx * 1e3)
     log(f"[bench] decode {dwall * 1e6:.1f} us/step, kernels (us): "
         + ", ".join(f"{k} {v * 1e6:.1f}" for k, v in dkt.items()))
     cpu_d = None

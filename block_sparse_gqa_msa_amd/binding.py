@@ -21,7 +21,9 @@ MSA_F32, MSA_BF16 = 0, 1
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
 EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_scores",
            "msa_topk_workspace_size", "msa_topk_from_block_scores",
-           "msa_sparse_attn_workspace_size", "msa_sparse_attn_prefill", "msa_sparse_attn_decode",
+           "msa_sparse_attn_workspace_size", "msa_sparse_attn_prefill",
+           "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_partials",
+           "msa_sparse_attn_prefill_merge", "msa_sparse_attn_decode",
            "msa_last_error", "msa_abi_version")
 
 
@@ -66,6 +68,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_topk_from_block_scores.argtypes = [S, P, P, P, ctypes.c_size_t, P]
     lib.msa_index_topk.argtypes = [S, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_prefill.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_sparse_attn_prefill_plan.argtypes = [S, P, P, ctypes.c_size_t, P]
+    lib.msa_sparse_attn_prefill_partials.argtypes = [S, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_sparse_attn_prefill_merge.argtypes = [S, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_decode.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     for f in EXPORTS:
         if f == "msa_last_error":
@@ -201,6 +206,32 @@ def msa_sparse_attn_prefill(shape: MsaShape, q, k, v, sel, o, lse=None, workspac
         ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k, et, "k"), _ptr(v, et, "v"),
         _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"), _ptr(lse, torch.float32, "lse"),
         wp, wn, _stream(stream, o)))
+
+
+def msa_sparse_attn_prefill_plan(shape: MsaShape, sel, workspace=None, stream=None) -> None:
+    import torch
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_sparse_attn_prefill_plan(
+        ctypes.byref(shape), _ptr(sel, torch.int32, "sel"), wp, wn, _stream(stream, sel)))
+
+
+def msa_sparse_attn_prefill_partials(shape: MsaShape, q, k, v, workspace=None,
+                                     stream=None) -> None:
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_sparse_attn_prefill_partials(
+        ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k, et, "k"), _ptr(v, et, "v"), wp, wn,
+        _stream(stream, q)))
+
+
+def msa_sparse_attn_prefill_merge(shape: MsaShape, sel, o, lse=None, workspace=None,
+                                  stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_sparse_attn_prefill_merge(
+        ctypes.byref(shape), _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"),
+        _ptr(lse, torch.float32, "lse"), wp, wn, _stream(stream, o)))
 
 
 def msa_sparse_attn_decode(shape: MsaShape, q, k_cache, v_cache, sel, o, lse=None,

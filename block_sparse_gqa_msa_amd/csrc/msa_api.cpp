@@ -298,14 +298,14 @@ int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes) {
   return ok();
 }
 
-int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k, const void *v,
-                            const int32_t *sel, void *o, float *lse, void *workspace,
-                            size_t workspace_bytes, void *stream) {
+// Validates a prefill-attention call and fills the kernel arguments over the caller's
+// workspace; the pointers a stage does not use may be NULL.
+static int prefill_args(const msa_shape *shape, void *workspace, size_t workspace_bytes,
+                        msa::KvArgs *out) {
   int rc = check_shape(shape);
   if (rc) return rc;
   const msa_shape &s = *shape;
   if ((rc = check_attn_dims(s))) return rc;
-  if (!q || !k || !v || !sel || !o) return fail(MSA_ERR_INVALID_ARG, "q, k, v, sel and o must be non-NULL");
   if ((rc = check_prefill_limits(s))) return rc;
   msa::KvLayout lay;
   const size_t need = attn_prefill_ws(s, &lay);
@@ -317,16 +317,67 @@ int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k
   const int n_seg = (s.n_q + seg_rows - 1) / seg_rows;
   const long long NB = (long long)n_seg * s.batch * s.h_kv * n_blocks(s);
   int32_t *cnt = reinterpret_cast<int32_t *>(ws + lay.cnt);
-  msa::KvArgs a{q, k, v, sel, o, lse, cnt, cnt + NB,
-                reinterpret_cast<int32_t *>(ws + lay.boff), reinterpret_cast<int32_t *>(ws + lay.coff),
-                reinterpret_cast<int32_t *>(ws + lay.list), reinterpret_cast<int32_t *>(ws + lay.cmap),
-                reinterpret_cast<long *>(ws + lay.tile_sum), ws + lay.part_o,
-                reinterpret_cast<float *>(ws + lay.part_ml), s.batch, s.n_q, s.n_k, s.q_start,
-                s.h_q, s.h_kv, s.block_size, s.top_k, cap_of(s), (int)n_blocks(s), seg_rows,
-                n_seg, (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};
-  hipError_t e = msa::launch_attn_prefill_kv(a, s.dtype, s.d_h, reinterpret_cast<hipStream_t>(stream));
+  *out = msa::KvArgs{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, cnt, cnt + NB,
+                     reinterpret_cast<int32_t *>(ws + lay.boff), reinterpret_cast<int32_t *>(ws + lay.coff),
+                     reinterpret_cast<int32_t *>(ws + lay.list), reinterpret_cast<int32_t *>(ws + lay.cmap),
+                     reinterpret_cast<long *>(ws + lay.tile_sum), ws + lay.part_o,
+                     reinterpret_cast<float *>(ws + lay.part_ml), s.batch, s.n_q, s.n_k, s.q_start,
+                     s.h_q, s.h_kv, s.block_size, s.top_k, cap_of(s), (int)n_blocks(s), seg_rows,
+                     n_seg, (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};
+  return MSA_OK;
+}
+
+static int run_prefill(const msa_shape &s, const msa::KvArgs &a, int stages, void *stream) {
+  hipError_t e = msa::launch_attn_prefill_kv(a, s.dtype, s.d_h, stages,
+                                             reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   return ok();
+}
+
+int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k, const void *v,
+                            const int32_t *sel, void *o, float *lse, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  msa::KvArgs a;
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !k || !v || !sel || !o) return fail(MSA_ERR_INVALID_ARG, "q, k, v, sel and o must be non-NULL");
+  if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
+  a.q = q; a.k = k; a.v = v; a.sel = sel; a.o = o; a.lse = lse;
+  return run_prefill(*shape, a, msa::KV_STAGE_ALL, stream);
+}
+
+int msa_sparse_attn_prefill_plan(const msa_shape *shape, const int32_t *sel, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+  msa::KvArgs a;
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!sel) return fail(MSA_ERR_INVALID_ARG, "sel must be non-NULL");
+  if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
+  a.sel = sel;
+  return run_prefill(*shape, a, msa::KV_STAGE_PLAN, stream);
+}
+
+int msa_sparse_attn_prefill_partials(const msa_shape *shape, const void *q, const void *k,
+                                     const void *v, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+  msa::KvArgs a;
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !k || !v) return fail(MSA_ERR_INVALID_ARG, "q, k and v must be non-NULL");
+  if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
+  a.q = q; a.k = k; a.v = v;
+  return run_prefill(*shape, a, msa::KV_STAGE_ATTEND, stream);
+}
+
+int msa_sparse_attn_prefill_merge(const msa_shape *shape, const int32_t *sel, void *o, float *lse,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  msa::KvArgs a;
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!sel || !o) return fail(MSA_ERR_INVALID_ARG, "sel and o must be non-NULL");
+  if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
+  a.sel = sel; a.o = o; a.lse = lse;
+  return run_prefill(*shape, a, msa::KV_STAGE_MERGE, stream);
 }
 
 int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_cache,

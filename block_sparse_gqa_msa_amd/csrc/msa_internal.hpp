@@ -89,7 +89,9 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s);
 hipError_t launch_topk_final(const TopkArgs &a, hipStream_t s);
 hipError_t launch_index_select_decode(const IndexArgs &a, int dtype, int d_idx, int block_size,
                                       hipStream_t s);
-hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, hipStream_t s);
+// Stages of the prefill attention: list build from sel, per-selection partials, merge.
+enum { KV_STAGE_PLAN = 1, KV_STAGE_ATTEND = 2, KV_STAGE_MERGE = 4, KV_STAGE_ALL = 7 };
+hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, int stages, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s);
 
 }  // namespace msa

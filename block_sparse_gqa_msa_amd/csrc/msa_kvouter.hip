@@ -576,28 +576,33 @@ void scan(const KvArgs &a, long NB, hipStream_t s) {
 }
 
 template <typename E, int DH, int BS>
-hipError_t run_kv(const KvArgs &a, int log2g, hipStream_t s) {
+hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
   const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
   const long entries = (long)a.batch * a.h_kv * a.n_q * a.top_k;
-  hipLaunchKernelGGL(fill_i32, dim3((unsigned)std::min(4096L, (2 * NB + 255) / 256)), dim3(256), 0, s,
-                     a.cnt, 2 * NB, 0);  // cnt and cursor are adjacent
-  if (a.n_blocks <= HIST_MAX_BLOCKS) {
-    const long rows_per_wg = std::max(1, HIST_ROWS_ENTRIES / a.top_k);  // divides seg_rows
-    const unsigned wgs = (unsigned)((long)a.batch * a.h_kv * ((a.n_q + rows_per_wg - 1) / rows_per_wg));
-    const size_t lds = (size_t)a.n_blocks * sizeof(int32_t);
-    hipLaunchKernelGGL(kv_count_hist, dim3(wgs), dim3(1024), lds, s, a);
-    scan(a, NB, s);
-    hipLaunchKernelGGL(kv_fill_hist, dim3(wgs), dim3(1024), lds, s, a);
-  } else {
-    const unsigned eg = (unsigned)((entries + 255) / 256);
-    hipLaunchKernelGGL(kv_count, dim3(eg), dim3(256), 0, s, a);
-    scan(a, NB, s);
-    hipLaunchKernelGGL(kv_fill, dim3(eg), dim3(256), 0, s, a);
+  if (stages & KV_STAGE_PLAN) {
+    hipLaunchKernelGGL(fill_i32, dim3((unsigned)std::min(4096L, (2 * NB + 255) / 256)), dim3(256), 0, s,
+                       a.cnt, 2 * NB, 0);  // cnt and cursor are adjacent
+    if (a.n_blocks <= HIST_MAX_BLOCKS) {
+      const long rows_per_wg = std::max(1, HIST_ROWS_ENTRIES / a.top_k);  // divides seg_rows
+      const unsigned wgs = (unsigned)((long)a.batch * a.h_kv * ((a.n_q + rows_per_wg - 1) / rows_per_wg));
+      const size_t lds = (size_t)a.n_blocks * sizeof(int32_t);
+      hipLaunchKernelGGL(kv_count_hist, dim3(wgs), dim3(1024), lds, s, a);
+      scan(a, NB, s);
+      hipLaunchKernelGGL(kv_fill_hist, dim3(wgs), dim3(1024), lds, s, a);
+    } else {
+      const unsigned eg = (unsigned)((entries + 255) / 256);
+      hipLaunchKernelGGL(kv_count, dim3(eg), dim3(256), 0, s, a);
+      scan(a, NB, s);
+      hipLaunchKernelGGL(kv_fill, dim3(eg), dim3(256), 0, s, a);
+    }
   }
-  // persistent: a few workgroups per CU loop over the chunks
-  const long max_chunks = (entries + CHUNK - 1) / CHUNK + NB;
-  const unsigned grid = (unsigned)std::min(max_chunks, 256L * 8);
-  hipLaunchKernelGGL((kv_attend<E, DH, BS, false>), dim3(grid), dim3(256), 0, s, a, log2g);
+  if (stages & KV_STAGE_ATTEND) {
+    // persistent: a few workgroups per CU loop over the chunks
+    const long max_chunks = (entries + CHUNK - 1) / CHUNK + NB;
+    const unsigned grid = (unsigned)std::min(max_chunks, 256L * 8);
+    hipLaunchKernelGGL((kv_attend<E, DH, BS, false>), dim3(grid), dim3(256), 0, s, a, log2g);
+  }
+  if (!(stages & KV_STAGE_MERGE)) return hipGetLastError();
   const long rows = (long)a.batch * a.h_kv * a.n_q;
   const dim3 mg((unsigned)((rows + 3) / 4));
   const int epl = std::max(8, (DH << log2g) >> 6);
@@ -645,12 +650,12 @@ size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_bl
   return o;
 }
 
-hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, hipStream_t s) {
+hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, int stages, hipStream_t s) {
   int lg = 0;
   while ((1 << lg) < a.h_q / a.h_kv) ++lg;
 #define MSA_KV(E, DH)                                                             \
-  if (a.block_size == 32) return run_kv<E, DH, 32>(a, lg, s);                     \
-  return run_kv<E, DH, 64>(a, lg, s);
+  if (a.block_size == 32) return run_kv<E, DH, 32>(a, lg, stages, s);                     \
+  return run_kv<E, DH, 64>(a, lg, stages, s);
   if (dtype == 0) {
     if (d_h == 64) { MSA_KV(float, 64) }
     MSA_KV(float, 128)

@@ -136,7 +136,7 @@ int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes);
  *   o        out, dtype of q; rounded to nearest even for bf16
  *   lse      optional out (NULL to skip): natural-log sum of exp of the scaled scores
  *   workspace at least msa_sparse_attn_workspace_size bytes: the per-block query lists
- *            and one normalised partial output per (row, group, selected block), i.e.
+ *            and one unnormalised partial output per (row, group, selected block), i.e.
  *            about batch * h_kv * n_q * top_k * (h_q / h_kv) * d_h * sizeof(dtype) bytes.
  * Computed KV-block-outer: each selected block is staged once per chunk of the rows that
  * chose it, and the partials are merged with log-sum-exp weights (no float atomics).
@@ -145,6 +145,24 @@ int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes);
 int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k, const void *v,
                             const int32_t *sel, void *o, float *lse, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * The three stages of msa_sparse_attn_prefill as separate calls, for callers that
+ * schedule or time them apart. Called in this order with the same shape and the same
+ * workspace (whose contents carry over from one stage to the next) on one stream, they
+ * give the same bits as the single call; the workspace size is the same too.
+ *   _plan      reads sel and builds the per-block query lists in the workspace.
+ *   _partials  reads q, k, v and the lists; writes one partial output per selection.
+ *   _merge     reads sel and the partials; writes o and (optional) lse.
+ * Arguments mean what they mean for msa_sparse_attn_prefill; the same errors apply.
+ */
+int msa_sparse_attn_prefill_plan(const msa_shape *shape, const int32_t *sel, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+int msa_sparse_attn_prefill_partials(const msa_shape *shape, const void *q, const void *k,
+                                     const void *v, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+int msa_sparse_attn_prefill_merge(const msa_shape *shape, const int32_t *sel, void *o, float *lse,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Main branch, single-token decode: n_q == 1 and q_start == n_k - 1 (the new

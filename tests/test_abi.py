@@ -113,6 +113,31 @@ def test_attention_rejects(lib):
                                        None, 0, None) == msa.MSA_ERR_WORKSPACE
 
 
+def test_prefill_stage_calls_reject(lib):
+    dummy = 1 << 20
+    s = good()
+    need = msa.msa_sparse_attn_workspace_size(s)
+    ok = ctypes.c_size_t(need)
+    assert lib.msa_sparse_attn_prefill_plan(ctypes.byref(s), None, dummy, ok, None) \
+        == msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_sparse_attn_prefill_partials(ctypes.byref(s), dummy, None, dummy, dummy, ok,
+                                                None) == msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_sparse_attn_prefill_merge(ctypes.byref(s), dummy, None, None, dummy, ok,
+                                             None) == msa.MSA_ERR_INVALID_ARG
+    small = ctypes.c_size_t(need - 1)
+    assert lib.msa_sparse_attn_prefill_plan(ctypes.byref(s), dummy, dummy, small, None) \
+        == msa.MSA_ERR_WORKSPACE
+    assert lib.msa_sparse_attn_prefill_partials(ctypes.byref(s), dummy, dummy, dummy, None, ok,
+                                                None) == msa.MSA_ERR_WORKSPACE
+    assert lib.msa_sparse_attn_prefill_merge(ctypes.byref(s), dummy, dummy, None, dummy, small,
+                                             None) == msa.MSA_ERR_WORKSPACE
+    d = good(d_h=96)
+    assert lib.msa_sparse_attn_prefill_plan(ctypes.byref(d), dummy, dummy, ok, None) \
+        == msa.MSA_ERR_UNSUPPORTED
+    assert lib.msa_sparse_attn_prefill_plan(None, dummy, dummy, ok, None) \
+        == msa.MSA_ERR_INVALID_ARG
+
+
 def test_index_workspace_too_small(lib):
     s = good()
     need = msa.msa_index_topk_workspace_size(s)

@@ -225,3 +225,23 @@ def test_split_index_calls_equal_fused():
         local = (w.q_start + torch.arange(w.n_q, device="cuda")) // w.block_size
         vis = torch.arange(nb, device="cuda")[None, :] <= local[:, None]
         assert torch.equal(scores[..., vis], fused.block_scores[..., vis]), w.name
+
+
+def test_staged_prefill_calls_equal_single_call():
+    """_plan, _partials and _merge in order on one workspace give the same bits as
+    msa_sparse_attn_prefill, for a prefill and for a chunk of rows at q_start > 0."""
+    for w in (W("staged_prefill", n_q=2000, n_k=2000, top_k=16, needles=6),
+              W("staged_chunk_f32", dtype="f32", n_q=300, n_k=1500, q_start=1200, h_q=8,
+                h_kv=2, d_h=64, d_idx=32, block_size=32, top_k=5, idx_range=3, qkv_scale=1.0)):
+        inp = generate(w, device="cuda")
+        one = run_gpu(w, inp)
+        s = msa.shape_of(w)
+        o = torch.full_like(one.o, float("nan"))
+        lse = torch.full_like(one.lse, float("nan"))
+        ws = torch.empty(msa.msa_sparse_attn_workspace_size(s), dtype=torch.uint8, device="cuda")
+        msa.msa_sparse_attn_prefill_plan(s, one.sel, ws)
+        msa.msa_sparse_attn_prefill_partials(s, inp["q"], inp["k"], inp["v"], ws)
+        msa.msa_sparse_attn_prefill_merge(s, one.sel, o, lse, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, one.o), w.name
+        assert torch.equal(lse, one.lse), w.name
