@@ -129,7 +129,8 @@ int kv_seg_rows(const msa_shape &s) {
 int check_prefill_limits(const msa_shape &s) {
   const long long entries = (long long)s.batch * s.h_kv * s.n_q * s.top_k;
   const long long n_seg = (s.n_q + kv_seg_rows(s) - 1) / kv_seg_rows(s);
-  if (entries >= (1LL << 31) || s.n_q >= (1 << 25) ||
+  const long long merge_threads = (long long)s.batch * s.h_q * s.n_q * (s.d_h / 8);
+  if (entries >= (1LL << 31) || s.n_q >= (1 << 25) || merge_threads >= (1LL << 32) ||
       n_seg * s.batch * s.h_kv * n_blocks(s) >= (1LL << 30))
     return fail(MSA_ERR_UNSUPPORTED, "prefill too large for one call (%lld selection entries); "
                 "split the query rows over several calls", entries);

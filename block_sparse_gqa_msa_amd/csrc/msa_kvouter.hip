@@ -18,8 +18,8 @@
 //      x the G heads of the group): S^T = K Q^T, a softmax over the block, O^T = V^T P^T.
 //      It writes, for every (row, slot, head), the block's unnormalised output sum_j p_j v_j
 //      and (m, l) with p_j = 2^(z_j - m), l = sum_j p_j (log2 units).
-//   3. kv_merge: one wave per (b, r, row) combines the row's partials in slot order with
-//      weights 2^(m_s - M): O = sum_s w_s o_s / sum_s w_s l_s, LSE = (M + log2 L) ln 2.
+//   3. kv_merge: G * DH / 8 threads per (b, r, row) combine the row's partials in slot order
+//      with weights 2^(m_s - M): O = sum_s w_s o_s / sum_s w_s l_s, LSE = (M + log2 L) ln 2.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -238,6 +238,8 @@ struct KvLds {
 };
 
 // Stage block rows [kb, kb+BS) of K (row-major) and V (transposed) into LDS, 256 threads.
+// bf16 loads are non-temporal: a block is staged once per chunk and its lines are not
+// worth keeping in L2 over the Q rows the chunks gather.
 template <typename E, int DH, int BS>
 __device__ __forceinline__ void stage_block(const E *kp, const E *vp, long kb, int n_k,
                                             unsigned char *ks, unsigned char *vt) {
@@ -248,8 +250,8 @@ __device__ __forceinline__ void stage_block(const E *kp, const E *vp, long kb, i
   for (int pc = tid; pc < KPIECES; pc += 256) {
     const int key = pc / PER_ROW, off = pc % PER_ROW;
     const long j = kb + key;
-    const u32x4 x = j < n_k ? *reinterpret_cast<const u32x4 *>(
-                                  reinterpret_cast<const unsigned char *>(kp + j * DH) + off * 16)
+    const u32x4 x = j < n_k ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                                  reinterpret_cast<const unsigned char *>(kp + j * DH) + off * 16))
                             : u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4 *>(ks + key * L::KROW + off * 16) = x;
   }
@@ -258,8 +260,10 @@ __device__ __forceinline__ void stage_block(const E *kp, const E *vp, long kb, i
     for (int pc = tid; pc < VPIECES; pc += 256) {
       const int kpair = pc % PAIRS, d0 = (pc / PAIRS) * 8;
       const long j0 = kb + 2 * kpair, j1 = j0 + 1;
-      const u32x4 x = j0 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 y = j1 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 x = j0 < n_k ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0))
+                               : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 y = j1 < n_k ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0))
+                               : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e) * L::VROW + kpair * 4) =
@@ -437,7 +441,8 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
         }
       }
       // Stage the tile's 16 output rows in LDS, then write each entry's G x DH block with
-      // contiguous 16-byte pieces (consecutive lanes, consecutive addresses).
+      // contiguous 16-byte pieces (consecutive lanes, consecutive addresses), non-temporal:
+      // the merge reads them once, long after.
       unsigned char *so = s_o[w];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) store4(reinterpret_cast<E *>(so + c16 * OROW) + dt * 16 + g * 4, o[dt]);
@@ -456,8 +461,9 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
           if (ee < n_e) {
             const int en = s_list[ee];
             const long pss = ((((long)b * a.h_kv + r) * a.n_q + (en >> 6)) * a.top_k + (en & 63)) * G + hh;
-            *reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.part_o) + pss * DH * L::ES + off * 16) =
-                *reinterpret_cast<const u32x4 *>(so + row * OROW + off * 16);
+            __builtin_nontemporal_store(
+                *reinterpret_cast<const u32x4 *>(so + row * OROW + off * 16),
+                reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.part_o) + pss * DH * L::ES + off * 16));
           }
         }
       }
@@ -470,51 +476,58 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
 
 // ---------------------------------------------------------------- merge
 
-template <typename E>
-__device__ __forceinline__ void load8(const E *p, float (&x)[8]);
-template <>
-__device__ __forceinline__ void load8<bf16_t>(const bf16_t *p, float (&x)[8]) {
-  const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __uint_as_float(v[e] << 16);
-    x[2 * e + 1] = __uint_as_float(v[e] & 0xffff0000u);
+// 8 partial-output elements of one (slot, head), packed as stored (read once: non-temporal).
+template <typename E> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  u32x4 x;
+  __device__ __forceinline__ void load(const bf16_t *p) { x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)); }
+  __device__ __forceinline__ float operator[](int e) const {
+    const uint32_t u = x[e >> 1];
+    return __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
   }
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float *p, float (&x)[8]) {
-  const f32x4 u = *reinterpret_cast<const f32x4 *>(p), v = *reinterpret_cast<const f32x4 *>(p + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[e] = u[e];
-    x[4 + e] = v[e];
+};
+template <> struct Raw8<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ void load(const float *p) {
+    lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + 4));
   }
-}
+  __device__ __forceinline__ float operator[](int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
+};
 
-// One wave per (b, r, row): lane covers EPL consecutive outputs of one head,
-// EPL = max(8, G * DH / 64).
-template <typename E, int DH, int EPL>
+// Each (b, r, row) is merged by LPR = G * DH / 8 consecutive threads (a wave holds several
+// rows when LPR < 64; a row spans LPR / 64 waves otherwise); a thread owns 8 consecutive
+// outputs of one head. Slots are taken U at a time with their loads in flight together.
+template <typename E, int DH, int U>
 __global__ __launch_bounds__(256) void kv_merge(KvArgs a, int log2g) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + w;  // (b, r, t)
-  if (row >= (long)a.batch * a.h_kv * a.n_q) return;
   const int G = 1 << log2g;
-  const int cl = lane < a.top_k ? a.sel[row * a.top_k + lane] : -1;
-  const uint64_t valid = ballot(cl >= 0 && cl < a.n_blocks);  // valid slots (top_k <= 64)
-  if (lane * EPL >= G * DH) return;  // idle lanes (no cross-lane work below)
-  const int hd = (lane * EPL) / DH;
-  const int d0 = (lane * EPL) % DH;
-  const int t = (int)(row % a.n_q);
-  const long br = row / a.n_q;
-  const int r = (int)(br % a.h_kv), b = (int)(br / a.h_kv);
+  const int lpr_log2 = log2g + (DH == 128 ? 4 : 3);
+  const int span = min(1 << lpr_log2, 64);  // lanes of one row inside a wave
+  const long gl = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = gl >> lpr_log2;          // (b, r, t)
+  const long rows = (long)a.batch * a.h_kv * a.n_q;
+  const int lane = threadIdx.x & 63;
+  const int j = (int)(gl & ((1L << lpr_log2) - 1));
+
+  // valid slots of this row (top_k <= 64): ballots over the row's lanes, span slots a round
+  uint64_t mask = 0;
+  for (int m = 0; m * span < a.top_k; ++m) {
+    const int sl = m * span + (lane & (span - 1));
+    const int c = (sl < a.top_k && row < rows) ? a.sel[row * a.top_k + sl] : -1;
+    const uint64_t bl = ballot(c >= 0 && c < a.n_blocks);
+    const uint64_t bits = span == 64 ? bl : ((bl >> (lane & ~(span - 1))) & ((1ull << span) - 1));
+    mask |= bits << (m * span);
+  }
+  if (row >= rows) return;  // no cross-lane work below
+
+  const int hd = j / (DH / 8), d0 = (j % (DH / 8)) * 8;
   const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row * a.top_k * G + hd;
   const E *pbase = reinterpret_cast<const E *>(a.part_o) + (row * a.top_k * G + hd) * DH + d0;
-  float acc[EPL];
+  float acc[8];
 #pragma unroll
-  for (int x = 0; x < EPL; ++x) acc[x] = 0.f;
+  for (int x = 0; x < 8; ++x) acc[x] = 0.f;
   float M = -INFINITY, Ls = 0.f;
-  constexpr int U = 8;  // slots whose loads are in flight together
-  uint64_t v = valid;
+  uint64_t v = mask;
   while (v) {
     int sl[U];
 #pragma unroll
@@ -523,20 +536,11 @@ __global__ __launch_bounds__(256) void kv_merge(KvArgs a, int log2g) {
       v &= v - 1;  // no-op once v is 0
     }
     float2 mls[U];
-    float part[U][EPL];
+    Raw8<E> part[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       mls[u] = sl[u] >= 0 ? ml[(long)sl[u] * G] : make_float2(-INFINITY, 0.f);
-      if (sl[u] >= 0) {
-        const E *po = pbase + (long)sl[u] * G * DH;
-#pragma unroll
-        for (int x8 = 0; x8 < EPL; x8 += 8) {
-          float tmp[8];
-          load8<E>(po + x8, tmp);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) part[u][x8 + e] = tmp[e];
-        }
-      }
+      if (sl[u] >= 0) part[u].load(pbase + (long)sl[u] * G * DH);
     }
     float Mb = M;
 #pragma unroll
@@ -545,25 +549,25 @@ __global__ __launch_bounds__(256) void kv_merge(KvArgs a, int log2g) {
     const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);  // rescale earlier slots
     Ls *= sc;
 #pragma unroll
-    for (int x = 0; x < EPL; ++x) acc[x] *= sc;
+    for (int x = 0; x < 8; ++x) acc[x] *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (mls[u].y > 0.f) {
         const float wgt = __builtin_amdgcn_exp2f(mls[u].x - Mb);
         Ls += wgt * mls[u].y;
 #pragma unroll
-        for (int x = 0; x < EPL; ++x) acc[x] += wgt * part[u][x];
+        for (int x = 0; x < 8; ++x) acc[x] += wgt * part[u][x];
       }
     }
     M = Mb;
   }
+  const int t = (int)(row % a.n_q);
+  const long br = row / a.n_q;
+  const int r = (int)(br % a.h_kv), b = (int)(br / a.h_kv);
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
   E *o = reinterpret_cast<E *>(a.o) + (((long)b * a.h_q + r * G + hd) * a.n_q + t) * DH + d0;
-#pragma unroll
-  for (int x4 = 0; x4 < EPL; x4 += 4) {
-    const f32x4 v4 = {acc[x4] * inv, acc[x4 + 1] * inv, acc[x4 + 2] * inv, acc[x4 + 3] * inv};
-    store4(o + x4, v4);
-  }
+  store4(o, f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv});
+  store4(o + 4, f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv});
   if (a.lse && d0 == 0)
     a.lse[((long)b * a.h_q + r * G + hd) * a.n_q + t] = (M + __log2f(Ls)) * 0.69314718055994531f;
 }
@@ -598,20 +602,27 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
   }
   if (stages & KV_STAGE_ATTEND) {
     // persistent: a few workgroups per CU loop over the chunks
+    // two rounds of the workgroups that fit on the device at once: each takes every
+    // grid-th chunk, so per-workgroup work evens out over ~max_chunks / grid chunks
+    static const int per_cu = [] {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kv_attend<E, DH, BS, false>, 256, 0) !=
+              hipSuccess || n < 1)
+        n = 1;
+      return n;
+    }();
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
     const long max_chunks = (entries + CHUNK - 1) / CHUNK + NB;
-    const unsigned grid = (unsigned)std::min(max_chunks, 256L * 8);
+    const unsigned grid = (unsigned)std::min(max_chunks, 2L * per_cu * cus);
     hipLaunchKernelGGL((kv_attend<E, DH, BS, false>), dim3(grid), dim3(256), 0, s, a, log2g);
   }
   if (!(stages & KV_STAGE_MERGE)) return hipGetLastError();
-  const long rows = (long)a.batch * a.h_kv * a.n_q;
-  const dim3 mg((unsigned)((rows + 3) / 4));
-  const int epl = std::max(8, (DH << log2g) >> 6);
-  if (epl == 8)
-    hipLaunchKernelGGL((kv_merge<E, DH, 8>), mg, dim3(256), 0, s, a, log2g);
-  else if (epl == 16)
-    hipLaunchKernelGGL((kv_merge<E, DH, 16>), mg, dim3(256), 0, s, a, log2g);
-  else
-    hipLaunchKernelGGL((kv_merge<E, DH, 32>), mg, dim3(256), 0, s, a, log2g);
+  const long threads = (long)a.batch * a.h_kv * a.n_q * ((long)DH << log2g) / 8;
+  hipLaunchKernelGGL((kv_merge<E, DH, 16>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     a, log2g);
   return hipGetLastError();
 }
 

@@ -140,7 +140,8 @@ int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes);
  *            about batch * h_kv * n_q * top_k * (h_q / h_kv) * d_h * sizeof(dtype) bytes.
  * Computed KV-block-outer: each selected block is staged once per chunk of the rows that
  * chose it, and the partials are merged with log-sum-exp weights (no float atomics).
- * At most 2^31 selection entries (batch * h_kv * n_q * top_k) and n_q < 2^25 per call.
+ * Per call: fewer than 2^31 selection entries (batch * h_kv * n_q * top_k), n_q < 2^25
+ * and batch * h_q * n_q * d_h < 2^35 output elements; larger calls return UNSUPPORTED.
  */
 int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k, const void *v,
                             const int32_t *sel, void *o, float *lse, void *workspace,
