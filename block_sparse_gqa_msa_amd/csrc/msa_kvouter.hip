@@ -364,14 +364,16 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
     }
 
     const int n_tiles = (n_e + QPT - 1) / QPT;
+    // Q rows of tile tt. The loads are unconditional (lanes past the chunk's entries read
+    // the first entry's row; their columns are masked and never stored) so that the
+    // prefetch of the next tile stays in flight: a load under a branch makes the compiler
+    // wait for every outstanding load before the next use of any of them.
     auto load_q = [&](int tt, F (&dst)[DC]) {
       const int e = tt * QPT + qi;
-      const bool ok = tt < n_tiles && e < n_e;
-      const int t = ok ? (s_list[e] >> 6) : 0;
+      const int t = s_list[(tt < n_tiles && e < n_e) ? e : 0] >> 6;
+      const E *src = q + (((long)b * a.h_q + h) * a.n_q + t) * DH + g * 8;
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        dst[dc] = ok ? load_frag(q + (((long)b * a.h_q + h) * a.n_q + t) * DH + dc * 32 + g * 8)
-                     : zero_frag(q);
+      for (int dc = 0; dc < DC; ++dc) dst[dc] = load_frag(src + dc * 32);
     };
     F bq[DC], bq_next[DC];
     load_q(w, bq);
