@@ -6,7 +6,9 @@
 // empty slot) and a wave holding V items per lane finds the exact m-th item by
 //   1. a ballot-counted bitwise search over the 64 lane maxima (a lower bound on the
 //      threshold that at least m items reach),
-//   2. ranking only the items at or above that bound (normally a few dozen) in LDS,
+//   2. compacting the items at or above that bound (normally a few dozen) into LDS and
+//      finding the exact m-th among them by a second bitwise search (keys, then indices
+//      for ties at the threshold),
 //   3. an exact bitwise search over all items when ties make that set too large.
 #pragma once
 
@@ -21,66 +23,81 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // Exact m-th item (1 <= m <= 63) of the wave's items under (key desc, idx asc); at least m
 // slots are non-empty. lk / li: wave-private LDS of SELECT_CAP + 1 entries. On return, an
 // item is among the best m iff key > kstar || (key == kstar && idx <= istar).
+// Returns C >= m when the items with key >= a lower bound T (C of them, in item order:
+// slot-major, then lane) are left in lk / li, or -1 when heavy ties sent it to the
+// exhaustive search (lk / li then hold nothing useful).
 template <int V>
-__device__ void wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V], int m,
-                               uint32_t *lk, int32_t *li, uint32_t &kstar, int32_t &istar) {
+__device__ int wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V], int m,
+                              uint32_t *lk, int32_t *li, uint32_t &kstar, int32_t &istar) {
   constexpr int CAP = SELECT_CAP;
-  const int lane = lane_id();
+  constexpr int Q = CAP / 64;
   uint32_t lm = 0;
 #pragma unroll
   for (int s = 0; s < V; ++s) lm = max(lm, key[s]);
+  // Largest T that at least m lane maxima reach: at least m items are >= T.
   uint32_t T = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t c = T | (1u << bit);
     if (popc64(ballot(lm >= c)) >= m) T = c;
   }
   T = max(T, 1u);
+  // Compact the items >= T into LDS in item order (positions past CAP are dropped).
   int C = 0;
 #pragma unroll
-  for (int s = 0; s < V; ++s) C += popc64(ballot(key[s] >= T));
-
+  for (int s = 0; s < V; ++s) {
+    const bool pr = key[s] >= T;
+    const uint64_t mk = ballot(pr);
+    const int pos = C + rank_below(mk);
+    if (pr && pos < CAP) {
+      lk[pos] = key[s];
+      li[pos] = idx[s];
+    }
+    C += popc64(mk);
+  }
   if (C <= CAP) {
-    int base = 0;
+    lds_wait();
+    const int nq = (C + 63) >> 6;  // wave-uniform
+    uint32_t ck[Q];
+    int32_t ci[Q];
 #pragma unroll
-    for (int s = 0; s < V; ++s) {
-      const bool pr = key[s] >= T;
-      const uint64_t mk = ballot(pr);
-      if (pr) {
-        const int pos = base + rank_below(mk);
-        lk[pos] = key[s];
-        li[pos] = idx[s];
+    for (int q = 0; q < Q; ++q) {
+      const int j = lane_id() + 64 * q;
+      ck[q] = (q < nq && j < C) ? lk[j] : 0u;
+      ci[q] = (q < nq && j < C) ? li[j] : 0x7fffffff;
+    }
+    // The m-th largest candidate key K, by a ballot-counted bitwise search.
+    uint32_t K = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = K | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if (q < nq) cnt += popc64(ballot(ck[q] >= c));
+      if (cnt >= m) K = c;
+    }
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (q < nq) {
+        ngt += popc64(ballot(ck[q] > K));
+        neq += popc64(ballot(ck[q] == K));
       }
-      base += popc64(mk);
-    }
-    lds_wait();
-    uint32_t ck[CAP / 64];
-    int32_t ci[CAP / 64];
-    int rk[CAP / 64];
+    const int need = m - ngt;  // 1 <= need <= neq
+    int32_t X = 0x7fffffff;    // all items with key K are taken ...
+    if (neq > need) {          // ... unless ties at K: then the `need` lowest indices
+      X = 0;
+      for (int bit = 30; bit >= 0; --bit) {
+        const int32_t c = X | (1 << bit);
+        int cnt = 0;
 #pragma unroll
-    for (int q = 0; q < CAP / 64; ++q) {
-      const int j = lane + 64 * q;
-      ck[q] = j < C ? lk[j] : 0u;
-      ci[q] = j < C ? li[j] : 0x7fffffff;
-      rk[q] = 0;
-    }
-    for (int x = 0; x < C; ++x) {
-      const uint32_t kx = lk[x];
-      const int32_t ix = li[x];
-#pragma unroll
-      for (int q = 0; q < CAP / 64; ++q) rk[q] += (kx > ck[q]) || (kx == ck[q] && ix < ci[q]);
-    }
-    lds_wait();
-#pragma unroll
-    for (int q = 0; q < CAP / 64; ++q)
-      if (lane + 64 * q < C && rk[q] == m - 1) {
-        lk[CAP] = ck[q];
-        li[CAP] = ci[q];
+        for (int q = 0; q < Q; ++q)
+          if (q < nq) cnt += popc64(ballot(ck[q] == K && ci[q] < c));
+        if (cnt < need) X = c;
       }
-    lds_wait();
-    kstar = lk[CAP];
-    istar = li[CAP];
-    lds_wait();
-    return;
+    }
+    kstar = K;
+    istar = X;
+    return C;
   }
   // Heavy ties: exact search over every item.
   T = 0;
@@ -105,6 +122,7 @@ __device__ void wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V]
   }
   kstar = T;
   istar = X;
+  return -1;
 }
 
 __device__ __forceinline__ bool taken(uint32_t k, int32_t i, uint32_t ks, int32_t is) {

@@ -55,38 +55,46 @@ __global__ __launch_bounds__(256) void topk_pass1(TopkArgs a) {
     key[s] = c < n_c ? order_key(row[c]) : 0u;
   }
   const int valid = min(TOPK_CHUNK, n_c - base);
-  if (nch == 1) {
-    uint32_t ks;
-    int32_t is;
-    wave_threshold(key, idx, m, s_key[w], s_idx[w], ks, is);
-    int pos = 0;
+  const bool single = nch == 1;
+  uint32_t *ck = a.cand_key + (pid * a.n_chunks + chunk) * (long)m;
+  int32_t *ci = a.cand_idx + (pid * a.n_chunks + chunk) * (long)m;
+  // Write the winners in item order (= ascending block order): to sel for a single chunk,
+  // else as this chunk's candidates.
+  auto put = [&](int at, uint32_t kv, int32_t iv) {
+    if (single) {
+      out[at] = iv;
+    } else {
+      ck[at] = kv;
+      ci[at] = iv;
+    }
+  };
+  uint32_t ks = 0;
+  int32_t is = 0x7fffffff;
+  int C = -1;
+  if (valid > m) C = wave_threshold(key, idx, m, s_key[w], s_idx[w], ks, is);
+  int pos = 0;
+  if (C >= 0) {  // the winners are among the C candidates left in LDS, in item order
+    for (int q = 0; q * 64 < C; ++q) {
+      const int j = q * 64 + lane;
+      const uint32_t kv = j < C ? s_key[w][j] : 0u;
+      const int32_t iv = j < C ? s_idx[w][j] : 0;
+      const bool pr = taken(kv, iv, ks, is);
+      const uint64_t mk = ballot(pr);
+      if (pr) put(pos + rank_below(mk), kv, iv);
+      pos += popc64(mk);
+    }
+  } else {
 #pragma unroll
     for (int s = 0; s < V; ++s) {  // slot-major order is ascending block order
       const bool pr = taken(key[s], idx[s], ks, is);
       const uint64_t mk = ballot(pr);
-      if (pr) out[pos + rank_below(mk)] = idx[s];
+      if (pr) put(pos + rank_below(mk), key[s], idx[s]);
       pos += popc64(mk);
     }
+  }
+  if (single) {
     if (lane == 0) out[m] = local;
-    return;
-  }
-  uint32_t *ck = a.cand_key + (pid * a.n_chunks + chunk) * (long)m;
-  int32_t *ci = a.cand_idx + (pid * a.n_chunks + chunk) * (long)m;
-  uint32_t ks = 0;
-  int32_t is = 0x7fffffff;
-  if (valid > m) wave_threshold(key, idx, m, s_key[w], s_idx[w], ks, is);
-  int pos = 0;
-#pragma unroll
-  for (int s = 0; s < V; ++s) {
-    const bool pr = taken(key[s], idx[s], ks, is);
-    const uint64_t mk = ballot(pr);
-    if (pr) {
-      ck[pos + rank_below(mk)] = key[s];
-      ci[pos + rank_below(mk)] = idx[s];
-    }
-    pos += popc64(mk);
-  }
-  if (lane >= pos && lane < m) {  // a short last chunk leaves empty slots
+  } else if (lane >= pos && lane < m) {  // a short last chunk leaves empty slots
     ck[lane] = 0u;
     ci[lane] = -1;
   }
