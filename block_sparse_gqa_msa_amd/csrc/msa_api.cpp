@@ -152,6 +152,8 @@ int key_chunk_prefill(const msa_shape &s) {
   const long long avg_keys = (long long)s.q_start + s.n_q / 2 + 1;
   int kc = 8192;
   while (kc > 512 && tiles * ((avg_keys + kc - 1) / kc) < 4096) kc /= 2;
+  const long long keys = (long long)s.q_start + s.n_q;
+  while ((keys + kc - 1) / kc > 65535) kc *= 2;  // key chunks are the grid's y dimension
   return kc;
 }
 

@@ -34,7 +34,11 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
     p[i] = value;
 }
 
-// Prefill / chunked prefill. Grid: x = key chunk, y = query tile, z = sequence.
+// Prefill / chunked prefill. Grid: x = query tile, y = key chunk, z = sequence. The query
+// tile varies fastest so that consecutive workgroups, which the dispatcher deals round-robin
+// to the eight XCDs, have the same amount of causal work: with the key chunk fastest, the
+// XCD would be fixed by the chunk index and the early chunks (present in every row) would
+// pile onto a few XCDs. Workgroups on one XCD then also share the chunk's k_idx in L2.
 // A workgroup owns TQ = 256 / R query rows for all R groups (256 columns; wave w takes
 // columns 64w..64w+63 as four 16-column N-tiles) and one chunk of keys. The k_idx tile
 // is staged once in LDS (double-buffered) and feeds every group: the index key is shared.
@@ -55,10 +59,10 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int R = a.h_kv, TQ = WG_COLS / R;
   const int b = blockIdx.z;
-  const int t0 = blockIdx.y * TQ;
+  const int t0 = blockIdx.x * TQ;
   const int t_last = min(t0 + TQ, a.n_q) - 1;
   const long p_first = (long)a.q_start + t0, p_last = (long)a.q_start + t_last;
-  const long k_begin = (long)blockIdx.x * a.key_chunk;
+  const long k_begin = (long)blockIdx.y * a.key_chunk;
   if (k_begin > p_last) return;  // uniform over the workgroup
   const long k_end = min(k_begin + (long)a.key_chunk, p_last + 1);
   const int n_tiles = (int)((k_end - k_begin + KT - 1) / KT);
@@ -370,7 +374,7 @@ template <typename E, int DI, int BS>
 hipError_t launch_prefill_t(const IndexArgs &a, hipStream_t s) {
   const int TQ = WG_COLS / a.h_kv;
   const long keys = (long)a.q_start + a.n_q;  // last position + 1
-  dim3 grid((unsigned)((keys + a.key_chunk - 1) / a.key_chunk), (unsigned)((a.n_q + TQ - 1) / TQ),
+  dim3 grid((unsigned)((a.n_q + TQ - 1) / TQ), (unsigned)((keys + a.key_chunk - 1) / a.key_chunk),
             (unsigned)a.batch);
   hipLaunchKernelGGL((index_pool_prefill<E, DI, BS>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
