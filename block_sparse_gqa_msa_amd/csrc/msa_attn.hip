@@ -48,12 +48,13 @@ struct VRegs<bf16_t, DH, BS> {  // key pairs packed into dwords
   u32x4 a[PIECES], b[PIECES];
   __device__ __forceinline__ void load(const bf16_t *vp, long kb, int n_k) {
     const int lane = lane_id(), kp = lane % PAIRS, seg = lane / PAIRS;
-    const long j0 = kb + 2 * kp, j1 = j0 + 1;
+    // keys past the end read the last key instead: their probabilities are 0
+    const long j0 = min(kb + 2 * kp, (long)n_k - 1), j1 = min(kb + 2 * kp + 1, (long)n_k - 1);
 #pragma unroll
     for (int i = 0; i < PIECES; ++i) {
       const int d0 = seg * DSEG + i * 8;
-      a[i] = j0 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
-      b[i] = j1 < n_k ? *reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0) : u32x4{0u, 0u, 0u, 0u};
+      a[i] = *reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0);
+      b[i] = *reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0);
     }
   }
   __device__ __forceinline__ void store_t(unsigned char *vt) const {
@@ -79,11 +80,10 @@ struct VRegs<float, DH, BS> {
   f32x4 a[PIECES];
   __device__ __forceinline__ void load(const float *vp, long kb, int n_k) {
     const int lane = lane_id(), key = lane % BS, seg = lane / BS;
-    const long j = kb + key;
+    const long j = min(kb + key, (long)n_k - 1);  // past the end: probability 0
 #pragma unroll
     for (int i = 0; i < PIECES; ++i)
-      a[i] = j < n_k ? *reinterpret_cast<const f32x4 *>(vp + j * DH + seg * DSEG + i * 4)
-                     : f32x4{0.f, 0.f, 0.f, 0.f};
+      a[i] = *reinterpret_cast<const f32x4 *>(vp + j * DH + seg * DSEG + i * 4);
   }
   __device__ __forceinline__ void store_t(unsigned char *vt) const {
     constexpr int ROW = VStage<float, DH, BS>::ROW;
@@ -129,18 +129,23 @@ __device__ __forceinline__ void attend_block(RowState<E, DH, BS> &st,
   constexpr int DC = DH / 32, KTN = BS / 16, DT = DH / 16;
   const int lane = lane_id(), g = lane >> 4, c16 = lane & 15;
 
+  // All loads are unconditional (keys past the end read the last key and are masked below):
+  // a load under a branch would make every MFMA wait for all loads issued before it.
   VRegs<E, DH, BS> vr;
   vr.load(vp, kb, n_k);  // in flight during the score MFMAs
+  F ka[KTN][DC];
+#pragma unroll
+  for (int kt = 0; kt < KTN; ++kt) {
+    const long j = min(kb + kt * 16 + c16, (long)n_k - 1);
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) ka[kt][dc] = load_frag(kp + j * DH + dc * 32 + g * 8);
+  }
   f32x4 s[KTN];
 #pragma unroll
   for (int kt = 0; kt < KTN; ++kt) {
-    const long j = kb + kt * 16 + c16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dc = 0; dc < DC; ++dc) {
-      const F a = j < n_k ? load_frag(kp + j * DH + dc * 32 + g * 8) : zero_frag(kp);
-      acc = mfma_chunk(a, bq[dc], acc);
-    }
+    for (int dc = 0; dc < DC; ++dc) acc = mfma_chunk(ka[kt][dc], bq[dc], acc);
     s[kt] = acc;
   }
   float mx = -INFINITY;
@@ -277,8 +282,11 @@ __global__ __launch_bounds__(256) void attn_decode_merge(AttnArgs a) {
     for (int u = 0; u < 8; ++u) {
       const int sp = s0 + u;
       wv[u] = __shfl(wl, sp & 63);  // 0 for splits past S (their lanes hold weight 0)
+      // unconditional loads (every split's partial is written, zeros if it saw no key);
+      // splits past S re-read the last one and are weighted 0
+      const int spc = min(sp, S - 1);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) pv[u][i] = (sp < S && wv[u] != 0.f) ? pbase[sp * DH + 64 * i] : 0.f;
+      for (int i = 0; i < PER; ++i) pv[u][i] = pbase[spc * DH + 64 * i];
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)

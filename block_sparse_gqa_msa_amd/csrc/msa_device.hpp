@@ -116,6 +116,15 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Pin a loaded value: an empty asm that reads and writes it. A load whose result only
+// some lanes use can otherwise be moved under a branch on those lanes, and loads under
+// branches are issued one at a time (each waits for the one before). Issue every load of
+// a batch first, then pin them all.
+template <typename T>
+__device__ __forceinline__ void pin(T &x) {
+  asm volatile("" : "+v"(x));
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 // Number of set bits of m below this lane.

@@ -282,14 +282,15 @@ __global__ __launch_bounds__(512) void index_select_decode(IndexArgs a) {
                        : zero_frag(qi);
   const long kw0 = (long)(c0 + w * NBW) * BS;  // this wave's first key
   constexpr int NT = NBW * BS / KT;            // key tiles per wave
+  // Keys past p read key p instead (pool masks them): unconditional loads keep the next
+  // tile's loads in flight, where a load under a branch would make the MFMAs wait for all.
   auto fetch = [&](int tile, F (&dst)[4][DC]) {
     const long k0 = kw0 + (long)tile * KT;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const long j = k0 + mt * 16 + c16;
+      const long j = min(k0 + mt * 16 + c16, p);
 #pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        dst[mt][dc] = (j < a.n_k && j <= p) ? load_frag(ki + j * DI + dc * 32 + g * 8) : zero_frag(ki);
+      for (int dc = 0; dc < DC; ++dc) dst[mt][dc] = load_frag(ki + j * DI + dc * 32 + g * 8);
     }
   };
   auto pool = [&](int tile, const F (&cur)[4][DC]) {
@@ -314,15 +315,15 @@ __global__ __launch_bounds__(512) void index_select_decode(IndexArgs a) {
   };
   // double-buffered key tiles: the next tile's fragments load while this one computes
   const int nt = (int)min((long)NT, (p - kw0) / KT + 1);  // tiles with a visible key
+  // The prefetches are unconditional too: past the last tile they re-read the last tile
+  // (a cache hit) rather than branch around the load.
   F fa[4][DC], fb[4][DC];
   if (nt > 0) fetch(0, fa);
   for (int tile = 0; tile < nt; tile += 2) {
-    if (tile + 1 < nt) fetch(tile + 1, fb);
+    fetch(min(tile + 1, nt - 1), fb);
     pool(tile, fa);
-    if (tile + 1 < nt) {
-      if (tile + 2 < nt) fetch(tile + 2, fa);
-      pool(tile + 1, fb);
-    }
+    fetch(min(tile + 2, nt - 1), fa);
+    if (tile + 1 < nt) pool(tile + 1, fb);
   }
   __syncthreads();
 

@@ -238,8 +238,11 @@ struct KvLds {
 };
 
 // Stage block rows [kb, kb+BS) of K (row-major) and V (transposed) into LDS, 256 threads.
-// bf16 loads are non-temporal: a block is staged once per chunk and its lines are not
-// worth keeping in L2 over the Q rows the chunks gather.
+// Every load of the block is issued before the first LDS write: rows past n_k read row
+// n_k - 1 instead (their keys are masked and their probabilities are 0), so no load sits
+// under a branch, which would make each wait for the one before. bf16 loads are
+// non-temporal: a block is staged once per chunk and its lines are not worth keeping in L2
+// over the Q rows the chunks gather.
 template <typename E, int DH, int BS>
 __device__ __forceinline__ void stage_block(const E *kp, const E *vp, long kb, int n_k,
                                             unsigned char *ks, unsigned char *vt) {
@@ -247,40 +250,82 @@ __device__ __forceinline__ void stage_block(const E *kp, const E *vp, long kb, i
   const int tid = threadIdx.x;
   constexpr int KPIECES = BS * DH * L::ES / 16;
   constexpr int PER_ROW = DH * L::ES / 16;
-  for (int pc = tid; pc < KPIECES; pc += 256) {
-    const int key = pc / PER_ROW, off = pc % PER_ROW;
-    const long j = kb + key;
-    const u32x4 x = j < n_k ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                                  reinterpret_cast<const unsigned char *>(kp + j * DH) + off * 16))
-                            : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4 *>(ks + key * L::KROW + off * 16) = x;
+  constexpr int KPT = (KPIECES + 255) / 256;
+  const long last = (long)n_k - 1;
+  u32x4 kx[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int pc = min(tid + 256 * i, KPIECES - 1);
+    const long j = min(kb + pc / PER_ROW, last);
+    kx[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+        reinterpret_cast<const unsigned char *>(kp + j * DH) + (pc % PER_ROW) * 16));
   }
   if constexpr (L::ES == 2) {
     constexpr int PAIRS = BS / 2, VPIECES = PAIRS * (DH / 8);
-    for (int pc = tid; pc < VPIECES; pc += 256) {
-      const int kpair = pc % PAIRS, d0 = (pc / PAIRS) * 8;
-      const long j0 = kb + 2 * kpair, j1 = j0 + 1;
-      const u32x4 x = j0 < n_k ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0))
-                               : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 y = j1 < n_k ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0))
-                               : u32x4{0u, 0u, 0u, 0u};
+    constexpr int VPT = (VPIECES + 255) / 256;
+    u32x4 vx[VPT], vy[VPT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e) * L::VROW + kpair * 4) =
-            (x[e] & 0xffffu) | (y[e] << 16);
-        *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e + 1) * L::VROW + kpair * 4) =
-            (x[e] >> 16) | (y[e] & 0xffff0000u);
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = min(tid + 256 * i, VPIECES - 1);
+      const int kpair = pc % PAIRS, d0 = (pc / PAIRS) * 8;
+      const long j0 = min(kb + 2 * kpair, last), j1 = min(kb + 2 * kpair + 1, last);
+      vx[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + j0 * DH + d0));
+      vy[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + j1 * DH + d0));
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) pin(kx[i]);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      pin(vx[i]);
+      pin(vy[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int pc = tid + 256 * i;
+      if (KPIECES % 256 == 0 || pc < KPIECES)
+        *reinterpret_cast<u32x4 *>(ks + (pc / PER_ROW) * L::KROW + (pc % PER_ROW) * 16) = kx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + 256 * i;
+      if (VPIECES % 256 == 0 || pc < VPIECES) {
+        const int kpair = pc % PAIRS, d0 = (pc / PAIRS) * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = vx[i][e], y = vy[i][e];
+          *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e) * L::VROW + kpair * 4) = (x & 0xffffu) | (y << 16);
+          *reinterpret_cast<uint32_t *>(vt + (d0 + 2 * e + 1) * L::VROW + kpair * 4) = (x >> 16) | (y & 0xffff0000u);
+        }
       }
     }
   } else {
     constexpr int VPIECES = BS * (DH / 4);
-    for (int pc = tid; pc < VPIECES; pc += 256) {
-      const int key = pc % BS, d0 = (pc / BS) * 4;
-      const long j = kb + key;
-      const f32x4 x = j < n_k ? *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(vp) + j * DH + d0)
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int VPT = (VPIECES + 255) / 256;
+    f32x4 vx[VPT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) *reinterpret_cast<float *>(vt + (d0 + e) * L::VROW + key * 4) = x[e];
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = min(tid + 256 * i, VPIECES - 1);
+      const long j = min(kb + pc % BS, last);
+      vx[i] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(vp) + j * DH + (pc / BS) * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) pin(kx[i]);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) pin(vx[i]);
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int pc = tid + 256 * i;
+      if (KPIECES % 256 == 0 || pc < KPIECES)
+        *reinterpret_cast<u32x4 *>(ks + (pc / PER_ROW) * L::KROW + (pc % PER_ROW) * 16) = kx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int pc = tid + 256 * i;
+      if (VPIECES % 256 == 0 || pc < VPIECES) {
+        const int key = pc % BS, d0 = (pc / BS) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *reinterpret_cast<float *>(vt + (d0 + e) * L::VROW + key * 4) = vx[i][e];
+      }
     }
   }
 }

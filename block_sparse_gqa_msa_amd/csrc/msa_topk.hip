@@ -7,6 +7,8 @@
 // ascending, -1 padded.
 //
 // No exponentials and no sort: see msa_select.hpp for the wave-level exact threshold.
+// Items past the end load from a valid address and are then blanked; the loads of a batch are
+// issued together and pinned (see pin()), since loads under branches go one at a time.
 // Problems with more than TOPK_CHUNK candidate blocks are cut into chunks whose best
 // top_k-1 are merged by a second pass with the same routine.
 #include "msa_device.hpp"
@@ -48,11 +50,16 @@ __global__ __launch_bounds__(256) void topk_pass1(TopkArgs a) {
   const float *row = a.bmax + pid * (long)a.n_blocks;
   uint32_t key[V];
   int32_t idx[V];
+  float x[V];
+#pragma unroll
+  for (int s = 0; s < V; ++s) x[s] = row[min(base + s * 64 + lane, n_c - 1)];
+#pragma unroll
+  for (int s = 0; s < V; ++s) pin(x[s]);
 #pragma unroll
   for (int s = 0; s < V; ++s) {
     const int c = base + s * 64 + lane;
     idx[s] = c;
-    key[s] = c < n_c ? order_key(row[c]) : 0u;
+    key[s] = c < n_c ? order_key(x[s]) : 0u;
   }
   const int valid = min(TOPK_CHUNK, n_c - base);
   const bool single = nch == 1;
@@ -132,9 +139,20 @@ __global__ __launch_bounds__(256) void topk_pass2(TopkArgs a) {
   int32_t idx[V];
 #pragma unroll
   for (int s = 0; s < V; ++s) {
-    const int e = s * 64 + lane;
-    key[s] = e < total ? ck[e] : 0u;
-    idx[s] = e < total ? ci[e] : 0x7fffffff;
+    const int ec = min(s * 64 + lane, total - 1);  // unconditional loads (see below)
+    key[s] = ck[ec];
+    idx[s] = ci[ec];
+  }
+#pragma unroll
+  for (int s = 0; s < V; ++s) {
+    pin(key[s]);
+    pin(idx[s]);
+  }
+#pragma unroll
+  for (int s = 0; s < V; ++s) {
+    const bool in = s * 64 + lane < total;
+    key[s] = in ? key[s] : 0u;
+    idx[s] = in ? idx[s] : 0x7fffffff;
   }
   uint32_t ks;
   int32_t is;
@@ -159,6 +177,109 @@ __global__ __launch_bounds__(256) void topk_pass2(TopkArgs a) {
   if (lane == 0) out[m] = local;
 }
 
+// Final merge for few problems with many candidates (decode: one problem per (sequence,
+// group), the winners of every key range of the sequence): a workgroup of MW waves per
+// problem. Each wave keeps the best m of its share of the candidates; the first wave then
+// takes the best m of those MW * m and writes them in ascending block order, local block last.
+constexpr int MW = 8;            // waves per problem
+constexpr int MV = TOPK_CHUNK / (64 * MW);  // candidates per lane in the first stage
+
+__global__ __launch_bounds__(MW * 64) void topk_merge_wide(TopkArgs a) {
+  __shared__ uint32_t s_key[MW][CAP + 1];
+  __shared__ int32_t s_idx[MW][CAP + 1];
+  __shared__ uint32_t w_key[MW * 64];  // per-wave winners, padded with key 0
+  __shared__ int32_t w_idx[MW * 64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long pid = blockIdx.x;
+  const int t = (int)(pid % a.n_q);
+  const long p = (long)a.q_start + t;
+  const int local = (int)(p / a.block_size);
+  const int k = a.top_k, m = k - 1;
+  int32_t *out = a.sel + pid * k;
+  if (local + 1 <= k || m == 0) {  // sees k blocks or fewer, or k == 1 (uniform)
+    if (w == 0) {
+      if (local + 1 <= k) {
+        if (lane < k) out[lane] = lane <= local ? lane : -1;
+      } else if (lane == 0) {
+        out[0] = local;
+      }
+    }
+    return;
+  }
+  const int nch = (local + a.chunk_blocks - 1) / a.chunk_blocks;
+  const int total = nch * m;  // <= TOPK_CHUNK (checked on the host)
+  const uint32_t *ck = a.cand_key + pid * a.n_chunks * (long)m;
+  const int32_t *ci = a.cand_idx + pid * a.n_chunks * (long)m;
+  // Stage 1: wave w ranks items [w * 64 * MV, (w + 1) * 64 * MV).
+  uint32_t key[MV];
+  int32_t idx[MV];
+  int nv = 0;
+#pragma unroll
+  for (int s = 0; s < MV; ++s) {
+    const int ec = min((w * MV + s) * 64 + lane, total - 1);  // unconditional loads
+    key[s] = ck[ec];
+    idx[s] = ci[ec];
+  }
+#pragma unroll
+  for (int s = 0; s < MV; ++s) {
+    pin(key[s]);
+    pin(idx[s]);
+  }
+#pragma unroll
+  for (int s = 0; s < MV; ++s) {
+    const bool in = (w * MV + s) * 64 + lane < total;
+    key[s] = in ? key[s] : 0u;
+    idx[s] = in ? idx[s] : 0x7fffffff;
+    nv += popc64(ballot(key[s] != 0u));
+  }
+  uint32_t ks = 0;
+  int32_t is = 0x7fffffff;
+  if (nv > m) wave_threshold(key, idx, m, s_key[w], s_idx[w], ks, is);
+  int pos = 0;
+#pragma unroll
+  for (int s = 0; s < MV; ++s) {
+    const bool pr = taken(key[s], idx[s], ks, is);
+    const uint64_t mk = ballot(pr);
+    if (pr) {
+      w_key[w * 64 + pos + rank_below(mk)] = key[s];
+      w_idx[w * 64 + pos + rank_below(mk)] = idx[s];
+    }
+    pos += popc64(mk);
+  }
+  if (lane >= pos) {
+    w_key[w * 64 + lane] = 0u;
+    w_idx[w * 64 + lane] = 0x7fffffff;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  // Stage 2: the best m of the waves' winners.
+  uint32_t k2[MW];
+  int32_t i2[MW];
+#pragma unroll
+  for (int s = 0; s < MW; ++s) {
+    k2[s] = w_key[s * 64 + lane];
+    i2[s] = w_idx[s * 64 + lane];
+  }
+  wave_threshold(k2, i2, m, s_key[0], s_idx[0], ks, is);
+  uint32_t *list = reinterpret_cast<uint32_t *>(s_idx[0]);
+  pos = 0;
+#pragma unroll
+  for (int s = 0; s < MW; ++s) {
+    const bool pr = taken(k2[s], i2[s], ks, is);
+    const uint64_t mk = ballot(pr);
+    if (pr) list[pos + rank_below(mk)] = (uint32_t)i2[s];
+    pos += popc64(mk);
+  }
+  lds_wait();
+  if (lane < m) {  // place each winner by its rank in block order
+    const uint32_t mine = list[lane];
+    int rank = 0;
+    for (int x = 0; x < m; ++x) rank += list[x] < mine;
+    out[rank] = (int32_t)mine;
+  }
+  if (lane == 0) out[m] = local;
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
@@ -173,7 +294,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
 
 hipError_t launch_topk_final(const TopkArgs &a, hipStream_t s) {
   const long n_prob = (long)a.batch * a.h_kv * a.n_q;
-  hipLaunchKernelGGL(topk_pass2, dim3((unsigned)((n_prob + 3) / 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(topk_merge_wide, dim3((unsigned)n_prob), dim3(MW * 64), 0, s, a);
   return hipGetLastError();
 }
 
