@@ -157,22 +157,15 @@ __global__ __launch_bounds__(256) void topk_pass2(TopkArgs a) {
   uint32_t ks;
   int32_t is;
   wave_threshold(key, idx, m, s_key[w], s_idx[w], ks, is);
-  // Collect the m winners, then place each by its rank in block order.
-  uint32_t *list = reinterpret_cast<uint32_t *>(s_idx[w]);
+  // The chunks' winners were written in ascending block order, chunk after chunk, so the
+  // items are in ascending order (padding is never taken): compact the m winners in order.
   int pos = 0;
 #pragma unroll
   for (int s = 0; s < V; ++s) {
     const bool pr = taken(key[s], idx[s], ks, is);
     const uint64_t mk = ballot(pr);
-    if (pr) list[pos + rank_below(mk)] = (uint32_t)idx[s];
+    if (pr) out[pos + rank_below(mk)] = idx[s];
     pos += popc64(mk);
-  }
-  lds_wait();
-  if (lane < m) {
-    const uint32_t mine = list[lane];
-    int rank = 0;
-    for (int x = 0; x < m; ++x) rank += list[x] < mine;
-    out[rank] = (int32_t)mine;
   }
   if (lane == 0) out[m] = local;
 }
@@ -261,21 +254,16 @@ __global__ __launch_bounds__(MW * 64) void topk_merge_wide(TopkArgs a) {
     i2[s] = w_idx[s * 64 + lane];
   }
   wave_threshold(k2, i2, m, s_key[0], s_idx[0], ks, is);
-  uint32_t *list = reinterpret_cast<uint32_t *>(s_idx[0]);
+  // Candidates arrive in ascending block order (key range after key range), each wave keeps
+  // its winners in that order and the waves cover consecutive shares: compacting the
+  // winners in item order gives ascending blocks.
   pos = 0;
 #pragma unroll
   for (int s = 0; s < MW; ++s) {
     const bool pr = taken(k2[s], i2[s], ks, is);
     const uint64_t mk = ballot(pr);
-    if (pr) list[pos + rank_below(mk)] = (uint32_t)i2[s];
+    if (pr) out[pos + rank_below(mk)] = i2[s];
     pos += popc64(mk);
-  }
-  lds_wait();
-  if (lane < m) {  // place each winner by its rank in block order
-    const uint32_t mine = list[lane];
-    int rank = 0;
-    for (int x = 0; x < m; ++x) rank += list[x] < mine;
-    out[rank] = (int32_t)mine;
   }
   if (lane == 0) out[m] = local;
 }
