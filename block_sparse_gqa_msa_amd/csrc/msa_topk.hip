@@ -21,6 +21,72 @@ namespace {
 constexpr int V = TOPK_CHUNK / 64;  // items per lane
 constexpr int CAP = SELECT_CAP;
 
+// Best m of candidates [base, base + valid) of one problem's block scores, VI per lane.
+template <int VI>
+__device__ __forceinline__ void select_chunk(const TopkArgs &a, long pid, int chunk, int base,
+                                             int n_c, int valid, bool single, int local,
+                                             uint32_t *lk, int32_t *li) {
+  const int lane = lane_id();
+  const int m = a.top_k - 1;
+  int32_t *out = a.sel + pid * a.top_k;
+  const float *row = a.bmax + pid * (long)a.n_blocks;
+  uint32_t key[VI];
+  int32_t idx[VI];
+  float x[VI];
+#pragma unroll
+  for (int s = 0; s < VI; ++s) x[s] = row[min(base + s * 64 + lane, n_c - 1)];
+#pragma unroll
+  for (int s = 0; s < VI; ++s) pin(x[s]);
+#pragma unroll
+  for (int s = 0; s < VI; ++s) {
+    const int c = base + s * 64 + lane;
+    idx[s] = c;
+    key[s] = c < n_c ? order_key(x[s]) : 0u;
+  }
+  uint32_t *ck = a.cand_key + (pid * a.n_chunks + chunk) * (long)m;
+  int32_t *ci = a.cand_idx + (pid * a.n_chunks + chunk) * (long)m;
+  // Write the winners in item order (= ascending block order): to sel for a single chunk,
+  // else as this chunk's candidates.
+  auto put = [&](int at, uint32_t kv, int32_t iv) {
+    if (single) {
+      out[at] = iv;
+    } else {
+      ck[at] = kv;
+      ci[at] = iv;
+    }
+  };
+  uint32_t ks = 0;
+  int32_t is = 0x7fffffff;
+  int C = -1;
+  if (valid > m) C = wave_threshold(key, idx, m, lk, li, ks, is);
+  int pos = 0;
+  if (C >= 0) {  // the winners are among the C candidates left in LDS, in item order
+    for (int q = 0; q * 64 < C; ++q) {
+      const int j = q * 64 + lane;
+      const uint32_t kv = j < C ? lk[j] : 0u;
+      const int32_t iv = j < C ? li[j] : 0;
+      const bool pr = taken(kv, iv, ks, is);
+      const uint64_t mk = ballot(pr);
+      if (pr) put(pos + rank_below(mk), kv, iv);
+      pos += popc64(mk);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < VI; ++s) {  // slot-major order is ascending block order
+      const bool pr = taken(key[s], idx[s], ks, is);
+      const uint64_t mk = ballot(pr);
+      if (pr) put(pos + rank_below(mk), key[s], idx[s]);
+      pos += popc64(mk);
+    }
+  }
+  if (single) {
+    if (lane == 0) out[m] = local;
+  } else if (lane >= pos && lane < m) {  // a short last chunk leaves empty slots
+    ck[lane] = 0u;
+    ci[lane] = -1;
+  }
+}
+
 // Pass 1. Grid: x = groups of 4 problems (one wave each), y = chunk.
 __global__ __launch_bounds__(256) void topk_pass1(TopkArgs a) {
   __shared__ uint32_t s_key[4][CAP + 1];
@@ -47,64 +113,14 @@ __global__ __launch_bounds__(256) void topk_pass1(TopkArgs a) {
   const int nch = (n_c + TOPK_CHUNK - 1) / TOPK_CHUNK;
   if (chunk >= nch) return;
   const int base = chunk * TOPK_CHUNK;
-  const float *row = a.bmax + pid * (long)a.n_blocks;
-  uint32_t key[V];
-  int32_t idx[V];
-  float x[V];
-#pragma unroll
-  for (int s = 0; s < V; ++s) x[s] = row[min(base + s * 64 + lane, n_c - 1)];
-#pragma unroll
-  for (int s = 0; s < V; ++s) pin(x[s]);
-#pragma unroll
-  for (int s = 0; s < V; ++s) {
-    const int c = base + s * 64 + lane;
-    idx[s] = c;
-    key[s] = c < n_c ? order_key(x[s]) : 0u;
-  }
   const int valid = min(TOPK_CHUNK, n_c - base);
-  const bool single = nch == 1;
-  uint32_t *ck = a.cand_key + (pid * a.n_chunks + chunk) * (long)m;
-  int32_t *ci = a.cand_idx + (pid * a.n_chunks + chunk) * (long)m;
-  // Write the winners in item order (= ascending block order): to sel for a single chunk,
-  // else as this chunk's candidates.
-  auto put = [&](int at, uint32_t kv, int32_t iv) {
-    if (single) {
-      out[at] = iv;
-    } else {
-      ck[at] = kv;
-      ci[at] = iv;
-    }
-  };
-  uint32_t ks = 0;
-  int32_t is = 0x7fffffff;
-  int C = -1;
-  if (valid > m) C = wave_threshold(key, idx, m, s_key[w], s_idx[w], ks, is);
-  int pos = 0;
-  if (C >= 0) {  // the winners are among the C candidates left in LDS, in item order
-    for (int q = 0; q * 64 < C; ++q) {
-      const int j = q * 64 + lane;
-      const uint32_t kv = j < C ? s_key[w][j] : 0u;
-      const int32_t iv = j < C ? s_idx[w][j] : 0;
-      const bool pr = taken(kv, iv, ks, is);
-      const uint64_t mk = ballot(pr);
-      if (pr) put(pos + rank_below(mk), kv, iv);
-      pos += popc64(mk);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < V; ++s) {  // slot-major order is ascending block order
-      const bool pr = taken(key[s], idx[s], ks, is);
-      const uint64_t mk = ballot(pr);
-      if (pr) put(pos + rank_below(mk), key[s], idx[s]);
-      pos += popc64(mk);
-    }
-  }
-  if (single) {
-    if (lane == 0) out[m] = local;
-  } else if (lane >= pos && lane < m) {  // a short last chunk leaves empty slots
-    ck[lane] = 0u;
-    ci[lane] = -1;
-  }
+  // Items per lane sized to this chunk's candidates (wave-uniform choice).
+  if (valid <= 512)
+    select_chunk<8>(a, pid, chunk, base, n_c, valid, nch == 1, local, s_key[w], s_idx[w]);
+  else if (valid <= 1024)
+    select_chunk<16>(a, pid, chunk, base, n_c, valid, nch == 1, local, s_key[w], s_idx[w]);
+  else
+    select_chunk<V>(a, pid, chunk, base, n_c, valid, nch == 1, local, s_key[w], s_idx[w]);
 }
 
 // Pass 2: merge the chunk winners of problems with more than one chunk. One wave each.
