@@ -269,7 +269,7 @@ def main():
     dwall, dkt = time_step(wd, inp, args.decode_steps, args.warmup, decode=True)
     d_bytes, d_index_bytes, _ = decode_work(wd)
     t_idx = dkt["index_topk"]
-    droof = dict(kernel="index_select_decode+topk_pass2", bound="hbm",
+    droof = dict(kernel="index_select_decode+topk_merge_wide", bound="hbm",
                  achieved=d_index_bytes / t_idx / 1e9, peak=PEAK_HBM_BYTES / 1e9,
                  unit="GB/s", frac=d_index_bytes / t_idx / PEAK_HBM_BYTES,
                  traffic=measured_traffic("index_select_decode", wd.name),
