@@ -62,7 +62,7 @@ struct KvArgs {          // KV-outer prefill attention
   void *part_o;          // [B*R*n_q*top_k][G][DH] unnormalised partial outputs (dtype)
   float *part_ml;        // [B*R*n_q*top_k][G][2] (max in log2 units, sum)
   int batch, n_q, n_k, q_start, h_q, h_kv, block_size, top_k, cap, n_blocks;
-  int seg_rows;          // lists are keyed (row segment, b, r, block), segment-major
+  int seg_rows;          // lists are keyed (r, row segment, b, block), group-major
   int n_seg;
   float scale_log2;
 };
