@@ -18,6 +18,7 @@ namespace msa {
 namespace {
 
 constexpr int KT = 64;        // keys per key tile: four 16-row MFMA tiles
+constexpr int SEL_WAVES = 8;  // waves of a decode index-select workgroup
 constexpr int WG_COLS = 256;  // (group, query) columns per prefill workgroup: 4 waves x 64
 
 template <typename E, int DI>
@@ -251,26 +252,26 @@ __global__ __launch_bounds__(256) void index_pool_decode(IndexArgs a) {
 }
 
 // Decode with the first selection stage fused in. Grid: x = range of SEL_NBLK key blocks,
-// z = sequence; 512 threads. Each wave pools 32 blocks for all groups into LDS; then one
-// wave per group ranks the range's blocks before the local block and writes its best
-// top_k - 1 (key, block) pairs; a final merge pass picks the overall best.
+// z = sequence; SEL_WAVES waves. Each wave pools its share of the blocks for all groups
+// into LDS; then one wave per group ranks the range's blocks before the local block and
+// writes its best top_k - 1 (key, block) pairs; a final merge pass picks the overall best.
 template <typename E, int DI, int BS>
-__global__ __launch_bounds__(512) void index_select_decode(IndexArgs a) {
+__global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs a) {
   using F = typename Frag<E>::type;
   constexpr int DC = DI / 32;
   constexpr int BPT = KT / BS;
   constexpr int MPB = BS / 16;
-  constexpr int NBW = SEL_NBLK / 8;  // blocks per wave
+  constexpr int NBW = SEL_NBLK / SEL_WAVES;  // blocks per wave
   __shared__ float s_m[16][SEL_NBLK];
-  __shared__ uint32_t s_key[8][SELECT_CAP + 1];
-  __shared__ int32_t s_idx[8][SELECT_CAP + 1];
+  __shared__ uint32_t s_key[SEL_WAVES][SELECT_CAP + 1];
+  __shared__ int32_t s_idx[SEL_WAVES][SELECT_CAP + 1];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int R = a.h_kv, b = blockIdx.z, wg = blockIdx.x;
   const long p = a.q_start;
   const int local = (int)(p / BS);
   const int c0 = wg * SEL_NBLK;
 
-  for (int x = tid; x < 16 * SEL_NBLK; x += 512) (&s_m[0][0])[x] = -INFINITY;
+  for (int x = tid; x < 16 * SEL_NBLK; x += SEL_WAVES * 64) (&s_m[0][0])[x] = -INFINITY;
   __syncthreads();
 
   const E *qi = reinterpret_cast<const E *>(a.q_idx);
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(512) void index_select_decode(IndexArgs a) {
   const int m = a.top_k - 1;
   const int nv = max(0, min(SEL_NBLK, local - c0));  // candidates: blocks c0.. before `local`
   const int n_wg = gridDim.x;
-  for (int r = w; r < R; r += 8) {  // one wave per group
+  for (int r = w; r < R; r += SEL_WAVES) {  // one wave per group
     if (m == 0) break;
     uint32_t key[4];
     int32_t idx[4];
@@ -367,7 +368,7 @@ template <typename E, int DI, int BS>
 hipError_t launch_select_t(const IndexArgs &a, hipStream_t s) {
   const long blocks = a.q_start / BS + 1;  // blocks 0 .. local
   dim3 grid((unsigned)((blocks + SEL_NBLK - 1) / SEL_NBLK), 1, (unsigned)a.batch);
-  hipLaunchKernelGGL((index_select_decode<E, DI, BS>), grid, dim3(512), 0, s, a);
+  hipLaunchKernelGGL((index_select_decode<E, DI, BS>), grid, dim3(SEL_WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -675,7 +675,7 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
   }
   if (!(stages & KV_STAGE_MERGE)) return hipGetLastError();
   const long threads = (long)a.batch * a.h_kv * a.n_q * ((long)DH << log2g) / 8;
-  hipLaunchKernelGGL((kv_merge<E, DH, 16>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL((kv_merge<E, DH, 32>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                      a, log2g);
   return hipGetLastError();
 }
