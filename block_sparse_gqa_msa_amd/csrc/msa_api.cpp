@@ -40,8 +40,8 @@ int cap_of(const msa_shape &s) { return s.kv_capacity ? s.kv_capacity : s.n_k; }
 // Checks shared by every entry point.
 int check_shape(const msa_shape *s) {
   if (!s) return fail(MSA_ERR_INVALID_ARG, "shape is NULL");
-  if (s->batch < 1 || s->n_q < 1 || s->n_k < 1 || s->q_start < 0)
-    return fail(MSA_ERR_INVALID_ARG, "batch, n_q, n_k must be >= 1 and q_start >= 0 (got %d, %d, %d, %d)",
+  if (s->batch < 0 || s->n_q < 0 || s->n_k < 0 || s->q_start < 0)
+    return fail(MSA_ERR_INVALID_ARG, "batch, n_q, n_k and q_start must be >= 0 (got %d, %d, %d, %d)",
                 s->batch, s->n_q, s->n_k, s->q_start);
   if ((long long)s->q_start + s->n_q > s->n_k)
     return fail(MSA_ERR_INVALID_ARG, "q_start + n_q (%lld) exceeds n_k (%d)",
@@ -62,6 +62,9 @@ int check_shape(const msa_shape *s) {
     return fail(MSA_ERR_UNSUPPORTED, "h_q / h_kv = %d not in {1,2,4,8,16}", s->h_q / s->h_kv);
   return MSA_OK;
 }
+
+// No rows to compute (batch or n_q is 0): every call is a no-op that succeeds.
+bool empty(const msa_shape &s) { return s.batch == 0 || s.n_q == 0; }
 
 int topk_chunks(const msa_shape &s) {
   if (s.top_k == 1) return 1;  // the local block alone: no ranking
@@ -177,6 +180,10 @@ int msa_index_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
   if (rc) return rc;
   if ((rc = check_index_dims(*shape))) return rc;
   if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (empty(*shape)) {
+    *bytes = 0;
+    return ok();
+  }
   IndexWs w;
   if ((rc = index_ws(*shape, true, &w))) return rc;
   *bytes = w.total;
@@ -215,6 +222,7 @@ int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx,
   if (rc) return rc;
   const msa_shape &s = *shape;
   if ((rc = check_index_dims(s))) return rc;
+  if (empty(s)) return ok();
   if (!q_idx || !k_idx || !sel) return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx and sel must be non-NULL");
   IndexWs w;
   if ((rc = index_ws(s, block_scores == nullptr, &w))) return rc;
@@ -253,6 +261,7 @@ int msa_index_block_scores(const msa_shape *shape, const void *q_idx, const void
   if (rc) return rc;
   const msa_shape &s = *shape;
   if ((rc = check_index_dims(s))) return rc;
+  if (empty(s)) return ok();
   if (!q_idx || !k_idx || !block_scores)
     return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx and block_scores must be non-NULL");
   if ((rc = launch_scores(s, q_idx, k_idx, block_scores, reinterpret_cast<hipStream_t>(stream))))
@@ -264,6 +273,10 @@ int msa_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (empty(*shape)) {
+    *bytes = 0;
+    return ok();
+  }
   IndexWs w;
   if ((rc = index_ws(*shape, false, &w))) return rc;
   *bytes = w.total;
@@ -275,6 +288,7 @@ int msa_topk_from_block_scores(const msa_shape *shape, const float *block_scores
   int rc = check_shape(shape);
   if (rc) return rc;
   const msa_shape &s = *shape;
+  if (empty(s)) return ok();
   if (!block_scores || !sel) return fail(MSA_ERR_INVALID_ARG, "block_scores and sel must be non-NULL");
   IndexWs w;
   if ((rc = index_ws(s, false, &w))) return rc;
@@ -292,6 +306,10 @@ int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes) {
   if (rc) return rc;
   if ((rc = check_attn_dims(*shape))) return rc;
   if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (empty(*shape)) {
+    *bytes = 0;
+    return ok();
+  }
   if ((rc = check_prefill_limits(*shape))) return rc;
   *bytes = attn_prefill_ws(*shape, nullptr);
   if (is_decode(*shape)) {  // either entry point may be called for a decode shape
@@ -299,6 +317,12 @@ int msa_sparse_attn_workspace_size(const msa_shape *shape, size_t *bytes) {
     if (d > *bytes) *bytes = d;
   }
   return ok();
+}
+
+// An attention call with no rows: the dimensions must still be supported; nothing runs.
+static int empty_attn_call(const msa_shape &s) {
+  const int rc = check_attn_dims(s);
+  return rc ? rc : ok();
 }
 
 // Validates a prefill-attention call and fills the kernel arguments over the caller's
@@ -343,6 +367,7 @@ int msa_sparse_attn_prefill(const msa_shape *shape, const void *q, const void *k
   msa::KvArgs a;
   int rc = check_shape(shape);
   if (rc) return rc;
+  if (empty(*shape)) return empty_attn_call(*shape);
   if (!q || !k || !v || !sel || !o) return fail(MSA_ERR_INVALID_ARG, "q, k, v, sel and o must be non-NULL");
   if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
   a.q = q; a.k = k; a.v = v; a.sel = sel; a.o = o; a.lse = lse;
@@ -354,6 +379,7 @@ int msa_sparse_attn_prefill_plan(const msa_shape *shape, const int32_t *sel, voi
   msa::KvArgs a;
   int rc = check_shape(shape);
   if (rc) return rc;
+  if (empty(*shape)) return empty_attn_call(*shape);
   if (!sel) return fail(MSA_ERR_INVALID_ARG, "sel must be non-NULL");
   if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
   a.sel = sel;
@@ -366,6 +392,7 @@ int msa_sparse_attn_prefill_partials(const msa_shape *shape, const void *q, cons
   msa::KvArgs a;
   int rc = check_shape(shape);
   if (rc) return rc;
+  if (empty(*shape)) return empty_attn_call(*shape);
   if (!q || !k || !v) return fail(MSA_ERR_INVALID_ARG, "q, k and v must be non-NULL");
   if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
   a.q = q; a.k = k; a.v = v;
@@ -377,6 +404,7 @@ int msa_sparse_attn_prefill_merge(const msa_shape *shape, const int32_t *sel, vo
   msa::KvArgs a;
   int rc = check_shape(shape);
   if (rc) return rc;
+  if (empty(*shape)) return empty_attn_call(*shape);
   if (!sel || !o) return fail(MSA_ERR_INVALID_ARG, "sel and o must be non-NULL");
   if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
   a.sel = sel; a.o = o; a.lse = lse;
@@ -393,6 +421,7 @@ int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_
   if (s.n_q != 1 || s.q_start != s.n_k - 1)
     return fail(MSA_ERR_INVALID_ARG, "decode needs n_q == 1 and q_start == n_k - 1 (got %d, %d, n_k %d)",
                 s.n_q, s.q_start, s.n_k);
+  if (empty(s)) return ok();
   if (!q || !k_cache || !v_cache || !sel || !o)
     return fail(MSA_ERR_INVALID_ARG, "q, k_cache, v_cache, sel and o must be non-NULL");
   const size_t need = attn_decode_ws(s);

@@ -29,6 +29,9 @@
  *   - Errors: a call validates everything it can on the host first; on any
  *     error it returns a negative code, enqueues nothing and sets the text
  *     returned by msa_last_error(). Launch failures return MSA_ERR_HIP.
+ *   - Empty calls: with batch == 0 or n_q == 0 there is nothing to compute. Such a
+ *     call still checks the shape and the supported set, then returns MSA_OK
+ *     without touching any pointer or enqueueing anything; workspace sizes are 0.
  *
  * Supported set: dtype F32 or BF16; d_h in {64, 128}; d_idx in {32, 64};
  * block_size in {32, 64}; 1 <= top_k <= 64; h_kv and h_q / h_kv in
@@ -56,9 +59,9 @@ enum {
 };
 
 typedef struct {
-  int32_t batch;       /* sequences, >= 1 */
-  int32_t n_q;         /* query rows per sequence, >= 1 */
-  int32_t n_k;         /* valid keys per sequence; q_start + n_q <= n_k */
+  int32_t batch;       /* sequences, >= 0 (0: empty call) */
+  int32_t n_q;         /* query rows per sequence, >= 0 (0: empty call) */
+  int32_t n_k;         /* valid keys per sequence, >= 0; q_start + n_q <= n_k */
   int32_t q_start;     /* absolute position of row 0, >= 0 */
   int32_t h_q;         /* query heads */
   int32_t h_kv;        /* KV heads = GQA groups = index heads */

@@ -65,8 +65,8 @@ def test_workspace_sizes(lib):
 
 
 BAD = [
-    (dict(batch=0), msa.MSA_ERR_INVALID_ARG),
-    (dict(n_q=0), msa.MSA_ERR_INVALID_ARG),
+    (dict(batch=-1), msa.MSA_ERR_INVALID_ARG),
+    (dict(n_q=-1), msa.MSA_ERR_INVALID_ARG),
     (dict(q_start=-1), msa.MSA_ERR_INVALID_ARG),
     (dict(n_q=100, n_k=120, q_start=30), msa.MSA_ERR_INVALID_ARG),   # q_start + n_q > n_k
     (dict(h_q=30), msa.MSA_ERR_INVALID_ARG),                        # not a multiple of h_kv
@@ -172,3 +172,32 @@ def test_missing_library_raises(tmp_path):
             msa.load_library(str(tmp_path / "nope.so"))
         finally:
             msa._lib = msa._lib_saved
+
+
+def test_empty_calls_are_noops(lib):
+    """batch == 0 or n_q == 0: every entry point validates the shape, touches no pointer,
+    enqueues nothing (no GPU needed) and returns MSA_OK; workspace sizes are 0."""
+    for kw in (dict(batch=0), dict(n_q=0), dict(n_q=0, n_k=0), dict(n_q=0, q_start=128)):
+        s = good(**kw)
+        assert msa.msa_index_topk_workspace_size(s) == 0
+        assert msa.msa_topk_workspace_size(s) == 0
+        assert msa.msa_sparse_attn_workspace_size(s) == 0
+        sb = ctypes.byref(s)
+        assert lib.msa_index_topk(sb, None, None, None, None, None, 0, None) == msa.MSA_OK
+        assert lib.msa_index_block_scores(sb, None, None, None, None) == msa.MSA_OK
+        assert lib.msa_topk_from_block_scores(sb, None, None, None, 0, None) == msa.MSA_OK
+        assert lib.msa_sparse_attn_prefill(sb, None, None, None, None, None, None, None, 0,
+                                           None) == msa.MSA_OK
+        assert lib.msa_sparse_attn_prefill_plan(sb, None, None, 0, None) == msa.MSA_OK
+        assert lib.msa_sparse_attn_prefill_partials(sb, None, None, None, None, 0, None) == msa.MSA_OK
+        assert lib.msa_sparse_attn_prefill_merge(sb, None, None, None, None, 0, None) == msa.MSA_OK
+    d = good(batch=0, n_q=1, n_k=5000, q_start=4999)
+    assert lib.msa_sparse_attn_decode(ctypes.byref(d), None, None, None, None, None, None, None, 0,
+                                      None) == msa.MSA_OK
+    # the supported set is still checked
+    s = good(n_q=0, d_h=96)
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(s), None, None, None, None, None, None, None, 0,
+                                       None) == msa.MSA_ERR_UNSUPPORTED
+    s = good(batch=0, d_idx=48)
+    assert lib.msa_index_topk(ctypes.byref(s), None, None, None, None, None, 0, None) \
+        == msa.MSA_ERR_UNSUPPORTED

@@ -47,6 +47,10 @@ SMALL = [
       top_k=4, idx_range=3, qkv_scale=1.0),
     W("prefill_two_level_topk", n_q=64, n_k=70064, q_start=70000, block_size=32, d_idx=32,
       top_k=32, needles=16),
+    W("batch3_unaligned_chunk", batch=3, n_q=333, n_k=2000, q_start=1667, h_q=16, h_kv=2,
+      d_h=128, d_idx=64, block_size=64, top_k=7, needles=5),
+    W("bf16_d64_bs64_g8", n_q=1500, n_k=1500, h_q=32, h_kv=4, d_h=64, d_idx=32, block_size=64,
+      top_k=10, needles=4),
     # more than 32768 key blocks: the list build falls back to per-entry counters
     W("prefill_many_blocks", n_q=40, n_k=(1 << 20) + 96, q_start=(1 << 20) + 56, h_q=8,
       h_kv=2, d_h=64, d_idx=32, block_size=32, top_k=16, needles=8),
@@ -97,6 +101,10 @@ DECODE_SMALL = [
     W("decode_k1", batch=2, n_q=1, n_k=3000, q_start=2999, top_k=1),
     W("decode_ties", batch=2, n_q=1, n_k=70000, q_start=69999, d_idx=32, top_k=32,
       idx_range=0),  # all index scores equal: lowest blocks win every tie
+    W("decode_g1_r8", batch=2, n_q=1, n_k=9000, q_start=8999, h_q=8, h_kv=8, d_h=64,
+      top_k=12, needles=4),
+    W("decode_g16_r1_f32", dtype="f32", batch=2, n_q=1, n_k=4100, q_start=4099, h_q=16, h_kv=1,
+      d_h=128, d_idx=64, block_size=64, top_k=9, idx_range=3, qkv_scale=1.0),
 ]
 
 
@@ -245,3 +253,15 @@ def test_staged_prefill_calls_equal_single_call():
         torch.cuda.synchronize()
         assert torch.equal(o, one.o), w.name
         assert torch.equal(lse, one.lse), w.name
+
+
+def test_empty_step_is_noop():
+    """batch == 0 and n_q == 0 shapes go through the whole step on the GPU as no-ops."""
+    for w in (W("empty_batch", batch=0), W("empty_rows", n_q=0, n_k=512, q_start=512),
+              W("empty_decode", batch=0, n_q=1, n_k=4096, q_start=4095)):
+        s = msa.shape_of(w)
+        buf = msa.Buffers(s)
+        inp = generate(w, device="cuda")
+        msa.msa_step(buf, inp)
+        torch.cuda.synchronize()
+        assert buf.sel.numel() == 0 and buf.o.numel() == 0, w.name
