@@ -240,6 +240,40 @@ def pin_bf16_storage_widening(orc):
         assert np.array_equal(a[key], b[key]), key
 
 
+def pin_general_sparse(orc):
+    """General sparse selections (neither dense, local-only nor token-level): the selection
+    satisfies the threshold property against exact integer block maxima (every selected
+    earlier block beats every unselected visible one under (score desc, block asc), the
+    local block is in, the count is min(k, local+1), ascending), and the attention output
+    equals torch's fp64 SDPA under the token mask of that selection."""
+    for kw in (dict(batch=2, h_q=8, h_kv=2, n_q=70, n_k=70, d_h=8, d_idx=4, block_size=4,
+                    top_k=5),
+               dict(batch=1, h_q=6, h_kv=3, n_q=33, n_k=101, q_start=68, d_h=5, d_idx=3,
+                    block_size=8, top_k=4)):
+        w = shape(**kw)
+        inp = rand_inputs(w, seed=21, idx_values=(-3, 4))
+        out = orc.run(w, inp)
+        m = exact_block_max(w, inp)
+        sel = out["sel"]
+        for b, r, t in itertools.product(range(w.batch), range(w.h_kv), range(w.n_q)):
+            local = (w.q_start + t) // w.block_size
+            row = sel[b, r, t]
+            chosen = [int(c) for c in row if c >= 0]
+            assert len(chosen) == min(w.top_k, local + 1)
+            assert chosen == sorted(set(chosen)) and local in chosen
+            assert list(row[len(chosen):]) == [-1] * (w.top_k - len(chosen))
+            picked = [c for c in chosen if c != local]
+            others = [c for c in range(local) if c not in chosen]
+            for c in picked:
+                for c2 in others:
+                    mc, mc2 = m[b, r, t, c], m[b, r, t, c2]
+                    assert mc > mc2 or (mc == mc2 and c < c2), (b, r, t, c, c2)
+        o, lse = sdpa_reference(w, inp, visible_token_mask(w, sel))
+        assert np.allclose(out["o"], o, rtol=0, atol=1e-12)
+        assert np.allclose(out["lse"], lse, rtol=0, atol=1e-12)
+
+
 PINS = [pin_block_scores_exact, pin_topk_bruteforce, pin_dense_when_k_covers,
         pin_local_block_only, pin_token_level, pin_zero_query_closed_form,
-        pin_group_map_and_ones, pin_entry_point_consistency, pin_bf16_storage_widening]
+        pin_group_map_and_ones, pin_entry_point_consistency, pin_bf16_storage_widening,
+        pin_general_sparse]
