@@ -45,7 +45,7 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 // is staged once in LDS (double-buffered) and feeds every group: the index key is shared.
 // Pooled maxima are collected in LDS for OUT_RUN consecutive blocks and written as
 // contiguous runs of each output row.
-constexpr int OUT_RUN = 16;
+constexpr int OUT_RUN = 32;
 
 template <typename E, int DI, int BS>
 __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
@@ -105,10 +105,11 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
     }
   };
   // Write s_out's first n blocks of every column to block columns [c0, c0 + n) of the rows:
-  // four threads per column, 16 columns per wave per pass.
+  // OUT_RUN / 4 threads per column, four blocks each.
   auto flush = [&](long c0, int n) {
-    const int j0 = (tid & 3) * 4;
-    for (int col = tid >> 2; col < WG_COLS; col += 64) {
+    constexpr int TPC = OUT_RUN / 4;
+    const int j0 = (tid % TPC) * 4;
+    for (int col = tid / TPC; col < WG_COLS; col += 256 / TPC) {
       const int r = col / TQ, t = t0 + col % TQ;
       if (t >= a.n_q) continue;
       const long base = (((long)b * R + r) * a.n_q + t) * (long)a.n_blocks + c0;
@@ -263,8 +264,8 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
   constexpr int MPB = BS / 16;
   constexpr int NBW = SEL_NBLK / SEL_WAVES;  // blocks per wave
   __shared__ float s_m[16][SEL_NBLK];
-  __shared__ uint32_t s_key[SEL_WAVES][SELECT_CAP + 1];
-  __shared__ int32_t s_idx[SEL_WAVES][SELECT_CAP + 1];
+  __shared__ uint32_t s_key[SEL_WAVES][SELECT_LDS];
+  __shared__ int32_t s_idx[SEL_WAVES][SELECT_LDS];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int R = a.h_kv, b = blockIdx.z, wg = blockIdx.x;
   const long p = a.q_start;

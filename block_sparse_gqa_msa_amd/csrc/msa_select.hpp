@@ -17,11 +17,13 @@
 namespace msa {
 
 constexpr int SELECT_CAP = 256;  // candidates ranked in LDS (4 per lane)
+constexpr int SELECT_LDS = SELECT_CAP + 64;  // entries of a wave's lk / li: CAP + a spare per lane
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Exact m-th item (1 <= m <= 63) of the wave's items under (key desc, idx asc); at least m
-// slots are non-empty. lk / li: wave-private LDS of SELECT_CAP + 1 entries. On return, an
+// slots are non-empty. lk / li: wave-private LDS of SELECT_LDS entries (the last 64 are
+// write-only spares, one per lane). On return, an
 // item is among the best m iff key > kstar || (key == kstar && idx <= istar).
 // Returns C >= m when the items with key >= a lower bound T (C of them, in item order:
 // slot-major, then lane) are left in lk / li, or -1 when heavy ties sent it to the
@@ -41,17 +43,18 @@ __device__ int wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V],
     if (popc64(ballot(lm >= c)) >= m) T = c;
   }
   T = max(T, 1u);
-  // Compact the items >= T into LDS in item order (positions past CAP are dropped).
+  // Compact the items >= T into LDS in item order. Every lane writes every step (no branch):
+  // items below T, and positions past CAP, go to the lane's own spare slot.
   int C = 0;
+  const int spare = CAP + lane_id();
 #pragma unroll
   for (int s = 0; s < V; ++s) {
     const bool pr = key[s] >= T;
     const uint64_t mk = ballot(pr);
-    const int pos = C + rank_below(mk);
-    if (pr && pos < CAP) {
-      lk[pos] = key[s];
-      li[pos] = idx[s];
-    }
+    const int at = C + rank_below(mk);
+    const int pos = (pr && at < CAP) ? at : spare;
+    lk[pos] = key[s];
+    li[pos] = idx[s];
     C += popc64(mk);
   }
   if (C <= CAP) {

@@ -89,8 +89,8 @@ __device__ __forceinline__ void select_chunk(const TopkArgs &a, long pid, int ch
 
 // Pass 1. Grid: x = groups of 4 problems (one wave each), y = chunk.
 __global__ __launch_bounds__(256) void topk_pass1(TopkArgs a) {
-  __shared__ uint32_t s_key[4][CAP + 1];
-  __shared__ int32_t s_idx[4][CAP + 1];
+  __shared__ uint32_t s_key[4][SELECT_LDS];
+  __shared__ int32_t s_idx[4][SELECT_LDS];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long n_prob = (long)a.batch * a.h_kv * a.n_q;
   const long pid = (long)blockIdx.x * 4 + w;
@@ -125,8 +125,8 @@ __global__ __launch_bounds__(256) void topk_pass1(TopkArgs a) {
 
 // Pass 2: merge the chunk winners of problems with more than one chunk. One wave each.
 __global__ __launch_bounds__(256) void topk_pass2(TopkArgs a) {
-  __shared__ uint32_t s_key[4][CAP + 1];
-  __shared__ int32_t s_idx[4][CAP + 1];
+  __shared__ uint32_t s_key[4][SELECT_LDS];
+  __shared__ int32_t s_idx[4][SELECT_LDS];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long n_prob = (long)a.batch * a.h_kv * a.n_q;
   const long pid = (long)blockIdx.x * 4 + w;
@@ -194,8 +194,8 @@ constexpr int MW = 8;            // waves per problem
 constexpr int MV = TOPK_CHUNK / (64 * MW);  // candidates per lane in the first stage
 
 __global__ __launch_bounds__(MW * 64) void topk_merge_wide(TopkArgs a) {
-  __shared__ uint32_t s_key[MW][CAP + 1];
-  __shared__ int32_t s_idx[MW][CAP + 1];
+  __shared__ uint32_t s_key[MW][SELECT_LDS];
+  __shared__ int32_t s_idx[MW][SELECT_LDS];
   __shared__ uint32_t w_key[MW * 64];  // per-wave winners, padded with key 0
   __shared__ int32_t w_idx[MW * 64];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
