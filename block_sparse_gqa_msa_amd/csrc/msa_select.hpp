@@ -7,8 +7,9 @@
 //   1. a ballot-counted bitwise search over the 64 lane maxima (a lower bound on the
 //      threshold that at least m items reach),
 //   2. compacting the items at or above that bound (normally a few dozen) into LDS and
-//      finding the exact m-th among them by a second bitwise search (keys, then indices
-//      for ties at the threshold),
+//      finding the exact m-th among them: by ranking every candidate against the others
+//      when there are at most 64, else by a second bitwise search (keys, then indices for
+//      ties at the threshold),
 //   3. an exact bitwise search over all items when ties make that set too large.
 #pragma once
 
@@ -22,7 +23,7 @@ constexpr int SELECT_LDS = SELECT_CAP + 64;  // entries of a wave's lk / li: CAP
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Exact m-th item (1 <= m <= 63) of the wave's items under (key desc, idx asc); at least m
-// slots are non-empty. lk / li: wave-private LDS of SELECT_LDS entries (the last 64 are
+// slots are non-empty and the non-empty items have distinct indices. lk / li: wave-private LDS of SELECT_LDS entries (the last 64 are
 // write-only spares, one per lane). On return, an
 // item is among the best m iff key > kstar || (key == kstar && idx <= istar).
 // Returns C >= m when the items with key >= a lower bound T (C of them, in item order:
@@ -57,16 +58,42 @@ __device__ int wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V],
     li[pos] = idx[s];
     C += popc64(mk);
   }
+  if (C <= 64) {
+    // Few candidates (the usual case): rank each one against all of them. Indices are
+    // distinct, so (key desc, idx asc) orders the candidates totally, their ranks are
+    // 0 .. C-1, and the candidate of rank m-1 is the m-th item.
+    if (lane_id() < 4) lk[C + lane_id()] = 0u;  // padding for the 4-wide loop: ranks last
+    lds_wait();
+    const bool mine = lane_id() < C;
+    const uint32_t k0 = mine ? lk[lane_id()] : 0u;
+    const int32_t i0 = mine ? li[lane_id()] : 0;
+    const uint64_t c0 = ((uint64_t)k0 << 32) | (0x7fffffffu - (uint32_t)i0);
+    int rank = 0;
+    for (int j = 0; j < C; j += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t cj = ((uint64_t)lk[j + u] << 32) | (0x7fffffffu - (uint32_t)li[j + u]);
+        rank += cj > c0 ? 1 : 0;
+      }
+    }
+    const uint64_t hit = ballot(mine && rank == m - 1);
+    if (hit) {  // always, for distinct indices
+      const int src = __builtin_ctzll(hit);
+      kstar = (uint32_t)__builtin_amdgcn_readlane((int)k0, src);
+      istar = __builtin_amdgcn_readlane(i0, src);
+      return C;
+    }
+  }
   if (C <= CAP) {
     lds_wait();
-    const int nq = (C + 63) >> 6;  // wave-uniform
+    // Empty slots hold key 0, which no search step below counts (every probe is >= 1).
     uint32_t ck[Q];
     int32_t ci[Q];
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const int j = lane_id() + 64 * q;
-      ck[q] = (q < nq && j < C) ? lk[j] : 0u;
-      ci[q] = (q < nq && j < C) ? li[j] : 0x7fffffff;
+      ck[q] = j < C ? lk[j] : 0u;
+      ci[q] = j < C ? li[j] : 0x7fffffff;
     }
     // The m-th largest candidate key K, by a ballot-counted bitwise search.
     uint32_t K = 0;
@@ -74,17 +101,15 @@ __device__ int wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V],
       const uint32_t c = K | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int q = 0; q < Q; ++q)
-        if (q < nq) cnt += popc64(ballot(ck[q] >= c));
+      for (int q = 0; q < Q; ++q) cnt += popc64(ballot(ck[q] >= c));
       if (cnt >= m) K = c;
     }
     int ngt = 0, neq = 0;
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
-      if (q < nq) {
-        ngt += popc64(ballot(ck[q] > K));
-        neq += popc64(ballot(ck[q] == K));
-      }
+    for (int q = 0; q < Q; ++q) {
+      ngt += popc64(ballot(ck[q] > K));
+      neq += popc64(ballot(ck[q] == K));
+    }
     const int need = m - ngt;  // 1 <= need <= neq
     int32_t X = 0x7fffffff;    // all items with key K are taken ...
     if (neq > need) {          // ... unless ties at K: then the `need` lowest indices
@@ -93,8 +118,7 @@ __device__ int wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V],
         const int32_t c = X | (1 << bit);
         int cnt = 0;
 #pragma unroll
-        for (int q = 0; q < Q; ++q)
-          if (q < nq) cnt += popc64(ballot(ck[q] == K && ci[q] < c));
+        for (int q = 0; q < Q; ++q) cnt += popc64(ballot(ck[q] == K && ci[q] < c));
         if (cnt < need) X = c;
       }
     }

@@ -51,6 +51,10 @@ SMALL = [
       d_h=128, d_idx=64, block_size=64, top_k=7, needles=5),
     W("bf16_d64_bs64_g8", n_q=1500, n_k=1500, h_q=32, h_kv=4, d_h=64, d_idx=32, block_size=64,
       top_k=10, needles=4),
+    # k = 48 over ~257 blocks: about 80 candidates reach the first bound, more than one
+    # per lane, so the exact m-th comes from the second bitwise search, not the ranking
+    W("k48_mid_candidates", n_q=64, n_k=16448, q_start=16384, h_q=8, h_kv=2, d_h=64,
+      d_idx=32, block_size=64, top_k=48, needles=8),
     # more than 32768 key blocks: the list build falls back to per-entry counters
     W("prefill_many_blocks", n_q=40, n_k=(1 << 20) + 96, q_start=(1 << 20) + 56, h_q=8,
       h_kv=2, d_h=64, d_idx=32, block_size=32, top_k=16, needles=8),
@@ -105,6 +109,8 @@ DECODE_SMALL = [
       top_k=12, needles=4),
     W("decode_g16_r1_f32", dtype="f32", batch=2, n_q=1, n_k=4100, q_start=4099, h_q=16, h_kv=1,
       d_h=128, d_idx=64, block_size=64, top_k=9, idx_range=3, qkv_scale=1.0),
+    W("decode_k48", batch=2, n_q=1, n_k=40000, q_start=39999, block_size=64, top_k=48,
+      needles=6),  # more candidates than lanes at the first bound: second bitwise search
 ]
 
 
