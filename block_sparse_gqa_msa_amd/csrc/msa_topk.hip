@@ -196,7 +196,7 @@ constexpr int MV = TOPK_CHUNK / (64 * MW);  // candidates per lane in the first 
 __global__ __launch_bounds__(MW * 64) void topk_merge_wide(TopkArgs a) {
   __shared__ uint32_t s_key[MW][SELECT_LDS];
   __shared__ int32_t s_idx[MW][SELECT_LDS];
-  __shared__ uint32_t w_key[MW * 64];  // per-wave winners, padded with key 0
+  __shared__ uint32_t w_key[MW * 64];  // per-wave winners (MW * m used), padded with key 0
   __shared__ int32_t w_idx[MW * 64];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long pid = blockIdx.x;
@@ -244,35 +244,39 @@ __global__ __launch_bounds__(MW * 64) void topk_merge_wide(TopkArgs a) {
   uint32_t ks = 0;
   int32_t is = 0x7fffffff;
   if (nv > m) wave_threshold(key, idx, m, s_key[w], s_idx[w], ks, is);
+  // Wave w's winners (at most m) go to entries [w * m, (w + 1) * m), padded with key 0.
   int pos = 0;
 #pragma unroll
   for (int s = 0; s < MV; ++s) {
     const bool pr = taken(key[s], idx[s], ks, is);
     const uint64_t mk = ballot(pr);
     if (pr) {
-      w_key[w * 64 + pos + rank_below(mk)] = key[s];
-      w_idx[w * 64 + pos + rank_below(mk)] = idx[s];
+      w_key[w * m + pos + rank_below(mk)] = key[s];
+      w_idx[w * m + pos + rank_below(mk)] = idx[s];
     }
     pos += popc64(mk);
   }
-  if (lane >= pos) {
-    w_key[w * 64 + lane] = 0u;
-    w_idx[w * 64 + lane] = 0x7fffffff;
+  if (lane >= pos && lane < m) {
+    w_key[w * m + lane] = 0u;
+    w_idx[w * m + lane] = 0x7fffffff;
   }
   __syncthreads();
   if (w != 0) return;
-  // Stage 2: the best m of the waves' winners.
+  // Stage 2: the best m of the MW * m entries, entry j in lane j % 64. Packed this way the
+  // winners spread over all lanes, which keeps the lane-maximum bound of the selection
+  // tight (a wave-per-slot layout leaves them on m lanes, and the bound admits nearly all).
   uint32_t k2[MW];
   int32_t i2[MW];
 #pragma unroll
   for (int s = 0; s < MW; ++s) {
-    k2[s] = w_key[s * 64 + lane];
-    i2[s] = w_idx[s * 64 + lane];
+    const int j = s * 64 + lane;
+    k2[s] = j < MW * m ? w_key[j] : 0u;
+    i2[s] = j < MW * m ? w_idx[j] : 0x7fffffff;
   }
   wave_threshold(k2, i2, m, s_key[0], s_idx[0], ks, is);
   // Candidates arrive in ascending block order (key range after key range), each wave keeps
   // its winners in that order and the waves cover consecutive shares: compacting the
-  // winners in item order gives ascending blocks.
+  // winners in entry order gives ascending blocks.
   pos = 0;
 #pragma unroll
   for (int s = 0; s < MW; ++s) {
