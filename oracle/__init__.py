@@ -38,6 +38,9 @@ class Oracle:
         i, p = ctypes.c_int, ctypes.c_void_p
         f.argtypes = [i] * 10 + [i, p, p, p, p, p, i, p, p, p, p, p, i]
         f.restype = i
+        g = self.lib.msa_oracle_kl
+        g.argtypes = [i] * 11 + [p, p, p, p, i, p, p, p, p, i]
+        g.restype = i
         self.lib.msa_oracle_max_threads.restype = i
 
     def max_threads(self) -> int:
@@ -87,6 +90,32 @@ class Oracle:
         if attention:
             out["o"], out["lse"] = o, lse
         return out
+
+
+    def kl(self, w, inputs: Dict, sel: np.ndarray, rows: Optional[Sequence[int]] = None,
+           n_threads: int = 0) -> Dict[str, np.ndarray]:
+        """The index-branch alignment loss L_KL and the student's normaliser lse_idx,
+        [B, R, n] float64, for the listed rows (default: all) given their selections
+        ``sel`` [B, R, n, k] (as ``run`` returns them for the same rows)."""
+        rows_arr = np.arange(w.n_q, dtype=np.int32) if rows is None else np.asarray(rows, np.int32)
+        rows_arr = np.ascontiguousarray(rows_arr)
+        n = len(rows_arr)
+        B, R, H, k = w.batch, w.h_kv, w.h_q, w.top_k
+        typ = 0 if w.dtype == "f32" else 1
+        arrs = {name: _as_numpy(inputs[name], typ) for name in ("q_idx", "k_idx", "q", "k")}
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        if sel.shape != (B, R, n, k):
+            raise ValueError(f"sel has shape {sel.shape}, expected {(B, R, n, k)}")
+        kl = np.empty((B, R, n), np.float64)
+        lse = np.empty((B, R, n), np.float64)
+        rc = self.lib.msa_oracle_kl(
+            B, w.n_q, w.n_k, w.q_start, H, R, w.d_h, w.d_idx, w.block_size, k, typ,
+            arrs["q_idx"].ctypes.data, arrs["k_idx"].ctypes.data, arrs["q"].ctypes.data,
+            arrs["k"].ctypes.data, n, rows_arr.ctypes.data, sel.ctypes.data, kl.ctypes.data,
+            lse.ctypes.data, int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"msa_oracle_kl failed with code {rc}")
+        return dict(kl=kl, lse_idx=lse)
 
 
 def _as_numpy(x, typ: int) -> np.ndarray:

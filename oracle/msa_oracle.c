@@ -14,6 +14,9 @@
  *   - 主分支 (main branch): the softmax attention equation O^(h)_i over the
  *     selected blocks' visible tokens, all heads of a group sharing the group's
  *     selection.
+ * and, for msa_oracle_kl, section 训练 of the same page: the index branch's
+ * distribution P^idx and the group-averaged main-branch distribution P^(r) over
+ * the selected tokens, and the alignment loss L_KL = KL(P^(r) || P^idx).
  *
  * Readings where the page is silent (each is listed with its reason in the
  * design notes):
@@ -261,6 +264,136 @@ int msa_oracle_run(int batch, int n_q, int n_k, int q_start, int h_q, int h_kv, 
       if (lse) lse[out] = l;
     }
     free(z);
+  }
+  return failed ? -2 : 0;
+}
+
+/*
+ * Alignment loss for one (sequence, group r, query row) at position p, given the row's
+ * selection (section 训练: the equations for P^idx, P^(r) and L_KL):
+ *   T          = the selected blocks' visible tokens (the main branch's token set)
+ *   S^idx_j    = q_idx . k_idx_j / sqrt(d_idx)       P^idx = softmax over T of S^idx
+ *   S^(l)_j    = q_l . k_j / sqrt(d_h), l in group r P^(r) = (1/G) sum_l softmax_T(S^(l))
+ *   L_KL       = sum_{j in T} P^(r)_j (log P^(r)_j - log P^idx_j), natural log; a term
+ *                with P^(r)_j = 0 adds 0.
+ *   lse_idx    = log sum_{j in T} exp(S^idx_j), the normaliser of P^idx.
+ * q_row0: the group's first query row, head l at l * q_head_stride elements; k_plane: the
+ * group's keys. Scratch (top_k * block_size each): key, sidx, zh, t.
+ */
+static void kl_row(const void *q_idx_row, const void *k_idx_seq, const void *q_row0,
+                   int64_t q_head_stride, const void *k_plane, int type, int d_idx, int d_h,
+                   int group, int64_t p, int block_size, const int32_t *sel, int top_k,
+                   int64_t *key, double *sidx, double *zh, double *t, double *kl,
+                   double *lse_idx) {
+  const size_t es = (type == ORACLE_F32) ? 4 : 2;
+  /* the token set T and the index scores S^idx on it */
+  int64_t n = 0;
+  for (int i = 0; i < top_k; ++i) {
+    if (sel[i] < 0) continue;
+    int64_t lo = (int64_t)sel[i] * block_size, hi = lo + block_size;
+    if (hi > p + 1) hi = p + 1;
+    for (int64_t j = lo; j < hi; ++j) {
+      double s = 0.0;
+      for (int d = 0; d < d_idx; ++d)
+        s += elem(q_idx_row, d, type) * elem(k_idx_seq, j * d_idx + d, type);
+      key[n] = j;
+      sidx[n] = s / sqrt((double)d_idx);
+      ++n;
+    }
+  }
+  /* student: log P^idx_j = S^idx_j - lse_idx */
+  double mu = -INFINITY;
+  for (int64_t j = 0; j < n; ++j)
+    if (sidx[j] > mu) mu = sidx[j];
+  double zsum = 0.0;
+  for (int64_t j = 0; j < n; ++j) zsum += exp(sidx[j] - mu);
+  const double lse_s = mu + log(zsum);
+  /* teacher: P^(r)_j = mean over the group's heads l of softmax_T(S^(l))_j */
+  for (int64_t j = 0; j < n; ++j) t[j] = 0.0;
+  const double scale = 1.0 / sqrt((double)d_h);
+  for (int l = 0; l < group; ++l) {
+    const void *q_row = (const char *)q_row0 + (int64_t)l * q_head_stride * (int64_t)es;
+    double hm = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+      double s = 0.0;
+      for (int d = 0; d < d_h; ++d) s += elem(q_row, d, type) * elem(k_plane, key[j] * d_h + d, type);
+      zh[j] = s * scale;
+      if (zh[j] > hm) hm = zh[j];
+    }
+    double hs = 0.0;
+    for (int64_t j = 0; j < n; ++j) hs += exp(zh[j] - hm);
+    for (int64_t j = 0; j < n; ++j) t[j] += exp(zh[j] - hm) / hs / (double)group;
+  }
+  /* L_KL = sum_j P^(r)_j (log P^(r)_j - log P^idx_j) */
+  double loss = 0.0;
+  for (int64_t j = 0; j < n; ++j)
+    if (t[j] > 0.0) loss += t[j] * (log(t[j]) - (sidx[j] - lse_s));
+  *kl = loss;
+  *lse_idx = lse_s;
+}
+
+/*
+ * The alignment loss for a list of query rows, given their selections.
+ *   sel [B, H_kv, n_rows, top_k] (as msa_oracle_run writes it for the same rows)
+ *   kl, lse_idx [B, H_kv, n_rows] double (lse_idx may be NULL)
+ * Layouts of q_idx, k_idx, q, k as for msa_oracle_run. Returns 0, -1 on a bad argument,
+ * -2 when out of memory.
+ */
+int msa_oracle_kl(int batch, int n_q, int n_k, int q_start, int h_q, int h_kv, int d_h,
+                  int d_idx, int block_size, int top_k, int type, const void *q_idx,
+                  const void *k_idx, const void *q, const void *k, int n_rows,
+                  const int32_t *rows, const int32_t *sel, double *kl, double *lse_idx,
+                  int n_threads) {
+  if (batch < 1 || n_q < 1 || n_k < 1 || q_start < 0 || h_kv < 1 || h_q < h_kv ||
+      h_q % h_kv || d_idx < 1 || d_h < 1 || block_size < 1 || top_k < 1 || n_rows < 0 ||
+      !q_idx || !k_idx || !q || !k || !rows || !sel || !kl ||
+      (type != ORACLE_F32 && type != ORACLE_BF16))
+    return -1;
+  for (int i = 0; i < n_rows; ++i)
+    if (rows[i] < 0 || rows[i] >= n_q || (int64_t)q_start + rows[i] >= n_k) return -1;
+  const int group = h_q / h_kv;
+  const size_t es = (type == ORACLE_F32) ? 4 : 2;
+#ifdef _OPENMP
+  if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+  (void)n_threads;
+#endif
+  int failed = 0;
+  const int64_t n_tasks = (int64_t)batch * h_kv * n_rows;
+  const int64_t max_t = (int64_t)top_k * block_size;
+#pragma omp parallel
+  {
+    int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)max_t);
+    double *sidx = (double *)malloc(sizeof(double) * (size_t)max_t);
+    double *zh = (double *)malloc(sizeof(double) * (size_t)max_t);
+    double *t = (double *)malloc(sizeof(double) * (size_t)max_t);
+    if (!key || !sidx || !zh || !t) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < n_tasks; ++task) {
+      if (failed) continue;
+      const int i = (int)(task % n_rows);
+      const int r = (int)((task / n_rows) % h_kv);
+      const int b = (int)(task / ((int64_t)n_rows * h_kv));
+      const int64_t tq = rows[i], p = (int64_t)q_start + tq;
+      const int64_t qi_off = (((int64_t)b * h_kv + r) * n_q + tq) * d_idx;
+      const int64_t ki_off = (int64_t)b * n_k * d_idx;
+      const int64_t q_off = (((int64_t)b * h_q + (int64_t)r * group) * n_q + tq) * d_h;
+      const int64_t k_off = ((int64_t)b * h_kv + r) * (int64_t)n_k * d_h;
+      const int64_t out = ((int64_t)b * h_kv + r) * n_rows + i;
+      double l;
+      kl_row((const char *)q_idx + qi_off * (int64_t)es, (const char *)k_idx + ki_off * (int64_t)es,
+             (const char *)q + q_off * (int64_t)es, (int64_t)n_q * d_h,
+             (const char *)k + k_off * (int64_t)es, type, d_idx, d_h, group, p, block_size,
+             sel + out * top_k, top_k, key, sidx, zh, t, kl + out, &l);
+      if (lse_idx) lse_idx[out] = l;
+    }
+    free(key);
+    free(sidx);
+    free(zh);
+    free(t);
   }
   return failed ? -2 : 0;
 }

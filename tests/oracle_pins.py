@@ -3,7 +3,9 @@ mathematics fix, none of which re-types the oracle's own code.
 
 Definitions pinned (page "MiniMax-M3: MSA 技术报告速读", section 核心机制):
   index-branch token scores and causal block max-pool, the per-group TopK with
-  the local block forced in, and the main-branch sparse softmax attention.
+  the local block forced in, and the main-branch sparse softmax attention; and
+  (section 训练) the index-branch distribution P^idx, the group-averaged teacher
+  P^(r) over the selected tokens and the alignment loss KL(P^(r) || P^idx).
 
 Each pin takes an ``oracle.Oracle`` and raises AssertionError on a mismatch, so
 the same pins also run against deliberately broken oracle builds.
@@ -273,7 +275,97 @@ def pin_general_sparse(orc):
         assert np.allclose(out["lse"], lse, rtol=0, atol=1e-12)
 
 
+# ----------------------------------------------------------------- alignment loss pins
+
+def pin_kl_two_tokens_closed_form(orc):
+    """Two selected tokens, one head: both distributions are Bernoulli, and
+    KL(a || b) = a ln(a/b) + (1-a) ln((1-a)/(1-b)) with a = sigmoid(z1 - z0), b =
+    sigmoid(s1 - s0), worked by hand: d_h = d_idx = 1, q = 2, k = (0, 1), q_idx = 1,
+    k_idx = (0, 3), so z = (0, 2) and s = (0, 3)."""
+    w = shape(n_q=2, n_k=2, h_q=1, h_kv=1, d_h=1, d_idx=1, block_size=1, top_k=2)
+    inp = dict(q=torch.tensor([2.0, 2.0]).reshape(1, 1, 2, 1),
+               k=torch.tensor([0.0, 1.0]).reshape(1, 1, 2, 1),
+               v=torch.zeros(1, 1, 2, 1),
+               q_idx=torch.tensor([1.0, 1.0]).reshape(1, 1, 2, 1),
+               k_idx=torch.tensor([0.0, 3.0]).reshape(1, 2, 1))
+    sel = orc.run(w, inp, attention=False)["sel"]
+    assert sel[0, 0, 1].tolist() == [0, 1]
+    out = orc.kl(w, inp, sel)
+    a, b = 1 / (1 + math.exp(-2)), 1 / (1 + math.exp(-3))
+    want = a * math.log(a / b) + (1 - a) * math.log((1 - a) / (1 - b))
+    assert abs(out["kl"][0, 0, 1] - want) < 1e-14, (out["kl"][0, 0, 1], want)
+    assert abs(out["lse_idx"][0, 0, 1] - math.log(1 + math.exp(3))) < 1e-14
+    assert out["kl"][0, 0, 0] == 0.0  # row 0 sees one token: both distributions are {1}
+
+
+def pin_kl_student_equals_teacher(orc):
+    """Index branch identical to the main branch (one group, d_idx = d_h, q_idx = q of a
+    head, k_idx = k): the student equals every head's distribution, so the loss is 0 for
+    one head and for G identical heads (the teacher is their mean), on sparse selections."""
+    for G in (1, 3):
+        w = shape(batch=2, h_q=G, h_kv=1, n_q=40, n_k=40, d_h=6, d_idx=6, block_size=4,
+                  top_k=3)
+        g = torch.Generator().manual_seed(5)
+        q1 = torch.randn(2, 1, 40, 6, generator=g)
+        k = torch.randn(2, 1, 40, 6, generator=g)
+        inp = dict(q=q1.repeat(1, G, 1, 1), k=k, v=torch.zeros_like(k), q_idx=q1.clone(),
+                   k_idx=k[:, 0].clone())
+        sel = orc.run(w, inp, attention=False)["sel"]
+        local = (w.q_start + np.arange(w.n_q)) // w.block_size
+        assert ((sel >= 0).sum(-1) < local + 1).any()  # some selections leave blocks out
+        out = orc.kl(w, inp, sel)
+        assert np.abs(out["kl"]).max() < 1e-12, np.abs(out["kl"]).max()
+
+
+def pin_kl_uniform_teacher(orc):
+    """q = 0 makes every head's distribution uniform over the selected tokens T, so the
+    loss is KL(U || P^idx) = -ln|T| - mean_T log P^idx, with log P^idx from scipy's
+    log_softmax of exact integer index scores / sqrt(d_idx) over T."""
+    from scipy.special import log_softmax
+    w = shape(batch=2, h_q=4, h_kv=2, n_q=50, n_k=50, d_h=4, d_idx=3, block_size=4, top_k=4)
+    inp = rand_inputs(w, seed=9, idx_values=(-3, 4))
+    inp["q"] = torch.zeros_like(inp["q"])
+    sel = orc.run(w, inp, attention=False)["sel"]
+    out = orc.kl(w, inp, sel)
+    mask = visible_token_mask(w, sel)
+    qi = inp["q_idx"].numpy().astype(np.int64)
+    ki = inp["k_idx"].numpy().astype(np.int64)
+    s = np.einsum("brtd,bjd->brtj", qi, ki) / math.sqrt(w.d_idx)
+    for b, r, t in itertools.product(range(w.batch), range(w.h_kv), range(w.n_q)):
+        m = mask[b, r, t]
+        assert m.any(), (b, r, t)  # every row selects at least its own block
+        logq = log_softmax(s[b, r, t][m])
+        want = -math.log(m.sum()) - logq.mean()
+        assert abs(out["kl"][b, r, t] - want) < 1e-12, (b, r, t)
+        assert abs(out["lse_idx"][b, r, t] - np.log(np.exp(s[b, r, t][m]).sum())) < 1e-12
+
+
+def pin_kl_dense_scipy(orc):
+    """k covering every block: T is the whole causal prefix, and the loss is scipy's
+    relative entropy of the mean of the G heads' softmaxes (scipy) against the softmax of
+    the index scores, per row; it is also never negative."""
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    w = shape(batch=1, h_q=4, h_kv=2, n_q=24, n_k=24, d_h=5, d_idx=3, block_size=4, top_k=6)
+    inp = rand_inputs(w, seed=13, idx_values=(-2, 3))
+    sel = orc.run(w, inp, attention=False)["sel"]
+    out = orc.kl(w, inp, sel)
+    G = w.h_q // w.h_kv
+    q = inp["q"].double().numpy()
+    k = inp["k"].double().numpy()
+    qi = inp["q_idx"].double().numpy()
+    ki = inp["k_idx"].double().numpy()
+    for r, t in itertools.product(range(w.h_kv), range(w.n_q)):
+        n = t + 1
+        heads = [softmax(q[0, r * G + l, t] @ k[0, r, :n].T / math.sqrt(w.d_h)) for l in range(G)]
+        teacher = np.mean(heads, axis=0)
+        student = softmax(qi[0, r, t] @ ki[0, :n].T / math.sqrt(w.d_idx))
+        assert abs(out["kl"][0, r, t] - entropy(teacher, student)) < 1e-12, (r, t)
+    assert out["kl"].min() >= -1e-15
+
+
 PINS = [pin_block_scores_exact, pin_topk_bruteforce, pin_dense_when_k_covers,
         pin_local_block_only, pin_token_level, pin_zero_query_closed_form,
         pin_group_map_and_ones, pin_entry_point_consistency, pin_bf16_storage_widening,
-        pin_general_sparse]
+        pin_general_sparse, pin_kl_two_tokens_closed_form, pin_kl_student_equals_teacher,
+        pin_kl_uniform_teacher, pin_kl_dense_scipy]

@@ -75,6 +75,18 @@ MUTANTS = [
                                     "elem(k_idx_seq, d * (p + 1) + j, type)")]),
     ("bf16 widened with the wrong shift", [("((uint32_t)((const uint16_t *)base)[i]) << 16",
                                             "((uint32_t)((const uint16_t *)base)[i]) << 15")]),
+    ("student scores without 1/sqrt(d_idx)", [("sidx[n] = s / sqrt((double)d_idx);",
+                                              "sidx[n] = s;")]),
+    ("teacher sums the heads", [("/ hs / (double)group;", "/ hs;")]),
+    ("teacher without 1/sqrt(d_h)", [("zh[j] = s * scale;", "zh[j] = s;")]),
+    ("KL in the reverse direction", [("if (t[j] > 0.0) loss += t[j] * (log(t[j]) - (sidx[j] - lse_s));",
+                                      "loss += exp(sidx[j] - lse_s) * ((sidx[j] - lse_s) - log(t[j]));")]),
+    ("student normaliser without the max", [("const double lse_s = mu + log(zsum);",
+                                             "const double lse_s = log(zsum);")]),
+    ("teacher heads of group r taken from r on", [("(((int64_t)b * h_q + (int64_t)r * group) * n_q + tq) * d_h",
+                                                    "(((int64_t)b * h_q + (int64_t)r) * n_q + tq) * d_h")]),
+    ("teacher head stride of one row", [("(const char *)q + q_off * (int64_t)es, (int64_t)n_q * d_h,",
+                                         "(const char *)q + q_off * (int64_t)es, (int64_t)d_h,")]),
     ("query position ignores q_start", [("const int64_t t = rows[i], p = (int64_t)q_start + t;\n      const int64_t qoff = (((int64_t)b * h_kv",
                                          "const int64_t t = rows[i], p = t;\n      const int64_t qoff = (((int64_t)b * h_kv")]),
 ]
