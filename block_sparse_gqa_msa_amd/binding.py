@@ -23,7 +23,7 @@ EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_s
            "msa_topk_workspace_size", "msa_topk_from_block_scores",
            "msa_sparse_attn_workspace_size", "msa_sparse_attn_prefill",
            "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_partials",
-           "msa_sparse_attn_prefill_merge", "msa_sparse_attn_decode",
+           "msa_sparse_attn_prefill_merge", "msa_sparse_attn_decode", "msa_index_kl",
            "msa_last_error", "msa_abi_version")
 
 
@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_prefill_partials.argtypes = [S, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_prefill_merge.argtypes = [S, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_decode.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_index_kl.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     for f in EXPORTS:
         if f == "msa_last_error":
             continue
@@ -243,6 +244,18 @@ def msa_sparse_attn_decode(shape: MsaShape, q, k_cache, v_cache, sel, o, lse=Non
         ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k_cache, et, "k_cache"),
         _ptr(v_cache, et, "v_cache"), _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"),
         _ptr(lse, torch.float32, "lse"), wp, wn, _stream(stream, o)))
+
+
+def msa_index_kl(shape: MsaShape, q, k, q_idx, k_idx, sel, lse, kl, lse_idx=None,
+                 workspace=None, stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_index_kl(
+        ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k, et, "k"), _ptr(q_idx, et, "q_idx"),
+        _ptr(k_idx, et, "k_idx"), _ptr(sel, torch.int32, "sel"), _ptr(lse, torch.float32, "lse"),
+        _ptr(kl, torch.float32, "kl"), _ptr(lse_idx, torch.float32, "lse_idx"), wp, wn,
+        _stream(stream, kl)))
 
 
 # ----------------------------------------------------------------- allocation helpers

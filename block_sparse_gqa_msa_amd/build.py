@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.cpp", "msa_index.hip", "msa_topk.hip", "msa_attn.hip", "msa_kvouter.hip"]
+SOURCES = ["msa_api.cpp", "msa_index.hip", "msa_topk.hip", "msa_attn.hip", "msa_kvouter.hip",
+           "msa_kl.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

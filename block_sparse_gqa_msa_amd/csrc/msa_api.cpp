@@ -411,6 +411,32 @@ int msa_sparse_attn_prefill_merge(const msa_shape *shape, const int32_t *sel, vo
   return run_prefill(*shape, a, msa::KV_STAGE_MERGE, stream);
 }
 
+int msa_index_kl(const msa_shape *shape, const void *q, const void *k, const void *q_idx,
+                 const void *k_idx, const int32_t *sel, const float *lse, float *kl,
+                 float *lse_idx, void *workspace, size_t workspace_bytes, void *stream) {
+  msa::KvArgs a;
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if ((rc = check_index_dims(s))) return rc;
+  if (empty(s)) return empty_attn_call(s);
+  if (!q || !k || !q_idx || !k_idx || !sel || !lse || !kl)
+    return fail(MSA_ERR_INVALID_ARG, "q, k, q_idx, k_idx, sel, lse and kl must be non-NULL");
+  if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
+  a.q = q; a.k = k; a.sel = sel;
+  if ((rc = run_prefill(s, a, msa::KV_STAGE_PLAN, stream))) return rc;
+  msa::KvLayout lay;
+  attn_prefill_ws(s, &lay);
+  unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
+  const msa::KlArgs kk{q_idx, k_idx, lse, kl, lse_idx, reinterpret_cast<float4 *>(ws + lay.part_o),
+                       reinterpret_cast<float2 *>(ws + lay.part_ml),
+                       (float)(1.0 / std::sqrt((double)s.d_idx))};
+  hipError_t e = msa::launch_index_kl(a, kk, s.dtype, s.d_h, s.d_idx,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "alignment loss launch");
+  return ok();
+}
+
 int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_cache,
                            const void *v_cache, const int32_t *sel, void *o, float *lse,
                            void *workspace, size_t workspace_bytes, void *stream) {

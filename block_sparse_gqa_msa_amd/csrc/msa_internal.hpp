@@ -67,6 +67,21 @@ struct KvArgs {          // KV-outer prefill attention
   float scale_log2;
 };
 
+constexpr int KV_CHUNK = 128;  // list entries per work item of the KV-outer kernels
+
+// The alignment loss over the KV-outer lists (the KvArgs of the same shape carry q, k, sel,
+// the lists and the sizes).
+struct KlArgs {
+  const void *q_idx;  // [B, R, n_q, DI]
+  const void *k_idx;  // [B, cap, DI]
+  const float *lse;   // [B, H, n_q] main-branch log-sum-exp (natural log) from the forward
+  float *kl;          // [B, R, n_q] out
+  float *lse_idx;     // [B, R, n_q] out, or null
+  float4 *part;       // [B*R*n_q*top_k] per selection: (sum t ln t, sum t S^idx, sum t, 0)
+  float2 *part_ml;    // [B*R*n_q*top_k] per selection: index scores' (max, sum), log2 units
+  float scale_idx;    // 1 / sqrt(d_idx)
+};
+
 struct KvLayout {
   size_t cnt, boff, coff, cmap, tile_sum, list, part_o, part_ml, total;
 };
@@ -93,5 +108,8 @@ hipError_t launch_index_select_decode(const IndexArgs &a, int dtype, int d_idx, 
 enum { KV_STAGE_PLAN = 1, KV_STAGE_ATTEND = 2, KV_STAGE_MERGE = 4, KV_STAGE_ALL = 7 };
 hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, int stages, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s);
+// Alignment loss from the lists a plan stage built: per-selection sums, then the merge.
+hipError_t launch_index_kl(const KvArgs &a, const KlArgs &k, int dtype, int d_h, int d_idx,
+                           hipStream_t s);
 
 }  // namespace msa

@@ -1,0 +1,274 @@
+// msa_kl.hip -- the index branch's alignment loss over the selected tokens.
+//
+// Definition ("MiniMax-M3: MSA 技术报告速读", section 训练, the equations for P^idx, P^(r)
+// and L_KL): for row t of group r, over the selected blocks' visible tokens T,
+//   student  P^idx_j = softmax_T(S^idx)_j,  S^idx_j = q_idx . k_idx_j / sqrt(d_idx)
+//   teacher  P^(r)_j = (1/G) sum over the group's heads l of softmax_T(S^(l))_j,
+//            S^(l)_j = q_l . k_j / sqrt(d_h)
+//   L_KL = KL(P^(r) || P^idx) = sum_j P^(r)_j (ln P^(r)_j - ln P^idx_j).
+// The teacher uses the main branch's log-sum-exp from the forward pass (the same page's
+// Kernel section has the sparse loss take it from the forward), so each head's
+// probabilities are exp(S^(l)_j - lse_l) with no second normalisation pass.
+//
+// Organised like the prefill attention, KV-block-outer over the same per-block row lists:
+//   kv_kl     each chunk stages one block's K and K_idx rows in LDS and, per 16-column
+//             tile (16/G rows x the G heads), computes S^T = K Q^T and S_idx^T = K_idx Q_idx^T
+//             on the matrix cores, the teacher weights t_j (the head-mean, across the G lanes
+//             of a row), and per (row, slot) the block's sums A = sum t ln t, B = sum t S^idx,
+//             T = sum t and the index scores' (max, sum of 2^(z - max)) in log2 units.
+//   kl_merge  per (b, r, row): L = A - B + lse_idx * T with lse_idx = ln sum_j exp(S^idx_j)
+//             from the slots' (max, sum) pairs. (T is 1 up to the rounding of the forward's
+//             lse; the loss keeps it as computed.)
+#include "msa_device.hpp"
+#include "msa_internal.hpp"
+
+namespace msa {
+namespace {
+
+// Stage rows [kb, kb+BS) of a row-major [*, D] array into LDS rows of ROWB bytes, 256
+// threads. All loads are issued before the first LDS write; rows past n_k read row n_k - 1
+// (their keys are masked later), so no load sits under a branch.
+template <typename E, int D, int BS, int ROWB>
+__device__ __forceinline__ void stage_rows(const E *src, long kb, int n_k, unsigned char *dst) {
+  constexpr int PER_ROW = D * (int)sizeof(E) / 16, PIECES = BS * PER_ROW;
+  constexpr int PT = (PIECES + 255) / 256;
+  const int tid = threadIdx.x;
+  const long last = (long)n_k - 1;
+  u32x4 x[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int pc = min(tid + 256 * i, PIECES - 1);
+    const long j = min(kb + pc / PER_ROW, last);
+    x[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+        reinterpret_cast<const unsigned char *>(src + j * D) + (pc % PER_ROW) * 16));
+  }
+#pragma unroll
+  for (int i = 0; i < PT; ++i) pin(x[i]);
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int pc = tid + 256 * i;
+    if (PIECES % 256 == 0 || pc < PIECES)
+      *reinterpret_cast<u32x4 *>(dst + (pc / PER_ROW) * ROWB + (pc % PER_ROW) * 16) = x[i];
+  }
+}
+
+// v plus lane (l' ) of v, where DPP control `ctl` names l' inside each row of 16 lanes.
+template <int CTL>
+__device__ __forceinline__ float add_dpp(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTL, 0xf, 0xf, false));
+}
+// Sum over the G consecutive lanes of a row (G = 1 << log2g <= 16, aligned inside each row
+// of 16): swaps within pairs and quads, then the half-row and row mirrors, each of which
+// pairs every lane with one holding the other half's partial sum.
+__device__ __forceinline__ float sum_heads(float v, int log2g) {
+  if (log2g >= 1) v = add_dpp<0xb1>(v);   // quad_perm(1,0,3,2): lane ^ 1
+  if (log2g >= 2) v = add_dpp<0x4e>(v);   // quad_perm(2,3,0,1): lane ^ 2
+  if (log2g >= 3) v = add_dpp<0x141>(v);  // row_half_mirror: lane 7 - l within 8
+  if (log2g >= 4) v = add_dpp<0x140>(v);  // row_mirror: lane 15 - l within 16
+  return v;
+}
+
+template <typename E, int DH, int DI, int BS>
+__global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
+  using F = typename Frag<E>::type;
+  constexpr int ES = (int)sizeof(E);
+  constexpr int KROW = DH * ES + 16, IROW = DI * ES + 16;
+  constexpr int DC = DH / 32, DCI = DI / 32, KTN = BS / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[BS * KROW];
+  __shared__ __attribute__((aligned(16))) unsigned char s_ki[BS * IROW];
+  __shared__ int32_t s_list[KV_CHUNK];
+
+  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
+  const int n_chunks = a.coff[NB];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int G = 1 << log2g, QPT = 16 >> log2g;
+  const int qi = c16 >> log2g, hd = c16 & (G - 1);
+  const E *q = reinterpret_cast<const E *>(a.q);
+  const E *qx = reinterpret_cast<const E *>(k.q_idx);
+  const float cs = a.scale_log2;             // log2(e) / sqrt(d_h)
+  const float ci = k.scale_idx * 1.44269504088896341f;  // log2(e) / sqrt(d_idx)
+  const float inv_g = 1.f / (float)G;
+
+  for (int chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {  // uniform loop
+    const long i = a.cmap[chunk];
+    const int c = (int)(i % a.n_blocks);
+    const long rsb = i / a.n_blocks;  // (r, seg, b) of the list
+    const int b = (int)(rsb % a.batch);
+    const int r = (int)(rsb / a.batch / a.n_seg);
+    const int e0 = a.boff[i] + (chunk - a.coff[i]) * KV_CHUNK;
+    const int n_e = min(e0 + KV_CHUNK, a.boff[i + 1]) - e0;
+    const E *kp = reinterpret_cast<const E *>(a.k) + ((long)b * a.h_kv + r) * (long)a.cap * DH;
+    const E *kip = reinterpret_cast<const E *>(k.k_idx) + (long)b * a.cap * DI;
+    const long kb = (long)c * BS;
+    const int h = r * G + hd;
+
+    __syncthreads();  // the previous chunk is done with the LDS buffers
+    if (tid < n_e) s_list[tid] = a.list[e0 + tid];
+    stage_rows<E, DH, BS, KROW>(kp, kb, a.n_k, s_k);
+    stage_rows<E, DI, BS, IROW>(kip, kb, a.n_k, s_ki);
+    __syncthreads();
+
+    F kf[KTN][DC], kif[KTN][DCI];
+#pragma unroll
+    for (int kt = 0; kt < KTN; ++kt) {
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        kf[kt][dc] = load_frag(reinterpret_cast<const E *>(s_k + (kt * 16 + c16) * KROW +
+                                                          (dc * 32 + g * 8) * ES));
+#pragma unroll
+      for (int dc = 0; dc < DCI; ++dc)
+        kif[kt][dc] = load_frag(reinterpret_cast<const E *>(s_ki + (kt * 16 + c16) * IROW +
+                                                           (dc * 32 + g * 8) * ES));
+    }
+
+    const int n_tiles = (n_e + QPT - 1) / QPT;
+    // The next tile's q, q_idx and lse load while this one computes. Loads are
+    // unconditional: lanes past the chunk's entries read entry 0's row (masked later), so
+    // no load sits under a branch.
+    struct TileIn {
+      F q[DC], qi[DCI];
+      float lse;
+    };
+    auto load_tile = [&](int tt, TileIn &d) {
+      const int e = tt * QPT + qi;
+      const int t = s_list[(tt < n_tiles && e < n_e) ? e : 0] >> 6;
+      const E *src = q + (((long)b * a.h_q + h) * a.n_q + t) * DH + g * 8;
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) d.q[dc] = load_frag(src + dc * 32);
+      const E *srci = qx + (((long)b * a.h_kv + r) * a.n_q + t) * DI + g * 8;
+#pragma unroll
+      for (int dc = 0; dc < DCI; ++dc) d.qi[dc] = load_frag(srci + dc * 32);
+      d.lse = k.lse[((long)b * a.h_q + h) * a.n_q + t];
+    };
+    TileIn cur, nxt;
+    load_tile(w, cur);
+    for (int tt = w; tt < n_tiles; tt += 4) {
+      load_tile(tt + 4, nxt);
+      const int e = tt * QPT + qi;
+      const bool valid = e < n_e;
+      const int ent = s_list[valid ? e : 0];
+      const int t = ent >> 6, slot = ent & 63;
+      const long p = (long)a.q_start + t;
+      const F(&bq)[DC] = cur.q;
+      const F(&bqi)[DCI] = cur.qi;
+      const float lse2 = cur.lse * 1.44269504088896341f;
+
+      f32x4 s[KTN], si[KTN];
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acci = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) acc = mfma_chunk(kf[kt][dc], bq[dc], acc);
+#pragma unroll
+        for (int dc = 0; dc < DCI; ++dc) acci = mfma_chunk(kif[kt][dc], bqi[dc], acci);
+        s[kt] = acc;
+        si[kt] = acci;
+      }
+      // key offset kt*16 + g*4 + ii of this block is visible to the row iff it is <= lim
+      const int lim = valid ? (int)min(p - kb, (long)BS - 1) : -1;
+      float sa = 0.f, sb = 0.f, st = 0.f, zm = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const bool vis = kt * 16 + g * 4 + ii <= lim;
+          // this head's probability, then the mean over the row's G heads
+          const float ph = vis ? __builtin_amdgcn_exp2f(fmaf(s[kt][ii], cs, -lse2)) : 0.f;
+          const float tj = sum_heads(ph, log2g) * inv_g;
+          const float sidx = si[kt][ii] * k.scale_idx;  // S^idx, natural units
+          if (tj > 0.f) sa += tj * (__builtin_amdgcn_logf(tj) * 0.69314718055994531f);
+          sb += tj * sidx;
+          st += tj;
+          if (vis) zm = fmaxf(zm, si[kt][ii] * ci);
+        }
+      float zl = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          if (kt * 16 + g * 4 + ii <= lim) zl += __builtin_amdgcn_exp2f(si[kt][ii] * ci - zm);
+      // the block's totals: sums over the 4 lane groups (each holds 4 keys of every tile)
+      sa = sum_groups(sa);
+      sb = sum_groups(sb);
+      st = sum_groups(st);
+      const float zmax = max_groups(zm);
+      zl = sum_groups(zm == -INFINITY ? 0.f : zl * __builtin_amdgcn_exp2f(zm - zmax));
+      if (valid && hd == 0 && g == 0) {
+        const long ps = (((long)b * a.h_kv + r) * a.n_q + t) * a.top_k + slot;
+        k.part[ps] = make_float4(sa, sb, st, 0.f);
+        k.part_ml[ps] = make_float2(zmax, zl);
+      }
+      cur = nxt;
+    }
+  }
+}
+
+// One thread per (b, r, row): the row's slots in order.
+__global__ __launch_bounds__(256) void kl_merge(KvArgs a, KlArgs k) {
+  const long row = (long)blockIdx.x * 256 + threadIdx.x;  // (b, r, t)
+  if (row >= (long)a.batch * a.h_kv * a.n_q) return;
+  float A = 0.f, B = 0.f, T = 0.f, M = -INFINITY, L = 0.f;
+  for (int sl = 0; sl < a.top_k; ++sl) {
+    const int c = a.sel[row * a.top_k + sl];
+    if (c < 0 || c >= a.n_blocks) continue;
+    const float4 pa = k.part[row * a.top_k + sl];
+    const float2 ml = k.part_ml[row * a.top_k + sl];
+    A += pa.x;
+    B += pa.y;
+    T += pa.z;
+    if (ml.y > 0.f) {
+      const float Mn = fmaxf(M, ml.x);
+      L = (M == -INFINITY ? 0.f : L * __builtin_amdgcn_exp2f(M - Mn)) +
+          ml.y * __builtin_amdgcn_exp2f(ml.x - Mn);
+      M = Mn;
+    }
+  }
+  const float lse_idx = (M + __log2f(L)) * 0.69314718055994531f;
+  k.kl[row] = A - B + lse_idx * T;
+  if (k.lse_idx) k.lse_idx[row] = lse_idx;
+}
+
+template <typename E, int DH, int DI, int BS>
+hipError_t run_kl(const KvArgs &a, const KlArgs &k, int log2g, hipStream_t s) {
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kv_kl<E, DH, DI, BS>, 256, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    return n;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
+  const long entries = (long)a.batch * a.h_kv * a.n_q * a.top_k;
+  const long max_chunks = (entries + KV_CHUNK - 1) / KV_CHUNK + NB;
+  const unsigned grid = (unsigned)std::min(max_chunks, 2L * per_cu * cus);
+  hipLaunchKernelGGL((kv_kl<E, DH, DI, BS>), dim3(grid), dim3(256), 0, s, a, k, log2g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long rows = (long)a.batch * a.h_kv * a.n_q;
+  hipLaunchKernelGGL(kl_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a, k);
+  return hipGetLastError();
+}
+
+template <typename E, int DH>
+hipError_t kl_dims(const KvArgs &a, const KlArgs &k, int d_idx, int lg, hipStream_t s) {
+  if (d_idx == 32)
+    return a.block_size == 32 ? run_kl<E, DH, 32, 32>(a, k, lg, s) : run_kl<E, DH, 32, 64>(a, k, lg, s);
+  return a.block_size == 32 ? run_kl<E, DH, 64, 32>(a, k, lg, s) : run_kl<E, DH, 64, 64>(a, k, lg, s);
+}
+
+}  // namespace
+
+hipError_t launch_index_kl(const KvArgs &a, const KlArgs &k, int dtype, int d_h, int d_idx,
+                           hipStream_t s) {
+  int lg = 0;
+  while ((1 << lg) < a.h_q / a.h_kv) ++lg;
+  if (dtype == 0)
+    return d_h == 64 ? kl_dims<float, 64>(a, k, d_idx, lg, s) : kl_dims<float, 128>(a, k, d_idx, lg, s);
+  return d_h == 64 ? kl_dims<bf16_t, 64>(a, k, d_idx, lg, s) : kl_dims<bf16_t, 128>(a, k, d_idx, lg, s);
+}
+
+}  // namespace msa

@@ -28,7 +28,7 @@
 namespace msa {
 namespace {
 
-constexpr int CHUNK = 128;                // entries per kv_attend work item
+constexpr int CHUNK = KV_CHUNK;           // entries per kv_attend work item
 constexpr long KV_Q_SLICE = 64L << 20;    // bytes of one group's Q rows per list segment
 constexpr int HIST_ROWS_ENTRIES = 32768;  // entries per list-build workgroup
 constexpr int HIST_MAX_BLOCKS = 32768;    // LDS histogram capacity (128 KiB)

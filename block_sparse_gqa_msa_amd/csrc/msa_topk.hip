@@ -19,7 +19,6 @@ namespace msa {
 namespace {
 
 constexpr int V = TOPK_CHUNK / 64;  // items per lane
-constexpr int CAP = SELECT_CAP;
 
 // Best m of candidates [base, base + valid) of one problem's block scores, VI per lane.
 template <int VI>

@@ -179,6 +179,31 @@ int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_
                            const void *v_cache, const int32_t *sel, void *o, float *lse,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Index-branch alignment loss ("MiniMax-M3: MSA 技术报告速读", section 训练: the equations
+ * for P^idx, P^(r) and L_KL), for every (b, group r, row t) over T = the visible tokens of
+ * the blocks in sel[b, r, t, :]:
+ *   student  P^idx = softmax over T of S^idx_j = q_idx . k_idx_j / sqrt(d_idx)
+ *   teacher  P^(r) = mean over the group's G heads h of softmax over T of q_h . k_j / sqrt(d_h)
+ *   kl[b, r, t] = KL(P^(r) || P^idx) = sum_j P^(r)_j (ln P^(r)_j - ln P^idx_j)
+ *   q, k, q_idx, k_idx, sel  as for msa_sparse_attn_prefill and msa_index_topk (any n_q and
+ *            q_start, decode rows included)
+ *   lse      [batch, h_q, n_q] float32: the natural-log LSE the attention entry points
+ *            write for the same q, k and sel; the teacher's probabilities are
+ *            exp(q_h . k_j / sqrt(d_h) - lse)
+ *   kl       out [batch, h_kv, n_q] float32
+ *   lse_idx  optional out (NULL to skip) [batch, h_kv, n_q] float32: ln sum_T exp(S^idx_j),
+ *            the student's normaliser
+ *   workspace at least msa_sparse_attn_workspace_size bytes (its lists and partials).
+ * Computed KV-block-outer over the same per-block row lists as the prefill attention:
+ * per selection, the block's sums of t ln t, t S^idx and t (t the teacher's weight) and
+ * the index scores' max and sum of exponentials, then a per-row merge. Supported set and
+ * size limits as for msa_sparse_attn_prefill plus d_idx in {32, 64}.
+ */
+int msa_index_kl(const msa_shape *shape, const void *q, const void *k, const void *q_idx,
+                 const void *k_idx, const int32_t *sel, const float *lse, float *kl,
+                 float *lse_idx, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Text of the last error on the calling thread (empty after a successful call). */
 const char *msa_last_error(void);
 

@@ -201,3 +201,24 @@ def test_empty_calls_are_noops(lib):
     s = good(batch=0, d_idx=48)
     assert lib.msa_index_topk(ctypes.byref(s), None, None, None, None, None, 0, None) \
         == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_index_kl_rejects(lib):
+    dummy = 1 << 20
+    s = good()
+    need = msa.msa_sparse_attn_workspace_size(s)
+    sb = ctypes.byref(s)
+    args = [dummy] * 7  # q, k, q_idx, k_idx, sel, lse, kl
+    for i in range(7):
+        a = list(args)
+        a[i] = None
+        assert lib.msa_index_kl(sb, *a, None, dummy, need, None) == msa.MSA_ERR_INVALID_ARG
+        assert "non-NULL" in msa.msa_last_error()
+    assert lib.msa_index_kl(sb, *args, None, dummy, need - 1, None) == msa.MSA_ERR_WORKSPACE
+    assert lib.msa_index_kl(sb, *args, None, None, need, None) == msa.MSA_ERR_WORKSPACE
+    for bad in (dict(d_idx=48), dict(d_h=96)):
+        x = good(**bad)
+        assert lib.msa_index_kl(ctypes.byref(x), *args, None, dummy, need, None) \
+            == msa.MSA_ERR_UNSUPPORTED
+    e = good(n_q=0)
+    assert lib.msa_index_kl(ctypes.byref(e), *([None] * 8), None, 0, None) == msa.MSA_OK
