@@ -11,11 +11,11 @@
 // probabilities are exp(S^(l)_j - lse_l) with no second normalisation pass.
 //
 // Organised like the prefill attention, KV-block-outer over the same per-block row lists:
-//   kv_kl     each chunk stages one block's K and K_idx rows in LDS and, per 16-column
-//             tile (16/G rows x the G heads), computes S^T = K Q^T and S_idx^T = K_idx Q_idx^T
-//             on the matrix cores, the teacher weights t_j (the head-mean, across the G lanes
-//             of a row), and per (row, slot) the block's sums A = sum t ln t, B = sum t S^idx,
-//             T = sum t and the index scores' (max, sum of 2^(z - max)) in log2 units.
+//   kv_kl     each chunk stages one block's K and K_idx rows in LDS and, per 16-row tile
+//             (16/G rows x the G heads), computes S = Q K^T and S_idx = Q_idx K_idx^T on the
+//             matrix cores, the teacher weights t_j (the head mean), and per (row, slot)
+//             the block's sums A = sum t ln t, B = sum t S^idx, T = sum t and the index
+//             scores' (max, sum of 2^(z - max)) in log2 units.
 //   kl_merge  per (b, r, row): L = A - B + lse_idx * T with lse_idx = ln sum_j exp(S^idx_j)
 //             from the slots' (max, sum) pairs. (T is 1 up to the rounding of the forward's
 //             lse; the loss keeps it as computed.)
@@ -52,28 +52,39 @@ __device__ __forceinline__ void stage_rows(const E *src, long kb, int n_k, unsig
   }
 }
 
-// v plus lane (l' ) of v, where DPP control `ctl` names l' inside each row of 16 lanes.
+// Lane (l') of v inside each row of 16 lanes, l' named by the DPP control CTL.
 template <int CTL>
-__device__ __forceinline__ float add_dpp(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTL, 0xf, 0xf, false));
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTL, 0xf, 0xf, false));
 }
-// Sum over the G consecutive lanes of a row (G = 1 << log2g <= 16, aligned inside each row
-// of 16): swaps within pairs and quads, then the half-row and row mirrors, each of which
-// pairs every lane with one holding the other half's partial sum.
-__device__ __forceinline__ float sum_heads(float v, int log2g) {
-  if (log2g >= 1) v = add_dpp<0xb1>(v);   // quad_perm(1,0,3,2): lane ^ 1
-  if (log2g >= 2) v = add_dpp<0x4e>(v);   // quad_perm(2,3,0,1): lane ^ 2
-  if (log2g >= 3) v = add_dpp<0x141>(v);  // row_half_mirror: lane 7 - l within 8
-  if (log2g >= 4) v = add_dpp<0x140>(v);  // row_mirror: lane 15 - l within 16
-  return v;
+// Sum / max over the 16 lanes of a row: swaps within pairs and quads, then the half-row and
+// row mirrors, each pairing every lane with one that holds the other half's partial.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp<0xb1>(v);   // quad_perm(1,0,3,2)
+  v += dpp<0x4e>(v);   // quad_perm(2,3,0,1)
+  v += dpp<0x141>(v);  // row_half_mirror
+  return v + dpp<0x140>(v);  // row_mirror
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<0xb1>(v));
+  v = fmaxf(v, dpp<0x4e>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  return fmaxf(v, dpp<0x140>(v));
 }
 
-template <typename E, int DH, int DI, int BS>
+// S = Q K^T with the row-heads of a 16-row tile down the accumulator rows and the block's
+// keys across the columns: lane (c16, g) holds key kt * 16 + c16 for row-heads m = 4g + i
+// (row m >> log2g of the tile, head m & (G - 1)), i = 0..3. A row's G heads then sit in one
+// lane (G <= 4) or in G / 4 lane groups (G = 8, 16), so the teacher's head mean is a few
+// in-lane adds and at most two half-wave swaps. LG = min(log2g, 2): the value slots of one
+// row in a lane are 1 << LG consecutive i; R4 = 4 >> LG rows per lane group.
+template <typename E, int DH, int DI, int BS, int LG>
 __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   using F = typename Frag<E>::type;
   constexpr int ES = (int)sizeof(E);
   constexpr int KROW = DH * ES + 16, IROW = DI * ES + 16;
   constexpr int DC = DH / 32, DCI = DI / 32, KTN = BS / 16;
+  constexpr int R4 = 4 >> LG;  // rows per lane group
   __shared__ __attribute__((aligned(16))) unsigned char s_k[BS * KROW];
   __shared__ __attribute__((aligned(16))) unsigned char s_ki[BS * IROW];
   __shared__ int32_t s_list[KV_CHUNK];
@@ -82,12 +93,13 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   const int n_chunks = a.coff[NB];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int G = 1 << log2g, QPT = 16 >> log2g;
-  const int qi = c16 >> log2g, hd = c16 & (G - 1);
+  const int qi = c16 >> log2g, hd = c16 & (G - 1);  // the row-head this lane feeds to the A operand
   const E *q = reinterpret_cast<const E *>(a.q);
   const E *qx = reinterpret_cast<const E *>(k.q_idx);
-  const float cs = a.scale_log2;             // log2(e) / sqrt(d_h)
+  const float cs = a.scale_log2;                        // log2(e) / sqrt(d_h)
   const float ci = k.scale_idx * 1.44269504088896341f;  // log2(e) / sqrt(d_idx)
   const float inv_g = 1.f / (float)G;
+  const bool writer_g = ((g * 4) & (G - 1)) == 0;  // first lane group of its rows
 
   for (int chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {  // uniform loop
     const long i = a.cmap[chunk];
@@ -100,7 +112,7 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
     const E *kp = reinterpret_cast<const E *>(a.k) + ((long)b * a.h_kv + r) * (long)a.cap * DH;
     const E *kip = reinterpret_cast<const E *>(k.k_idx) + (long)b * a.cap * DI;
     const long kb = (long)c * BS;
-    const int h = r * G + hd;
+    const float *lse_r = k.lse + ((long)b * a.h_q + (long)r * G) * a.n_q;  // head r*G, row 0
 
     __syncthreads();  // the previous chunk is done with the LDS buffers
     if (tid < n_e) s_list[tid] = a.list[e0 + tid];
@@ -122,81 +134,117 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
     }
 
     const int n_tiles = (n_e + QPT - 1) / QPT;
-    // The next tile's q, q_idx and lse load while this one computes. Loads are
-    // unconditional: lanes past the chunk's entries read entry 0's row (masked later), so
+    // The next tile's inputs load while this one computes: q and q_idx of the row-head
+    // this lane feeds, and the LSE of its four accumulator row-heads. Loads are
+    // unconditional (lanes past the chunk's entries read entry 0's row and are masked), so
     // no load sits under a branch.
     struct TileIn {
       F q[DC], qi[DCI];
-      float lse;
+      float lse[4];
+    };
+    auto row_of = [&](int tt, int qm) {  // s_list entry of row qm of tile tt, or entry 0
+      const int e = tt * QPT + qm;
+      return s_list[(tt < n_tiles && e < n_e) ? e : 0];
     };
     auto load_tile = [&](int tt, TileIn &d) {
-      const int e = tt * QPT + qi;
-      const int t = s_list[(tt < n_tiles && e < n_e) ? e : 0] >> 6;
-      const E *src = q + (((long)b * a.h_q + h) * a.n_q + t) * DH + g * 8;
+      const int t = row_of(tt, qi) >> 6;
+      const E *src = q + (((long)b * a.h_q + r * G + hd) * a.n_q + t) * DH + g * 8;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) d.q[dc] = load_frag(src + dc * 32);
       const E *srci = qx + (((long)b * a.h_kv + r) * a.n_q + t) * DI + g * 8;
 #pragma unroll
       for (int dc = 0; dc < DCI; ++dc) d.qi[dc] = load_frag(srci + dc * 32);
-      d.lse = k.lse[((long)b * a.h_q + h) * a.n_q + t];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int m = 4 * g + ii;
+        d.lse[ii] = lse_r[(long)(m & (G - 1)) * a.n_q + (row_of(tt, m >> log2g) >> 6)];
+      }
     };
     TileIn cur, nxt;
     load_tile(w, cur);
     for (int tt = w; tt < n_tiles; tt += 4) {
       load_tile(tt + 4, nxt);
-      const int e = tt * QPT + qi;
-      const bool valid = e < n_e;
-      const int ent = s_list[valid ? e : 0];
-      const int t = ent >> 6, slot = ent & 63;
-      const long p = (long)a.q_start + t;
-      const F(&bq)[DC] = cur.q;
-      const F(&bqi)[DCI] = cur.qi;
-      const float lse2 = cur.lse * 1.44269504088896341f;
-
       f32x4 s[KTN], si[KTN];
 #pragma unroll
       for (int kt = 0; kt < KTN; ++kt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acci = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) acc = mfma_chunk(kf[kt][dc], bq[dc], acc);
+        for (int dc = 0; dc < DC; ++dc) acc = mfma_chunk(cur.q[dc], kf[kt][dc], acc);
 #pragma unroll
-        for (int dc = 0; dc < DCI; ++dc) acci = mfma_chunk(kif[kt][dc], bqi[dc], acci);
+        for (int dc = 0; dc < DCI; ++dc) acci = mfma_chunk(cur.qi[dc], kif[kt][dc], acci);
         s[kt] = acc;
         si[kt] = acci;
       }
-      // key offset kt*16 + g*4 + ii of this block is visible to the row iff it is <= lim
-      const int lim = valid ? (int)min(p - kb, (long)BS - 1) : -1;
-      float sa = 0.f, sb = 0.f, st = 0.f, zm = -INFINITY;
+      // per value slot: the key offset c16 of each tile is visible to its row iff <= lim
+      int lim[4];
+      float lse2[4];
 #pragma unroll
-      for (int kt = 0; kt < KTN; ++kt)
+      for (int ii = 0; ii < 4; ++ii) {
+        const int qm = (4 * g + ii) >> log2g;
+        const bool valid = tt * QPT + qm < n_e;
+        const long p = (long)a.q_start + (row_of(tt, qm) >> 6);
+        lim[ii] = valid ? (int)min(p - kb, (long)BS - 1) : -1;
+        lse2[ii] = cur.lse[ii] * 1.44269504088896341f;
+      }
+      float sa[R4], sb[R4], st[R4], zm[R4];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const bool vis = kt * 16 + g * 4 + ii <= lim;
-          // this head's probability, then the mean over the row's G heads
-          const float ph = vis ? __builtin_amdgcn_exp2f(fmaf(s[kt][ii], cs, -lse2)) : 0.f;
-          const float tj = sum_heads(ph, log2g) * inv_g;
-          const float sidx = si[kt][ii] * k.scale_idx;  // S^idx, natural units
-          if (tj > 0.f) sa += tj * (__builtin_amdgcn_logf(tj) * 0.69314718055994531f);
-          sb += tj * sidx;
-          st += tj;
-          if (vis) zm = fmaxf(zm, si[kt][ii] * ci);
-        }
-      float zl = 0.f;
+      for (int j = 0; j < R4; ++j) {
+        sa[j] = 0.f;
+        sb[j] = 0.f;
+        st[j] = 0.f;
+        zm[j] = -INFINITY;
+      }
 #pragma unroll
-      for (int kt = 0; kt < KTN; ++kt)
+      for (int kt = 0; kt < KTN; ++kt) {
+        const int key = kt * 16 + c16;
+        float ph[4];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          if (kt * 16 + g * 4 + ii <= lim) zl += __builtin_amdgcn_exp2f(si[kt][ii] * ci - zm);
-      // the block's totals: sums over the 4 lane groups (each holds 4 keys of every tile)
-      sa = sum_groups(sa);
-      sb = sum_groups(sb);
-      st = sum_groups(st);
-      const float zmax = max_groups(zm);
-      zl = sum_groups(zm == -INFINITY ? 0.f : zl * __builtin_amdgcn_exp2f(zm - zmax));
-      if (valid && hd == 0 && g == 0) {
-        const long ps = (((long)b * a.h_kv + r) * a.n_q + t) * a.top_k + slot;
-        k.part[ps] = make_float4(sa, sb, st, 0.f);
-        k.part_ml[ps] = make_float2(zmax, zl);
+          ph[ii] = key <= lim[ii] ? __builtin_amdgcn_exp2f(fmaf(s[kt][ii], cs, -lse2[ii])) : 0.f;
+        // the head mean of each row of this lane group
+        float hs[R4];
+#pragma unroll
+        for (int j = 0; j < R4; ++j) {
+          float v = 0.f;
+#pragma unroll
+          for (int u = 0; u < (1 << LG); ++u) v += ph[(j << LG) + u];
+          hs[j] = v;
+        }
+        if constexpr (LG == 2) {  // G >= 4: one row per lane group, maybe across groups
+          const float x8 = sum_xor16(hs[0]);
+          const float x16 = sum_xor32(x8);
+          hs[0] = log2g >= 4 ? x16 : (log2g == 3 ? x8 : hs[0]);
+        }
+#pragma unroll
+        for (int j = 0; j < R4; ++j) {
+          const int ii = j << LG;
+          const float t = hs[j] * inv_g;
+          const float sidx = si[kt][ii] * k.scale_idx;  // S^idx, natural units
+          sa[j] += t > 0.f ? t * (__builtin_amdgcn_logf(t) * 0.69314718055994531f) : 0.f;
+          sb[j] += t * sidx;
+          st[j] += t;
+          zm[j] = key <= lim[ii] ? fmaxf(zm[j], si[kt][ii] * ci) : zm[j];
+        }
+      }
+      // the tile's rows: totals over the 16 keys of each key tile (lanes of a row of 16)
+#pragma unroll
+      for (int j = 0; j < R4; ++j) {
+        const int ii = j << LG;
+        const float M = max16(zm[j]);
+        float zl = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KTN; ++kt)
+          zl += kt * 16 + c16 <= lim[ii] ? __builtin_amdgcn_exp2f(si[kt][ii] * ci - M) : 0.f;
+        zl = sum16(zl);
+        const float ta = sum16(sa[j]), tb = sum16(sb[j]), tt_ = sum16(st[j]);
+        const int qm = (4 * g + ii) >> log2g;
+        const int e = tt * QPT + qm;
+        if (c16 == 0 && writer_g && e < n_e) {
+          const int ent = s_list[e];
+          const long ps = (((long)b * a.h_kv + r) * a.n_q + (ent >> 6)) * a.top_k + (ent & 63);
+          k.part[ps] = make_float4(ta, tb, tt_, 0.f);
+          k.part_ml[ps] = make_float2(M, zl);
+        }
       }
       cur = nxt;
     }
@@ -228,11 +276,11 @@ __global__ __launch_bounds__(256) void kl_merge(KvArgs a, KlArgs k) {
   if (k.lse_idx) k.lse_idx[row] = lse_idx;
 }
 
-template <typename E, int DH, int DI, int BS>
+template <typename E, int DH, int DI, int BS, int LG>
 hipError_t run_kl(const KvArgs &a, const KlArgs &k, int log2g, hipStream_t s) {
   static const int per_cu = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kv_kl<E, DH, DI, BS>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kv_kl<E, DH, DI, BS, LG>, 256, 0) !=
             hipSuccess || n < 1)
       n = 1;
     return n;
@@ -245,7 +293,7 @@ hipError_t run_kl(const KvArgs &a, const KlArgs &k, int log2g, hipStream_t s) {
   const long entries = (long)a.batch * a.h_kv * a.n_q * a.top_k;
   const long max_chunks = (entries + KV_CHUNK - 1) / KV_CHUNK + NB;
   const unsigned grid = (unsigned)std::min(max_chunks, 2L * per_cu * cus);
-  hipLaunchKernelGGL((kv_kl<E, DH, DI, BS>), dim3(grid), dim3(256), 0, s, a, k, log2g);
+  hipLaunchKernelGGL((kv_kl<E, DH, DI, BS, LG>), dim3(grid), dim3(256), 0, s, a, k, log2g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long rows = (long)a.batch * a.h_kv * a.n_q;
@@ -253,11 +301,18 @@ hipError_t run_kl(const KvArgs &a, const KlArgs &k, int log2g, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename E, int DH, int DI, int BS>
+hipError_t kl_groups(const KvArgs &a, const KlArgs &k, int lg, hipStream_t s) {
+  if (lg == 0) return run_kl<E, DH, DI, BS, 0>(a, k, lg, s);
+  if (lg == 1) return run_kl<E, DH, DI, BS, 1>(a, k, lg, s);
+  return run_kl<E, DH, DI, BS, 2>(a, k, lg, s);
+}
+
 template <typename E, int DH>
 hipError_t kl_dims(const KvArgs &a, const KlArgs &k, int d_idx, int lg, hipStream_t s) {
   if (d_idx == 32)
-    return a.block_size == 32 ? run_kl<E, DH, 32, 32>(a, k, lg, s) : run_kl<E, DH, 32, 64>(a, k, lg, s);
-  return a.block_size == 32 ? run_kl<E, DH, 64, 32>(a, k, lg, s) : run_kl<E, DH, 64, 64>(a, k, lg, s);
+    return a.block_size == 32 ? kl_groups<E, DH, 32, 32>(a, k, lg, s) : kl_groups<E, DH, 32, 64>(a, k, lg, s);
+  return a.block_size == 32 ? kl_groups<E, DH, 64, 32>(a, k, lg, s) : kl_groups<E, DH, 64, 64>(a, k, lg, s);
 }
 
 }  // namespace
