@@ -88,6 +88,8 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   __shared__ __attribute__((aligned(16))) unsigned char s_k[BS * KROW];
   __shared__ __attribute__((aligned(16))) unsigned char s_ki[BS * IROW];
   __shared__ int32_t s_list[KV_CHUNK];
+  __shared__ float4 s_part[KV_CHUNK];  // the chunk's results, stored once per chunk: a store
+  __shared__ float2 s_ml[KV_CHUNK];    // per tile would be waited for with the next loads
 
   const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
   const int n_chunks = a.coff[NB];
@@ -120,19 +122,6 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
     stage_rows<E, DI, BS, IROW>(kip, kb, a.n_k, s_ki);
     __syncthreads();
 
-    F kf[KTN][DC], kif[KTN][DCI];
-#pragma unroll
-    for (int kt = 0; kt < KTN; ++kt) {
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        kf[kt][dc] = load_frag(reinterpret_cast<const E *>(s_k + (kt * 16 + c16) * KROW +
-                                                          (dc * 32 + g * 8) * ES));
-#pragma unroll
-      for (int dc = 0; dc < DCI; ++dc)
-        kif[kt][dc] = load_frag(reinterpret_cast<const E *>(s_ki + (kt * 16 + c16) * IROW +
-                                                           (dc * 32 + g * 8) * ES));
-    }
-
     const int n_tiles = (n_e + QPT - 1) / QPT;
     // The next tile's inputs load while this one computes: q and q_idx of the row-head
     // this lane feeds, and the LSE of its four accumulator row-heads. Loads are
@@ -164,16 +153,39 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
     load_tile(w, cur);
     for (int tt = w; tt < n_tiles; tt += 4) {
       load_tile(tt + 4, nxt);
+      // an opaque zero offset keeps the compiler from hoisting the fragment reads below
+      // out of the loop (kept in registers they would cost about a hundred VGPRs and a
+      // third of the resident waves)
+      int lds0 = 0;
+      pin(lds0);
+      // The KTN key tiles' products run as independent accumulation chains, one
+      // d-chunk at a time (a chunk's fragments of every key tile are read first), so that
+      // consecutive matrix-core operations do not wait on each other's results.
       f32x4 s[KTN], si[KTN];
 #pragma unroll
       for (int kt = 0; kt < KTN; ++kt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acci = {0.f, 0.f, 0.f, 0.f};
+        s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        si[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-        for (int dc = 0; dc < DC; ++dc) acc = mfma_chunk(cur.q[dc], kf[kt][dc], acc);
+      for (int dc = 0; dc < DC; ++dc) {
+        F kf[KTN];
 #pragma unroll
-        for (int dc = 0; dc < DCI; ++dc) acci = mfma_chunk(cur.qi[dc], kif[kt][dc], acci);
-        s[kt] = acc;
-        si[kt] = acci;
+        for (int kt = 0; kt < KTN; ++kt)
+          kf[kt] = load_frag(reinterpret_cast<const E *>(s_k + lds0 + (kt * 16 + c16) * KROW +
+                                                        (dc * 32 + g * 8) * ES));
+#pragma unroll
+        for (int kt = 0; kt < KTN; ++kt) s[kt] = mfma_chunk(cur.q[dc], kf[kt], s[kt]);
+      }
+#pragma unroll
+      for (int dc = 0; dc < DCI; ++dc) {
+        F kif[KTN];
+#pragma unroll
+        for (int kt = 0; kt < KTN; ++kt)
+          kif[kt] = load_frag(reinterpret_cast<const E *>(s_ki + lds0 + (kt * 16 + c16) * IROW +
+                                                         (dc * 32 + g * 8) * ES));
+#pragma unroll
+        for (int kt = 0; kt < KTN; ++kt) si[kt] = mfma_chunk(cur.qi[dc], kif[kt], si[kt]);
       }
       // per value slot: the key offset c16 of each tile is visible to its row iff <= lim
       int lim[4];
@@ -240,13 +252,18 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
         const int qm = (4 * g + ii) >> log2g;
         const int e = tt * QPT + qm;
         if (c16 == 0 && writer_g && e < n_e) {
-          const int ent = s_list[e];
-          const long ps = (((long)b * a.h_kv + r) * a.n_q + (ent >> 6)) * a.top_k + (ent & 63);
-          k.part[ps] = make_float4(ta, tb, tt_, 0.f);
-          k.part_ml[ps] = make_float2(M, zl);
+          s_part[e] = make_float4(ta, tb, tt_, 0.f);
+          s_ml[e] = make_float2(M, zl);
         }
       }
       cur = nxt;
+    }
+    __syncthreads();
+    for (int e = tid; e < n_e; e += 256) {
+      const int ent = s_list[e];
+      const long ps = (((long)b * a.h_kv + r) * a.n_q + (ent >> 6)) * a.top_k + (ent & 63);
+      k.part[ps] = s_part[e];
+      k.part_ml[ps] = s_ml[e];
     }
   }
 }
