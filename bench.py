@@ -4,8 +4,10 @@ Headline (``value``): causal prefill tokens/s at N = 131072 (32 query heads / 4 
 groups, d_h 128, index d_idx 64, blocks of 64, top_k 32, bf16): one step is the index
 branch (block scores, top-k) plus the sparse prefill attention over all 131072 rows.
 The same line carries the 1M-token decode result (batch 4, one new token each, same
-heads) under ``decode``, each with the roofline of its dominant kernel and the fp64
-oracle timed on a bounded sample on the host cores.
+heads) under ``decode``, and the index branch's alignment loss (msa_index_kl) on the
+prefill's selection under ``index_kl`` (timed apart from the step), each with the
+roofline of its dominant kernel and the fp64 oracle timed on a bounded sample on the
+host cores.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing starts. Kernel
 durations come from HIP events recorded on the stream the library launches on.
@@ -42,6 +44,16 @@ def prefill_work(w):
     index = float(w.batch * w.h_kv * np.sum(p + 1) * 2 * w.d_idx)
     main = float(w.batch * w.h_q * np.sum(t_p) * 4 * w.d_h)
     return index, main
+
+
+def kl_work(w):
+    """Algorithmic FLOPs of msa_index_kl: per (row, group) and selected visible token, the
+    G heads' q.k (2*d_h each) and the index score q_idx.k_idx (2*d_idx)."""
+    p = w.q_start + np.arange(w.n_q, dtype=np.int64)
+    b = p // w.block_size
+    t_p = (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
+    G = w.h_q // w.h_kv
+    return float(w.batch * w.h_kv * np.sum(t_p) * (2 * w.d_h * G + 2 * w.d_idx))
 
 
 def decode_work(w):
@@ -128,6 +140,21 @@ def time_step(w, inputs, steps, warmup, decode):
     torch.cuda.synchronize()
     times = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) * 1e-3
              for i, (name, _) in enumerate(stages)}
+    if not decode:
+        # the alignment loss of the same step (sel and lse from the last step above)
+        kl = torch.empty((w.batch, R, n), dtype=torch.float32, device="cuda")
+        kl_call = lambda: msa.msa_index_kl(s, inputs["q"], inputs["k"], inputs["q_idx"],
+                                           inputs["k_idx"], sel, lse, kl, None, ws_attn)
+        for _ in range(max(1, warmup)):
+            kl_call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(steps):
+            kl_call()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        times["index_kl"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
     return wall, times
 
 
@@ -150,6 +177,28 @@ def cpu_baseline_prefill(w, inputs, target_s=12.0, seed=0):
     return dict(value=n / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
                 sample=f"{n} query rows drawn uniformly (seed {seed}) from the {w.n_q}-row "
                        f"prefill, all {w.h_kv} groups and {w.h_q} heads; {dt:.1f} s")
+
+
+def cpu_baseline_kl(w, inputs, target_s=6.0, seed=1):
+    import oracle
+    orc = oracle.get()
+    cpu = {k: inputs[k].cpu() for k in ("q", "k", "q_idx", "k_idx")}
+    rng = np.random.default_rng(seed)
+    probe = np.sort(rng.choice(w.n_q, size=8, replace=False))
+    sel = orc.run(w, cpu, rows=probe, attention=False)["sel"]
+    t0 = time.perf_counter()
+    orc.kl(w, cpu, sel, rows=probe)
+    dt = time.perf_counter() - t0
+    n = int(min(w.n_q, max(8, 8 * target_s / max(dt, 1e-3))))
+    rows = np.sort(rng.choice(w.n_q, size=n, replace=False))
+    sel = orc.run(w, cpu, rows=rows, attention=False)["sel"]
+    t0 = time.perf_counter()
+    orc.kl(w, cpu, sel, rows=rows)
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+                sample=f"{n} query rows drawn uniformly (seed {seed}) from the {w.n_q}-row "
+                       f"prefill, all {w.h_kv} groups (loss only; their selections are "
+                       f"computed first and not timed); {dt:.1f} s")
 
 
 def cpu_baseline_decode(w, inputs, target_s=6.0):
@@ -258,12 +307,24 @@ def main():
                 per_launch_flops=dom["flops"], avg_launch_ms=t_dom * 1e3)
     path = dict(flops=f_index + f_main, tflops=(f_index + f_main) / wall / 1e12,
                 mfma_frac=(f_index + f_main) / wall / PEAK_BF16_FLOPS)
+    t_kl = kt.pop("index_kl")
     log(f"[bench] prefill {wall * 1e3:.2f} ms/step, kernels (ms): "
         + ", ".join(f"{k} {v * 1e3:.3f}" for k, v in kt.items()))
+    f_kl = kl_work(wp)
+    kl = dict(workload=wp.name, value=wp.batch * wp.n_q / t_kl, unit="tok/s",
+              ms_per_call=t_kl * 1e3,
+              roofline=dict(kernel="kv_kl", bound="mfma", achieved=f_kl / t_kl / 1e12,
+                            peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                            frac=f_kl / t_kl / PEAK_BF16_FLOPS,
+                            traffic=measured_traffic("kv_kl", wp.name),
+                            per_launch_flops=f_kl, avg_launch_ms=t_kl * 1e3))
+    log(f"[bench] alignment loss {t_kl * 1e3:.2f} ms/call")
     cpu_p = None
     if not args.no_cpu:
         log("[bench] oracle CPU baseline (prefill sample)")
         cpu_p = cpu_baseline_prefill(wp, inp)
+        log("[bench] oracle CPU baseline (alignment loss sample)")
+        kl["cpu_baseline"] = cpu_baseline_kl(wp, inp)
     del inp
     torch.cuda.empty_cache()
 
@@ -306,6 +367,7 @@ def main():
         "path_mfma": path,
         "kernel_ms": {k: v * 1e3 for k, v in kt.items()},
         "cpu_baseline": cpu_p,
+        "index_kl": kl,
         "decode": {
             "workload": wd.name, "value": wd.batch / dwall, "unit": "tok/s",
             "steps": args.decode_steps, "ms_per_step": dwall * 1e3,
