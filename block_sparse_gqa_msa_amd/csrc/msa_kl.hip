@@ -16,9 +16,9 @@
 //             matrix cores, the teacher weights t_j (the head mean), and per (row, slot)
 //             the block's sums A = sum t ln t, B = sum t S^idx, T = sum t and the index
 //             scores' (max, sum of 2^(z - max)) in log2 units.
-//   kl_merge  per (b, r, row): L = A - B + lse_idx * T with lse_idx = ln sum_j exp(S^idx_j)
-//             from the slots' (max, sum) pairs. (T is 1 up to the rounding of the forward's
-//             lse; the loss keeps it as computed.)
+//   kl_merge  per (b, r, row), one wave over the row's slots: L = A - B + lse_idx * T with
+//             lse_idx = ln sum_j exp(S^idx_j) from the slots' (max, sum) pairs. (T is 1 up
+//             to the rounding of the forward's lse; the loss keeps it as computed.)
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
@@ -268,29 +268,35 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   }
 }
 
-// One thread per (b, r, row): the row's slots in order.
+// One wave per (b, r, row), a lane per slot (top_k <= 64): the row's partials are read
+// as contiguous runs, then reduced across the wave.
 __global__ __launch_bounds__(256) void kl_merge(KvArgs a, KlArgs k) {
-  const long row = (long)blockIdx.x * 256 + threadIdx.x;  // (b, r, t)
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, r, t)
   if (row >= (long)a.batch * a.h_kv * a.n_q) return;
-  float A = 0.f, B = 0.f, T = 0.f, M = -INFINITY, L = 0.f;
-  for (int sl = 0; sl < a.top_k; ++sl) {
-    const int c = a.sel[row * a.top_k + sl];
-    if (c < 0 || c >= a.n_blocks) continue;
-    const float4 pa = k.part[row * a.top_k + sl];
-    const float2 ml = k.part_ml[row * a.top_k + sl];
-    A += pa.x;
-    B += pa.y;
-    T += pa.z;
-    if (ml.y > 0.f) {
-      const float Mn = fmaxf(M, ml.x);
-      L = (M == -INFINITY ? 0.f : L * __builtin_amdgcn_exp2f(M - Mn)) +
-          ml.y * __builtin_amdgcn_exp2f(ml.x - Mn);
-      M = Mn;
-    }
+  const int sl = threadIdx.x & 63;
+  const int slc = min(sl, a.top_k - 1);  // lanes past top_k read the last slot, unused
+  const int c = a.sel[row * a.top_k + slc];
+  const float4 pa = k.part[row * a.top_k + slc];
+  const float2 ml = k.part_ml[row * a.top_k + slc];
+  const bool use = sl < a.top_k && c >= 0 && c < a.n_blocks;
+  float A = use ? pa.x : 0.f, B = use ? pa.y : 0.f, T = use ? pa.z : 0.f;
+  const bool has = use && ml.y > 0.f;
+  float M = has ? ml.x : -INFINITY;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    A += __shfl_xor(A, o);
+    B += __shfl_xor(B, o);
+    T += __shfl_xor(T, o);
+    M = fmaxf(M, __shfl_xor(M, o));
   }
-  const float lse_idx = (M + __log2f(L)) * 0.69314718055994531f;
-  k.kl[row] = A - B + lse_idx * T;
-  if (k.lse_idx) k.lse_idx[row] = lse_idx;
+  float L = has ? ml.y * __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  if (sl == 0) {
+    const float lse_idx = (M + __log2f(L)) * 0.69314718055994531f;
+    k.kl[row] = A - B + lse_idx * T;
+    if (k.lse_idx) k.lse_idx[row] = lse_idx;
+  }
 }
 
 template <typename E, int DH, int DI, int BS, int LG>
@@ -314,7 +320,7 @@ hipError_t run_kl(const KvArgs &a, const KlArgs &k, int log2g, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long rows = (long)a.batch * a.h_kv * a.n_q;
-  hipLaunchKernelGGL(kl_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a, k);
+  hipLaunchKernelGGL(kl_merge, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a, k);
   return hipGetLastError();
 }
 
