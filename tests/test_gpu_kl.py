@@ -85,7 +85,37 @@ def test_kl_small_full_oracle(w):
     check(w, kl, lse_idx, ref, w.name)
 
 
-@pytest.mark.parametrize("name", ["prefill_8k", "prefill_128k"])
+def test_kl_kv_capacity_stride():
+    """Caches allocated longer than the valid length (kv_capacity > n_k): the loss reads K
+    and K_idx with the capacity stride; padding past n_k holds values that would change it."""
+    import oracle
+    for w in (W("kl_cap_prefill", n_q=200, n_k=400, q_start=200, top_k=4),
+              W("kl_cap_decode", batch=2, n_q=1, n_k=900, q_start=899, top_k=6)):
+        inp = generate(w, device="cuda")
+        cap = w.n_k + 136
+        big = dict(q=inp["q"], q_idx=inp["q_idx"])
+        for key in ("k", "v"):
+            x = torch.full((w.batch, w.h_kv, cap, w.d_h), 2.0, dtype=inp[key].dtype, device="cuda")
+            x[:, :, : w.n_k] = inp[key]
+            big[key] = x
+        x = torch.full((w.batch, cap, w.d_idx), 3.0, dtype=inp["k_idx"].dtype, device="cuda")
+        x[:, : w.n_k] = inp["k_idx"]
+        big["k_idx"] = x
+        s = msa.shape_of(w, kv_capacity=cap)
+        buf = msa.Buffers(s)
+        msa.msa_step(buf, big)
+        kl = torch.empty((w.batch, w.h_kv, w.n_q), device="cuda")
+        lse_idx = torch.empty_like(kl)
+        msa.msa_index_kl(s, big["q"], big["k"], big["q_idx"], big["k_idx"], buf.sel, buf.lse, kl,
+                         lse_idx, buf.ws_attn)
+        torch.cuda.synchronize()
+        cpu = to_cpu(inp)
+        sel = oracle.get().run(w, cpu, attention=False)["sel"]
+        assert np.array_equal(buf.sel.cpu().numpy(), sel)
+        check(w, kl, lse_idx, oracle.get().kl(w, cpu, sel), w.name)
+
+
+@pytest.mark.parametrize("name", ["prefill_8k", "prefill_128k", "chunk_1m"])
 def test_kl_workload_sampled_rows(name):
     """The prefill workloads at full size: every row's loss is finite and >= -atol, and
     sampled rows match the oracle."""
@@ -97,7 +127,7 @@ def test_kl_workload_sampled_rows(name):
     kl, lse_idx = gpu_kl(w, inp, buf)
     atol, _ = KL_TOL[w.dtype]
     assert torch.isfinite(kl).all() and kl.min().item() >= -atol
-    rows = sample_rows(w, n_random=24 if name == "prefill_128k" else 64)
+    rows = sample_rows(w, n_random=64 if name == "prefill_8k" else 24)
     cpu = to_cpu(inp)
     orc = oracle.get()
     ridx = torch.as_tensor(rows, device="cuda")
