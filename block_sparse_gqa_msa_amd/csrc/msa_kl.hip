@@ -131,6 +131,9 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
       F q[DC], qi[DCI];
       float lse[4];
     };
+    // Tile row of accumulator slot ii: the slots of one row are 1 << LG consecutive i, so
+    // for G >= 4 all four share row_slot(0) (written so the compiler sees it).
+    auto row_slot = [&](int ii) { return (4 * g + ((ii >> LG) << LG)) >> log2g; };
     auto row_of = [&](int tt, int qm) {  // s_list entry of row qm of tile tt, or entry 0
       const int e = tt * QPT + qm;
       return s_list[(tt < n_tiles && e < n_e) ? e : 0];
@@ -143,10 +146,11 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
       const E *srci = qx + (((long)b * a.h_kv + r) * a.n_q + t) * DI + g * 8;
 #pragma unroll
       for (int dc = 0; dc < DCI; ++dc) d.qi[dc] = load_frag(srci + dc * 32);
+      const int t0 = row_of(tt, row_slot(0)) >> 6;  // slot rows: one lookup per row
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int m = 4 * g + ii;
-        d.lse[ii] = lse_r[(long)(m & (G - 1)) * a.n_q + (row_of(tt, m >> log2g) >> 6)];
+        const int tr = ((ii >> LG) << LG) == 0 ? t0 : row_of(tt, row_slot(ii)) >> 6;
+        d.lse[ii] = lse_r[(long)((4 * g + ii) & (G - 1)) * a.n_q + tr];
       }
     };
     TileIn cur, nxt;
@@ -192,10 +196,14 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
       float lse2[4];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int qm = (4 * g + ii) >> log2g;
-        const bool valid = tt * QPT + qm < n_e;
-        const long p = (long)a.q_start + (row_of(tt, qm) >> 6);
-        lim[ii] = valid ? (int)min(p - kb, (long)BS - 1) : -1;
+        if (((ii >> LG) << LG) == ii) {  // first slot of its row
+          const int qm = row_slot(ii);
+          const bool valid = tt * QPT + qm < n_e;
+          const long p = (long)a.q_start + (row_of(tt, qm) >> 6);
+          lim[ii] = valid ? (int)min(p - kb, (long)BS - 1) : -1;
+        } else {
+          lim[ii] = lim[(ii >> LG) << LG];
+        }
         lse2[ii] = cur.lse[ii] * 1.44269504088896341f;
       }
       float sa[R4], sb[R4], st[R4], zm[R4];
@@ -232,7 +240,8 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
           const int ii = j << LG;
           const float t = hs[j] * inv_g;
           const float sidx = si[kt][ii] * k.scale_idx;  // S^idx, natural units
-          sa[j] += t > 0.f ? t * (__builtin_amdgcn_logf(t) * 0.69314718055994531f) : 0.f;
+          // t ln t, 0 at t = 0 (the clamp keeps the logarithm finite)
+          sa[j] += t * (__builtin_amdgcn_logf(fmaxf(t, 1e-30f)) * 0.69314718055994531f);
           sb[j] += t * sidx;
           st[j] += t;
           zm[j] = key <= lim[ii] ? fmaxf(zm[j], si[kt][ii] * ci) : zm[j];
@@ -249,8 +258,7 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
           zl += kt * 16 + c16 <= lim[ii] ? __builtin_amdgcn_exp2f(si[kt][ii] * ci - M) : 0.f;
         zl = sum16(zl);
         const float ta = sum16(sa[j]), tb = sum16(sb[j]), tt_ = sum16(st[j]);
-        const int qm = (4 * g + ii) >> log2g;
-        const int e = tt * QPT + qm;
+        const int e = tt * QPT + row_slot(ii);
         if (c16 == 0 && writer_g && e < n_e) {
           s_part[e] = make_float4(ta, tb, tt_, 0.f);
           s_ml[e] = make_float2(M, zl);
