@@ -41,6 +41,9 @@ class Oracle:
         g = self.lib.msa_oracle_kl
         g.argtypes = [i] * 11 + [p, p, p, p, i, p, p, p, p, i]
         g.restype = i
+        bw = self.lib.msa_oracle_attn_bwd
+        bw.argtypes = [i] * 10 + [p, p, p, p, p, p, p, p, i]
+        bw.restype = i
         self.lib.msa_oracle_max_threads.restype = i
 
     def max_threads(self) -> int:
@@ -116,6 +119,31 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"msa_oracle_kl failed with code {rc}")
         return dict(kl=kl, lse_idx=lse)
+
+
+    def attn_bwd(self, w, inputs: Dict, sel: np.ndarray, dout, n_threads: int = 0
+                 ) -> Dict[str, np.ndarray]:
+        """Gradients of the main branch for every row, given the selections ``sel``
+        [B, R, n_q, k] (held fixed) and the output gradient ``dout`` [B, H_q, n_q, d_h] in
+        the inputs' storage type: dq [B, H_q, n_q, d_h], dk and dv [B, R, n_k, d_h], float64."""
+        B, R, H, k = w.batch, w.h_kv, w.h_q, w.top_k
+        typ = 0 if w.dtype == "f32" else 1
+        arrs = {name: _as_numpy(inputs[name], typ) for name in ("q", "k", "v")}
+        do = _as_numpy(dout, typ)
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        if sel.shape != (B, R, w.n_q, k):
+            raise ValueError(f"sel has shape {sel.shape}, expected {(B, R, w.n_q, k)}")
+        dq = np.empty((B, H, w.n_q, w.d_h), np.float64)
+        dk = np.empty((B, R, w.n_k, w.d_h), np.float64)
+        dv = np.empty((B, R, w.n_k, w.d_h), np.float64)
+        rc = self.lib.msa_oracle_attn_bwd(
+            B, w.n_q, w.n_k, w.q_start, H, R, w.d_h, w.block_size, k, typ,
+            arrs["q"].ctypes.data, arrs["k"].ctypes.data, arrs["v"].ctypes.data,
+            sel.ctypes.data, do.ctypes.data, dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+            int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"msa_oracle_attn_bwd failed with code {rc}")
+        return dict(dq=dq, dk=dk, dv=dv)
 
 
 def _as_numpy(x, typ: int) -> np.ndarray:

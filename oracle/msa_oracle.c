@@ -16,7 +16,10 @@
  *     selection.
  * and, for msa_oracle_kl, section 训练 of the same page: the index branch's
  * distribution P^idx and the group-averaged main-branch distribution P^(r) over
- * the selected tokens, and the alignment loss L_KL = KL(P^(r) || P^idx).
+ * the selected tokens, and the alignment loss L_KL = KL(P^(r) || P^idx); and, for
+ * msa_oracle_attn_bwd, the gradients of the main-branch equation with respect to q,
+ * k and v for a given output gradient, the selection held fixed (the same section
+ * cuts the index branch's gradient from the main branch).
  *
  * Readings where the page is silent (each is listed with its reason in the
  * design notes):
@@ -394,6 +397,122 @@ int msa_oracle_kl(int batch, int n_q, int n_k, int q_start, int h_q, int h_kv, i
     free(sidx);
     free(zh);
     free(t);
+  }
+  return failed ? -2 : 0;
+}
+
+/*
+ * Gradient of the main branch for one (sequence, head, row) at position p, accumulated:
+ *   z_j = q . k_j / sqrt(d_h),  P = softmax_T(z),  O = sum_j P_j v_j  (T as for attend_row)
+ *   for an output gradient dO:  dv_j += P_j dO
+ *                               dP_j = dO . v_j,  dz_j = P_j (dP_j - sum_u P_u dP_u)
+ *                               dq   += sum_j dz_j k_j / sqrt(d_h)
+ *                               dk_j += dz_j q / sqrt(d_h)
+ * dq: d_h doubles for this (head, row); dk, dv: the group's planes [n_k, d_h].
+ */
+static void attend_row_bwd(const void *q_row, const void *k_plane, const void *v_plane,
+                           const void *do_row, int type, int d_h, int64_t p, int block_size,
+                           const int32_t *sel, int top_k, int64_t *key, double *z,
+                           double *dp, double *dq, double *dk, double *dv) {
+  const double scale = 1.0 / sqrt((double)d_h);
+  int64_t n = 0;
+  double mu = -INFINITY;
+  for (int i = 0; i < top_k; ++i) {
+    if (sel[i] < 0) continue;
+    int64_t lo = (int64_t)sel[i] * block_size, hi = lo + block_size;
+    if (hi > p + 1) hi = p + 1;
+    for (int64_t j = lo; j < hi; ++j) {
+      double s = 0.0;
+      for (int d = 0; d < d_h; ++d) s += elem(q_row, d, type) * elem(k_plane, j * d_h + d, type);
+      key[n] = j;
+      z[n] = s * scale;
+      if (z[n] > mu) mu = z[n];
+      ++n;
+    }
+  }
+  double total = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    z[j] = exp(z[j] - mu);
+    total += z[j];
+  }
+  double dsum = 0.0; /* sum_u P_u dP_u */
+  for (int64_t j = 0; j < n; ++j) {
+    z[j] /= total; /* P_j */
+    double s = 0.0;
+    for (int d = 0; d < d_h; ++d) s += elem(do_row, d, type) * elem(v_plane, key[j] * d_h + d, type);
+    dp[j] = s;
+    dsum += z[j] * s;
+  }
+  for (int64_t j = 0; j < n; ++j) {
+    const double dz = z[j] * (dp[j] - dsum);
+    for (int d = 0; d < d_h; ++d) {
+      dq[d] += dz * elem(k_plane, key[j] * d_h + d, type) * scale;
+      dk[key[j] * d_h + d] += dz * elem(q_row, d, type) * scale;
+      dv[key[j] * d_h + d] += z[j] * elem(do_row, d, type);
+    }
+  }
+}
+
+/*
+ * Main-branch gradients for every row of every sequence, given the selections.
+ *   q, k, v and sel as for msa_oracle_run (sel [B, H_kv, n_q, top_k], all rows);
+ *   dout [B, H_q, n_q, d_h] in the storage type of the inputs.
+ *   dq [B, H_q, n_q, d_h], dk and dv [B, H_kv, n_k, d_h]: double, overwritten.
+ * One task per (sequence, group): it owns that group's dk and dv planes.
+ * Returns 0, -1 on a bad argument, -2 when out of memory.
+ */
+int msa_oracle_attn_bwd(int batch, int n_q, int n_k, int q_start, int h_q, int h_kv, int d_h,
+                        int block_size, int top_k, int type, const void *q, const void *k,
+                        const void *v, const int32_t *sel, const void *dout, double *dq,
+                        double *dk, double *dv, int n_threads) {
+  if (batch < 1 || n_q < 1 || n_k < 1 || q_start < 0 || h_kv < 1 || h_q < h_kv ||
+      h_q % h_kv || d_h < 1 || block_size < 1 || top_k < 1 || (int64_t)q_start + n_q > n_k ||
+      !q || !k || !v || !sel || !dout || !dq || !dk || !dv ||
+      (type != ORACLE_F32 && type != ORACLE_BF16))
+    return -1;
+  const int group = h_q / h_kv;
+  const size_t es = (type == ORACLE_F32) ? 4 : 2;
+#ifdef _OPENMP
+  if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+  (void)n_threads;
+#endif
+  memset(dq, 0, sizeof(double) * (size_t)batch * h_q * n_q * d_h);
+  memset(dk, 0, sizeof(double) * (size_t)batch * h_kv * n_k * d_h);
+  memset(dv, 0, sizeof(double) * (size_t)batch * h_kv * n_k * d_h);
+  int failed = 0;
+  const int64_t max_t = (int64_t)top_k * block_size;
+#pragma omp parallel
+  {
+    int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)max_t);
+    double *z = (double *)malloc(sizeof(double) * (size_t)max_t);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)max_t);
+    if (!key || !z || !dp) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < (int64_t)batch * h_kv; ++task) {
+      if (failed) continue;
+      const int r = (int)(task % h_kv), b = (int)(task / h_kv);
+      const int64_t kv_off = ((int64_t)b * h_kv + r) * (int64_t)n_k * d_h;
+      const void *kp = (const char *)k + kv_off * (int64_t)es;
+      const void *vp = (const char *)v + kv_off * (int64_t)es;
+      for (int l = 0; l < group; ++l) {
+        const int h = r * group + l;
+        for (int t = 0; t < n_q; ++t) {
+          const int64_t row = ((int64_t)b * h_q + h) * n_q + t;
+          attend_row_bwd((const char *)q + row * d_h * (int64_t)es, kp, vp,
+                         (const char *)dout + row * d_h * (int64_t)es, type, d_h,
+                         (int64_t)q_start + t, block_size,
+                         sel + (((int64_t)b * h_kv + r) * n_q + t) * top_k, top_k, key, z, dp,
+                         dq + row * d_h, dk + kv_off, dv + kv_off);
+        }
+      }
+    }
+    free(key);
+    free(z);
+    free(dp);
   }
   return failed ? -2 : 0;
 }

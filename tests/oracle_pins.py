@@ -5,7 +5,8 @@ Definitions pinned (page "MiniMax-M3: MSA 技术报告速读", section 核心机
   index-branch token scores and causal block max-pool, the per-group TopK with
   the local block forced in, and the main-branch sparse softmax attention; and
   (section 训练) the index-branch distribution P^idx, the group-averaged teacher
-  P^(r) over the selected tokens and the alignment loss KL(P^(r) || P^idx).
+  P^(r) over the selected tokens and the alignment loss KL(P^(r) || P^idx); and the
+  gradients of the main-branch equation for a fixed selection.
 
 Each pin takes an ``oracle.Oracle`` and raises AssertionError on a mismatch, so
 the same pins also run against deliberately broken oracle builds.
@@ -364,8 +365,64 @@ def pin_kl_dense_scipy(orc):
     assert out["kl"].min() >= -1e-15
 
 
+# ----------------------------------------------------------------- main-branch gradient pins
+
+def pin_bwd_autograd(orc):
+    """General sparse selections: dq, dk, dv equal torch autograd (fp64) through SDPA under
+    the selection's token mask, GQA by repeating K/V over each group's heads."""
+    for kw in (dict(batch=2, h_q=8, h_kv=2, n_q=40, n_k=40, d_h=8, d_idx=4, block_size=4,
+                    top_k=3),
+               dict(batch=1, h_q=6, h_kv=3, n_q=21, n_k=61, q_start=40, d_h=5, d_idx=3,
+                    block_size=8, top_k=4)):
+        w = shape(**kw)
+        inp = rand_inputs(w, seed=31, idx_values=(-3, 4))
+        g = torch.Generator().manual_seed(32)
+        dout = torch.randn(w.batch, w.h_q, w.n_q, w.d_h, generator=g)
+        sel = orc.run(w, inp, attention=False)["sel"]
+        got = orc.attn_bwd(w, inp, sel, dout)
+        G = w.h_q // w.h_kv
+        q = inp["q"].double().requires_grad_()
+        k = inp["k"].double().requires_grad_()
+        v = inp["v"].double().requires_grad_()
+        m = torch.from_numpy(visible_token_mask(w, sel)).repeat_interleave(G, dim=1)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q, k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1), attn_mask=m)
+        (o * dout.double()).sum().backward()
+        for name, ref in (("dq", q.grad), ("dk", k.grad), ("dv", v.grad)):
+            assert np.allclose(got[name], ref.numpy(), rtol=0, atol=1e-12), name
+
+
+def pin_bwd_finite_difference(orc):
+    """Central differences of L = sum(dout * O) through the (pinned) forward oracle, for a
+    spread of q, k and v coordinates; the selection does not depend on them."""
+    w = shape(batch=1, h_q=4, h_kv=2, n_q=12, n_k=12, d_h=3, d_idx=2, block_size=2, top_k=3)
+    inp = rand_inputs(w, seed=41, idx_values=(-2, 3))
+    g = torch.Generator().manual_seed(42)
+    dout = torch.randn(w.batch, w.h_q, w.n_q, w.d_h, generator=g)
+    sel = orc.run(w, inp, attention=False)["sel"]
+    got = orc.attn_bwd(w, inp, sel, dout)
+    eps = 2.0 ** -10  # x +- eps is exact in fp32 for these magnitudes
+    rng = np.random.default_rng(43)
+
+    def loss(x):
+        return float((orc.run(w, x)["o"] * dout.double().numpy()).sum())
+
+    for name, grad in (("q", "dq"), ("k", "dk"), ("v", "dv")):
+        shp = tuple(inp[name].shape)
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in shp)
+            plus = dict(inp)
+            minus = dict(inp)
+            plus[name] = inp[name].clone()
+            minus[name] = inp[name].clone()
+            plus[name][idx] += eps
+            minus[name][idx] -= eps
+            fd = (loss(plus) - loss(minus)) / (2 * eps)
+            assert abs(fd - got[grad][idx]) < 2e-5 * (1 + abs(fd)), (name, idx, fd, got[grad][idx])
+
+
 PINS = [pin_block_scores_exact, pin_topk_bruteforce, pin_dense_when_k_covers,
         pin_local_block_only, pin_token_level, pin_zero_query_closed_form,
         pin_group_map_and_ones, pin_entry_point_consistency, pin_bf16_storage_widening,
         pin_general_sparse, pin_kl_two_tokens_closed_form, pin_kl_student_equals_teacher,
-        pin_kl_uniform_teacher, pin_kl_dense_scipy]
+        pin_kl_uniform_teacher, pin_kl_dense_scipy, pin_bwd_autograd, pin_bwd_finite_difference]

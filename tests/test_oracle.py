@@ -87,6 +87,16 @@ MUTANTS = [
                                                     "(((int64_t)b * h_q + (int64_t)r) * n_q + tq) * d_h")]),
     ("teacher head stride of one row", [("(const char *)q + q_off * (int64_t)es, (int64_t)n_q * d_h,",
                                          "(const char *)q + q_off * (int64_t)es, (int64_t)d_h,")]),
+    ("gradient without the softmax's D term", [("const double dz = z[j] * (dp[j] - dsum);",
+                                                "const double dz = z[j] * dp[j];")]),
+    ("dk without 1/sqrt(d_h)", [("dk[key[j] * d_h + d] += dz * elem(q_row, d, type) * scale;",
+                                 "dk[key[j] * d_h + d] += dz * elem(q_row, d, type);")]),
+    ("dv weighted by dP instead of P", [("dv[key[j] * d_h + d] += z[j] * elem(do_row, d, type);",
+                                         "dv[key[j] * d_h + d] += dp[j] * elem(do_row, d, type);")]),
+    ("dq from v instead of k", [("dq[d] += dz * elem(k_plane, key[j] * d_h + d, type) * scale;",
+                                 "dq[d] += dz * elem(v_plane, key[j] * d_h + d, type) * scale;")]),
+    ("gradients land in the next group's planes", [("const int64_t kv_off = ((int64_t)b * h_kv + r) * (int64_t)n_k * d_h;\n      const void *kp",
+                                                    "const int64_t kv_off = ((int64_t)b * h_kv + (r + 1) % h_kv) * (int64_t)n_k * d_h;\n      const void *kp")]),
     ("query position ignores q_start", [("const int64_t t = rows[i], p = (int64_t)q_start + t;\n      const int64_t qoff = (((int64_t)b * h_kv",
                                          "const int64_t t = rows[i], p = t;\n      const int64_t qoff = (((int64_t)b * h_kv")]),
 ]
