@@ -24,6 +24,7 @@ EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_s
            "msa_sparse_attn_workspace_size", "msa_sparse_attn_prefill",
            "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_partials",
            "msa_sparse_attn_prefill_merge", "msa_sparse_attn_decode", "msa_index_kl",
+           "msa_sparse_attn_backward_workspace_size", "msa_sparse_attn_backward",
            "msa_last_error", "msa_abi_version")
 
 
@@ -73,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_prefill_merge.argtypes = [S, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_decode.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_index_kl.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_sparse_attn_backward_workspace_size.argtypes = [S, sz]
+    lib.msa_sparse_attn_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     for f in EXPORTS:
         if f == "msa_last_error":
             continue
@@ -256,6 +259,25 @@ def msa_index_kl(shape: MsaShape, q, k, q_idx, k_idx, sel, lse, kl, lse_idx=None
         _ptr(k_idx, et, "k_idx"), _ptr(sel, torch.int32, "sel"), _ptr(lse, torch.float32, "lse"),
         _ptr(kl, torch.float32, "kl"), _ptr(lse_idx, torch.float32, "lse_idx"), wp, wn,
         _stream(stream, kl)))
+
+
+def msa_sparse_attn_backward_workspace_size(shape: MsaShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_sparse_attn_backward_workspace_size(ctypes.byref(shape),
+                                                                  ctypes.byref(n)))
+    return int(n.value)
+
+
+def msa_sparse_attn_backward(shape: MsaShape, q, k, v, sel, o, lse, dout, dq, dk, dv,
+                             workspace=None, stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_sparse_attn_backward(
+        ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k, et, "k"), _ptr(v, et, "v"),
+        _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"), _ptr(lse, torch.float32, "lse"),
+        _ptr(dout, et, "dout"), _ptr(dq, et, "dq"), _ptr(dk, et, "dk"), _ptr(dv, et, "dv"),
+        wp, wn, _stream(stream, dq)))
 
 
 # ----------------------------------------------------------------- allocation helpers

@@ -437,6 +437,54 @@ int msa_index_kl(const msa_shape *shape, const void *q, const void *k, const voi
   return ok();
 }
 
+static size_t attn_backward_ws(const msa_shape &s, msa::BwdLayout *lay) {
+  return msa::kv_bwd_workspace_bytes(s.batch, s.h_kv, s.n_q, s.top_k, n_blocks(s), s.h_q / s.h_kv,
+                                     s.d_h, s.block_size, s.dtype == MSA_F32 ? 4 : 2, lay);
+}
+
+int msa_sparse_attn_backward_workspace_size(const msa_shape *shape, size_t *bytes) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_attn_dims(*shape))) return rc;
+  if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (empty(*shape)) {
+    *bytes = 0;
+    return ok();
+  }
+  if ((rc = check_prefill_limits(*shape))) return rc;
+  *bytes = attn_backward_ws(*shape, nullptr);
+  return ok();
+}
+
+int msa_sparse_attn_backward(const msa_shape *shape, const void *q, const void *k, const void *v,
+                             const int32_t *sel, const void *o, const float *lse, const void *dout,
+                             void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if (empty(s)) return empty_attn_call(s);
+  if (!q || !k || !v || !sel || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(MSA_ERR_INVALID_ARG, "q, k, v, sel, o, lse, dout, dq, dk and dv must be non-NULL");
+  if ((rc = check_attn_dims(s))) return rc;
+  if ((rc = check_prefill_limits(s))) return rc;
+  msa::BwdLayout lay;
+  const size_t need = attn_backward_ws(s, &lay);
+  if (!workspace || workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  msa::KvArgs a;
+  // the lists live at the start of the backward workspace, laid out as for the prefill
+  if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
+  a.q = q; a.k = k; a.v = v; a.sel = sel;
+  if ((rc = run_prefill(s, a, msa::KV_STAGE_PLAN, stream))) return rc;
+  hipError_t e = msa::launch_attn_backward(a, lay, reinterpret_cast<unsigned char *>(workspace), o, dout,
+                                           lse, dq, dk, dv, s.dtype, s.d_h,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return ok();
+}
+
 int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_cache,
                            const void *v_cache, const int32_t *sel, void *o, float *lse,
                            void *workspace, size_t workspace_bytes, void *stream) {

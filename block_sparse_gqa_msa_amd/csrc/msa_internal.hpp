@@ -92,6 +92,17 @@ int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long group, lon
 size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
                           long d_h, long elem_bytes, KvLayout *lay);
 
+// Backward workspace: the prefill lists (KvLayout; part_o holds the dq partials), D per
+// (b, h, t), and one fp32 dK/dV partial per (run, list) segment of the backward kernel.
+struct BwdLayout {
+  KvLayout kv;
+  size_t dsum, dkv, total;
+  int run;        // chunks per run
+  long max_runs;  // runs at most (segment slots [0, max_runs) start runs; list i's own is max_runs + i)
+};
+size_t kv_bwd_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
+                              long d_h, long block_size, long elem_bytes, BwdLayout *lay);
+
 constexpr int TOPK_CHUNK = 2048;  // candidate blocks one wave ranks at a time
 
 // Each launcher validates nothing (the C-ABI layer did) and returns the launch status.
@@ -111,5 +122,11 @@ hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t
 // Alignment loss from the lists a plan stage built: per-selection sums, then the merge.
 hipError_t launch_index_kl(const KvArgs &a, const KlArgs &k, int dtype, int d_h, int d_idx,
                            hipStream_t s);
+
+// Main-branch gradients for a fixed selection: lists (plan stage), D, per-block gradients,
+// then the dq merge and the dk/dv reduction.
+hipError_t launch_attn_backward(const KvArgs &a, const BwdLayout &lay, unsigned char *ws, const void *o,
+                                const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                int dtype, int d_h, hipStream_t s);
 
 }  // namespace msa

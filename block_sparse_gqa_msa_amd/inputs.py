@@ -134,3 +134,20 @@ def generate(w: Workload, device="cpu", seed: Optional[int] = None) -> Dict[str,
                 lo, hi = c * w.block_size, min((c + 1) * w.block_size, w.n_k)
                 k_idx[b, lo:hi] += 2
     return dict(q=q, k=k, v=v, q_idx=q_idx, k_idx=k_idx, needles=needles)
+
+
+def generate_dout(w: Workload, device="cpu", seed: Optional[int] = None) -> torch.Tensor:
+    """The output gradient for the backward of workload ``w``: [B, H_q, n_q, d_h] Gaussian
+    scaled like q (fp32 draw rounded once to the storage type), from its own stream
+    (seed + 1 unless ``seed`` is given)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed((w.seed + 1) if seed is None else seed)
+    out = torch.empty((w.batch, w.h_q, w.n_q, w.d_h), dtype=torch_dtype(w), device=device)
+    for b in range(w.batch):
+        x = torch.randn((w.h_q, w.n_q, w.d_h), generator=gen, device=device, dtype=torch.float32)
+        if w.qkv_scale != 1.0:
+            x.mul_(w.qkv_scale)
+        out[b].copy_(x)
+        del x
+    return out

@@ -204,6 +204,42 @@ int msa_index_kl(const msa_shape *shape, const void *q, const void *k, const voi
                  const void *k_idx, const int32_t *sel, const float *lse, float *kl,
                  float *lse_idx, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Workspace bytes msa_sparse_attn_backward needs for `shape`: the per-block query lists,
+ * one partial dq per (row, group, selected block, head) (about batch * h_kv * n_q *
+ * top_k * (h_q / h_kv) * d_h * sizeof(dtype) bytes, as for the prefill), D per (b, h, t)
+ * and the fp32 dk/dv partials of the per-block pass. Returns MSA_OK and writes *bytes.
+ */
+int msa_sparse_attn_backward_workspace_size(const msa_shape *shape, size_t *bytes);
+/*
+ * Gradients of the main branch ("MiniMax-M3: MSA 技术报告速读", section 核心机制 for the
+ * forward; section 训练 detaches the index branch, so sel is a constant here) with respect
+ * to q, k and v, for the forward msa_sparse_attn_prefill computes on the same shape. For
+ * each head h of group r and row t, over T = the visible tokens of the blocks in
+ * sel[b, r, t, :], with P_j = exp(q . k_j / sqrt(d_h) - lse), dP_j = dout . v_j and
+ * D = dout . o:
+ *   dq      = sum_j P_j (dP_j - D) k_j / sqrt(d_h)
+ *   dk_j   += P_j (dP_j - D) q / sqrt(d_h)     summed over every (row, head) whose T holds j
+ *   dv_j   += P_j dout                         likewise
+ *   q, k, v, sel  the forward's inputs (layouts above)
+ *   o, lse   the forward's outputs for them (lse: natural log, as msa_sparse_attn_prefill
+ *            writes it)
+ *   dout     [batch, h_q, n_q, d_h], dtype of q: the gradient of the loss with respect to o
+ *   dq       out [batch, h_q, n_q, d_h], dtype of q
+ *   dk, dv   out [batch, h_kv, kv_capacity, d_h], dtype of q: rows 0..n_k-1 are written
+ *            (zero for keys no row of the call sees); rows from n_k on are not touched
+ *   workspace at least msa_sparse_attn_backward_workspace_size bytes.
+ * Computed KV-block-outer over the same per-block row lists as the prefill: each staged
+ * block yields its dk, dv rows and one partial dq per selection, then the dq partials are
+ * summed per row and the block partials per block, in fixed orders (no float atomics).
+ * dk and dv sum each chunk of a block's rows in list order, which the list build sets
+ * with integer atomics, so they can differ in the last bits between calls; dq does not.
+ * Supported set and size limits as for msa_sparse_attn_prefill.
+ */
+int msa_sparse_attn_backward(const msa_shape *shape, const void *q, const void *k, const void *v,
+                             const int32_t *sel, const void *o, const float *lse, const void *dout,
+                             void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                             void *stream);
 /* Text of the last error on the calling thread (empty after a successful call). */
 const char *msa_last_error(void);
 

@@ -222,3 +222,36 @@ def test_index_kl_rejects(lib):
             == msa.MSA_ERR_UNSUPPORTED
     e = good(n_q=0)
     assert lib.msa_index_kl(ctypes.byref(e), *([None] * 8), None, 0, None) == msa.MSA_OK
+
+
+def test_backward_rejects(lib):
+    dummy = 1 << 20
+    s = good()
+    need = msa.msa_sparse_attn_backward_workspace_size(s)
+    # at least the prefill's lists and partials, D and one fp32 dk/dv partial per list
+    assert need > msa.msa_sparse_attn_workspace_size(s)
+    sb = ctypes.byref(s)
+    args = [dummy] * 10  # q, k, v, sel, o, lse, dout, dq, dk, dv
+    for i in range(10):
+        a = list(args)
+        a[i] = None
+        assert lib.msa_sparse_attn_backward(sb, *a, dummy, need, None) == msa.MSA_ERR_INVALID_ARG
+        assert "non-NULL" in msa.msa_last_error()
+    assert lib.msa_sparse_attn_backward(sb, *args, dummy, need - 1, None) == msa.MSA_ERR_WORKSPACE
+    assert lib.msa_sparse_attn_backward(sb, *args, None, need, None) == msa.MSA_ERR_WORKSPACE
+    for bad, code in ((dict(d_h=96), msa.MSA_ERR_UNSUPPORTED),
+                      (dict(block_size=16), msa.MSA_ERR_UNSUPPORTED),
+                      (dict(h_q=12), msa.MSA_ERR_UNSUPPORTED),
+                      (dict(h_q=30), msa.MSA_ERR_INVALID_ARG),
+                      (dict(q_start=10), msa.MSA_ERR_INVALID_ARG)):
+        x = good(**bad)
+        assert lib.msa_sparse_attn_backward(ctypes.byref(x), *args, dummy, need, None) == code
+    n = ctypes.c_size_t()
+    assert lib.msa_sparse_attn_backward_workspace_size(sb, None) == msa.MSA_ERR_INVALID_ARG
+    assert lib.msa_sparse_attn_backward_workspace_size(None, ctypes.byref(n)) \
+        == msa.MSA_ERR_INVALID_ARG
+    for kw in (dict(batch=0), dict(n_q=0)):
+        e = good(**kw)
+        assert msa.msa_sparse_attn_backward_workspace_size(e) == 0
+        assert lib.msa_sparse_attn_backward(ctypes.byref(e), *([None] * 10), None, 0, None) \
+            == msa.MSA_OK
