@@ -5,7 +5,8 @@ groups, d_h 128, index d_idx 64, blocks of 64, top_k 32, bf16): one step is the 
 branch (block scores, top-k) plus the sparse prefill attention over all 131072 rows.
 The same line carries the 1M-token decode result (batch 4, one new token each, same
 heads) under ``decode``, and the index branch's alignment loss (msa_index_kl) on the
-prefill's selection under ``index_kl`` (timed apart from the step), each with the
+prefill's selection under ``index_kl`` and the main branch's backward (dq, dk, dv for
+that selection) under ``attn_backward`` (both timed apart from the step), each with the
 roofline of its dominant kernel and the fp64 oracle timed on a bounded sample on the
 host cores.
 
@@ -54,6 +55,16 @@ def kl_work(w):
     t_p = (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
     G = w.h_q // w.h_kv
     return float(w.batch * w.h_kv * np.sum(t_p) * (2 * w.d_h * G + 2 * w.d_idx))
+
+
+def bwd_work(w):
+    """Algorithmic FLOPs of msa_sparse_attn_backward: per (row, head) and selected visible
+    token, q.k (recomputed), dout.v, and the three products that give dv, dk and dq
+    (2*d_h each)."""
+    p = w.q_start + np.arange(w.n_q, dtype=np.int64)
+    b = p // w.block_size
+    t_p = (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
+    return float(w.batch * w.h_q * np.sum(t_p) * 10 * w.d_h)
 
 
 def decode_work(w):
@@ -155,6 +166,27 @@ def time_step(w, inputs, steps, warmup, decode):
         ev[1].record(stream)
         torch.cuda.synchronize()
         times["index_kl"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+        del kl
+        # the main branch's backward for the same selection, o and lse
+        from block_sparse_gqa_msa_amd.inputs import generate_dout
+        dout = generate_dout(w, device="cuda")
+        dq = torch.empty_like(inputs["q"])
+        dk = torch.empty_like(inputs["k"])
+        dv = torch.empty_like(inputs["v"])
+        ws_bwd = torch.empty(msa.msa_sparse_attn_backward_workspace_size(s), dtype=torch.uint8,
+                             device="cuda")
+        bwd_call = lambda: msa.msa_sparse_attn_backward(s, inputs["q"], inputs["k"], inputs["v"],
+                                                        sel, o, lse, dout, dq, dk, dv, ws_bwd)
+        for _ in range(max(1, warmup)):
+            bwd_call()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(steps):
+            bwd_call()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        times["attn_backward"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+        del dout, dq, dk, dv, ws_bwd
     return wall, times
 
 
@@ -199,6 +231,37 @@ def cpu_baseline_kl(w, inputs, target_s=6.0, seed=1):
                 sample=f"{n} query rows drawn uniformly (seed {seed}) from the {w.n_q}-row "
                        f"prefill, all {w.h_kv} groups (loss only; their selections are "
                        f"computed first and not timed); {dt:.1f} s")
+
+
+def cpu_baseline_bwd(w, inputs, target_s=12.0):
+    """The oracle's backward on the last m rows of the prefill (their selections computed
+    first, untimed), m sized for about target_s seconds."""
+    import oracle
+    from block_sparse_gqa_msa_amd.inputs import generate_dout
+    orc = oracle.get()
+    dout_all = generate_dout(w, device="cuda")
+
+    def sub(m):
+        ws = w.replace(n_q=m, q_start=w.q_start + w.n_q - m)
+        cpu = {k: inputs[k].cpu() for k in ("k", "v", "k_idx")}
+        cpu["q"] = inputs["q"][:, :, -m:].cpu()
+        cpu["q_idx"] = inputs["q_idx"][:, :, -m:].cpu()
+        sel = orc.run(ws, cpu, attention=False)["sel"]
+        return ws, cpu, sel, dout_all[:, :, -m:].cpu()
+
+    ws, cpu, sel, do = sub(32)
+    t0 = time.perf_counter()
+    orc.attn_bwd(ws, cpu, sel, do)
+    dt = time.perf_counter() - t0
+    m = int(min(w.n_q, max(32, 32 * target_s / max(dt, 1e-3))))
+    ws, cpu, sel, do = sub(m)
+    t0 = time.perf_counter()
+    orc.attn_bwd(ws, cpu, sel, do)
+    dt = time.perf_counter() - t0
+    return dict(value=m / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+                sample=f"the last {m} rows of the {w.n_q}-row prefill, all {w.h_kv} groups and "
+                       f"{w.h_q} heads (dq of those rows, their dk and dv contributions; "
+                       f"selections computed first and not timed); {dt:.1f} s")
 
 
 def cpu_baseline_decode(w, inputs, target_s=6.0):
@@ -319,12 +382,24 @@ def main():
                             traffic=measured_traffic("kv_kl", wp.name),
                             per_launch_flops=f_kl, avg_launch_ms=t_kl * 1e3))
     log(f"[bench] alignment loss {t_kl * 1e3:.2f} ms/call")
+    t_bwd = kt.pop("attn_backward")
+    f_bwd = bwd_work(wp)
+    bwd = dict(workload=wp.name, value=wp.batch * wp.n_q / t_bwd, unit="tok/s",
+               ms_per_call=t_bwd * 1e3,
+               roofline=dict(kernel="kv_bwd", bound="mfma", achieved=f_bwd / t_bwd / 1e12,
+                             peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                             frac=f_bwd / t_bwd / PEAK_BF16_FLOPS,
+                             traffic=measured_traffic("kv_bwd", wp.name),
+                             per_launch_flops=f_bwd, avg_launch_ms=t_bwd * 1e3))
+    log(f"[bench] attention backward {t_bwd * 1e3:.2f} ms/call")
     cpu_p = None
     if not args.no_cpu:
         log("[bench] oracle CPU baseline (prefill sample)")
         cpu_p = cpu_baseline_prefill(wp, inp)
         log("[bench] oracle CPU baseline (alignment loss sample)")
         kl["cpu_baseline"] = cpu_baseline_kl(wp, inp)
+        log("[bench] oracle CPU baseline (backward sample)")
+        bwd["cpu_baseline"] = cpu_baseline_bwd(wp, inp)
     del inp
     torch.cuda.empty_cache()
 
@@ -368,6 +443,7 @@ def main():
         "kernel_ms": {k: v * 1e3 for k, v in kt.items()},
         "cpu_baseline": cpu_p,
         "index_kl": kl,
+        "attn_backward": bwd,
         "decode": {
             "workload": wd.name, "value": wd.batch / dwall, "unit": "tok/s",
             "steps": args.decode_steps, "ms_per_step": dwall * 1e3,

@@ -86,7 +86,7 @@ struct BwdLds {
   static constexpr int DSL = DH / NW;                // dq columns per wave
   static constexpr int PE = 16 / ES;                 // elements per 16-byte piece
   static constexpr int QROW = DH * ES + 16;          // Q, dO row-major rows
-  static constexpr int TROW = TR * ES + (ES == 2 ? 8 : 16);  // Q^T, dO^T rows (one per d)
+  static constexpr int TROW = TR * ES + 16;         // Q^T, dO^T rows (one per d)
   static constexpr int SROW = BS * ES + 16;          // dS rows, K^T rows
   static constexpr int OROW = DSL * ES + 16;         // per-wave dq staging rows
   static constexpr int NTASK = 16 * (DH / PE);       // (row pair, piece) tasks per tensor
@@ -94,15 +94,22 @@ struct BwdLds {
   static_assert(NT == 4 * BS && 2 * NTASK % NT == 0, "staging tasks must divide evenly");
 };
 
+// bf16 transposed staging rows hold 16 dwords of row-head pairs; the dword of pair p in row
+// d is p ^ tr_swz(d). The XOR (even, so 4-row-head units stay whole) spreads the staging
+// writes, whose lanes step d by 8, over the banks, while the fragment reads, whose lanes
+// step d by 1 within a 16-row tile, see one swizzle per instruction.
+__device__ __forceinline__ int tr_swz(int d) { return 2 * ((d >> 4) & 7); }
+
 // The 8 K-elements of a 32-wide chunk whose A side comes from two accumulator tiles:
 // row-heads 4g + 0..3 of the first, then 4g + 0..3 of the second (16 + 4g + 0..3), read
-// from a transposed staging row.
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *row, int g, const bf16_t *) {
-  const u32x2 lo = *reinterpret_cast<const u32x2 *>(row + (4 * g) * 2);
-  const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + (16 + 4 * g) * 2);
+// from transposed staging row d.
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *row, int d, int g, const bf16_t *) {
+  const int sw = tr_swz(d);
+  const u32x2 lo = *reinterpret_cast<const u32x2 *>(row + ((2 * g) ^ sw) * 4);
+  const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + ((8 + 2 * g) ^ sw) * 4);
   return __builtin_bit_cast(bf16x8, (u32x4{lo[0], lo[1], hi[0], hi[1]}));
 }
-__device__ __forceinline__ f32x8 tr_frag(const unsigned char *row, int g, const float *) {
+__device__ __forceinline__ f32x8 tr_frag(const unsigned char *row, int, int g, const float *) {
   const f32x4 lo = *reinterpret_cast<const f32x4 *>(row + (4 * g) * 4);
   const f32x4 hi = *reinterpret_cast<const f32x4 *>(row + (16 + 4 * g) * 4);
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -332,8 +339,9 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t x = px[j][0][e], y = px[j][1][e];
-              *reinterpret_cast<uint32_t *>(tr + (dg * 8 + 2 * e) * L::TROW + p * 4) = (x & 0xffffu) | (y << 16);
-              *reinterpret_cast<uint32_t *>(tr + (dg * 8 + 2 * e + 1) * L::TROW + p * 4) = (x >> 16) | (y & 0xffff0000u);
+              const int d = dg * 8 + 2 * e, col = (p ^ tr_swz(d)) * 4;  // d and d + 1 share it
+              *reinterpret_cast<uint32_t *>(tr + d * L::TROW + col) = (x & 0xffffu) | (y << 16);
+              *reinterpret_cast<uint32_t *>(tr + (d + 1) * L::TROW + col) = (x >> 16) | (y & 0xffff0000u);
             }
           } else {
 #pragma unroll
@@ -390,8 +398,9 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
           const F as = acc_frag(dp[0], dp[1], tagp);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            dv[dt] = mfma_chunk(ap, tr_frag(s_dot + (dt * 16 + c16) * L::TROW, g, tagp), dv[dt]);
-            dk[dt] = mfma_chunk(as, tr_frag(s_qt + (dt * 16 + c16) * L::TROW, g, tagp), dk[dt]);
+            const int d = dt * 16 + c16;
+            dv[dt] = mfma_chunk(ap, tr_frag(s_dot + d * L::TROW, d, g, tagp), dv[dt]);
+            dk[dt] = mfma_chunk(as, tr_frag(s_qt + d * L::TROW, d, g, tagp), dk[dt]);
           }
         }
         // dS (as the matrix cores take it) to LDS for the dq product
