@@ -44,6 +44,9 @@ class Oracle:
         bw = self.lib.msa_oracle_attn_bwd
         bw.argtypes = [i] * 10 + [p, p, p, p, p, p, p, p, i]
         bw.restype = i
+        pj = self.lib.msa_oracle_project
+        pj.argtypes = [i] * 6 + [p, p, p, p, p, i]
+        pj.restype = i
         self.lib.msa_oracle_max_threads.restype = i
 
     def max_threads(self) -> int:
@@ -144,6 +147,35 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"msa_oracle_attn_bwd failed with code {rc}")
         return dict(dq=dq, dk=dk, dv=dv)
+
+
+    def project(self, x, w_q, w_k, h_kv: int, d_idx: int, n_threads: int = 0
+                ) -> Dict[str, np.ndarray]:
+        """The index branch's projections of hidden states ``x`` [B, n, d_model]:
+        q_idx [B, h_kv, n, d_idx] = per group r, x w_q[r*d_idx:(r+1)*d_idx]^T, and
+        k_idx [B, n, d_idx] = x w_k^T, float64. ``w_q`` [h_kv*d_idx, d_model] and ``w_k``
+        [d_idx, d_model] share the storage type of ``x`` (fp32, or bf16 passed as raw bits)."""
+        typ = 1 if _is_bf16(x) else 0
+        xs, wq, wk = (_as_numpy(a, typ) for a in (x, w_q, w_k))
+        B, n, dm = xs.shape
+        if wq.shape != (h_kv * d_idx, dm) or wk.shape != (d_idx, dm):
+            raise ValueError(f"weights {wq.shape}, {wk.shape} do not match x {xs.shape}")
+        q = np.empty((B, h_kv, n, d_idx), np.float64)
+        k = np.empty((B, n, d_idx), np.float64)
+        rc = self.lib.msa_oracle_project(B, n, dm, h_kv, d_idx, typ, xs.ctypes.data,
+                                         wq.ctypes.data, wk.ctypes.data, q.ctypes.data,
+                                         k.ctypes.data, int(n_threads))
+        if rc != 0:
+            raise RuntimeError(f"msa_oracle_project failed with code {rc}")
+        return dict(q_idx=q, k_idx=k)
+
+
+def _is_bf16(x) -> bool:
+    try:
+        import torch
+        return isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16
+    except ImportError:
+        return False
 
 
 def _as_numpy(x, typ: int) -> np.ndarray:

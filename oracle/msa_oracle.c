@@ -19,7 +19,9 @@
  * the selected tokens, and the alignment loss L_KL = KL(P^(r) || P^idx); and, for
  * msa_oracle_attn_bwd, the gradients of the main-branch equation with respect to q,
  * k and v for a given output gradient, the selection held fixed (the same section
- * cuts the index branch's gradient from the main branch).
+ * cuts the index branch's gradient from the main branch); and, for msa_oracle_project,
+ * the two projection matrices the index branch adds to GQA (section 核心机制, 索引分支):
+ * one index query head per group and one index key shared by the groups.
  *
  * Readings where the page is silent (each is listed with its reason in the
  * design notes):
@@ -515,6 +517,46 @@ int msa_oracle_attn_bwd(int batch, int n_q, int n_k, int q_start, int h_q, int h
     free(dp);
   }
   return failed ? -2 : 0;
+}
+
+/*
+ * Index-branch projections of the hidden states x, one output element at a time:
+ *   q_idx[b, r, t, d] = sum_i x[b, t, i] * w_q[r * d_idx + d, i]   (one head per group r)
+ *   k_idx[b, t, d]    = sum_i x[b, t, i] * w_k[d, i]               (shared by the groups)
+ * x [B, n, d_model], w_q [h_kv * d_idx, d_model] and w_k [d_idx, d_model] in the storage
+ * type (each weight row holds one output's coefficients); q_idx [B, h_kv, n, d_idx] and
+ * k_idx [B, n, d_idx] double, overwritten. Returns 0, or -1 on a bad argument.
+ */
+int msa_oracle_project(int batch, int n, int d_model, int h_kv, int d_idx, int type,
+                       const void *x, const void *w_q, const void *w_k, double *q_idx,
+                       double *k_idx, int n_threads) {
+  if (batch < 1 || n < 1 || d_model < 1 || h_kv < 1 || d_idx < 1 || !x || !w_q || !w_k ||
+      !q_idx || !k_idx || (type != ORACLE_F32 && type != ORACLE_BF16))
+    return -1;
+#ifdef _OPENMP
+  if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+  (void)n_threads;
+#endif
+#pragma omp parallel for schedule(static)
+  for (int64_t row = 0; row < (int64_t)batch * n; ++row) {
+    const int64_t b = row / n, t = row % n;
+    const int64_t xo = row * d_model;
+    for (int r = 0; r < h_kv; ++r)
+      for (int d = 0; d < d_idx; ++d) {
+        const int64_t wo = ((int64_t)r * d_idx + d) * d_model;
+        double s = 0.0;
+        for (int i = 0; i < d_model; ++i) s += elem(x, xo + i, type) * elem(w_q, wo + i, type);
+        q_idx[((b * h_kv + r) * n + t) * d_idx + d] = s;
+      }
+    for (int d = 0; d < d_idx; ++d) {
+      double s = 0.0;
+      for (int i = 0; i < d_model; ++i)
+        s += elem(x, xo + i, type) * elem(w_k, (int64_t)d * d_model + i, type);
+      k_idx[row * d_idx + d] = s;
+    }
+  }
+  return 0;
 }
 
 /* Threads the oracle will use when n_threads <= 0. */

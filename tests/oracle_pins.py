@@ -5,8 +5,10 @@ Definitions pinned (page "MiniMax-M3: MSA 技术报告速读", section 核心机
   index-branch token scores and causal block max-pool, the per-group TopK with
   the local block forced in, and the main-branch sparse softmax attention; and
   (section 训练) the index-branch distribution P^idx, the group-averaged teacher
-  P^(r) over the selected tokens and the alignment loss KL(P^(r) || P^idx); and the
-  gradients of the main-branch equation for a fixed selection.
+  P^(r) over the selected tokens and the alignment loss KL(P^(r) || P^idx); the
+  gradients of the main-branch equation for a fixed selection; and (section 核心机制,
+  索引分支) the index branch's two projections: one index query head per group, one index
+  key shared by the groups.
 
 Each pin takes an ``oracle.Oracle`` and raises AssertionError on a mismatch, so
 the same pins also run against deliberately broken oracle builds.
@@ -421,8 +423,66 @@ def pin_bwd_finite_difference(orc):
             assert abs(fd - got[grad][idx]) < 2e-5 * (1 + abs(fd)), (name, idx, fd, got[grad][idx])
 
 
+def pin_project_selector_weights(orc):
+    """Weights whose rows each pick one input coordinate: every output is exactly one
+    element of x, which fixes the output layout (group-major index queries, one shared
+    index key per row) and the weight orientation (a row per output)."""
+    B, n, dm, R, DI = 2, 5, 24, 3, 4
+    g = torch.Generator().manual_seed(51)
+    x = torch.randn(B, n, dm, generator=g)
+    pq = torch.randperm(dm, generator=g)[: R * DI]
+    pk = torch.randperm(dm, generator=g)[:DI]
+    w_q = torch.zeros(R * DI, dm)
+    w_q[torch.arange(R * DI), pq] = 1.0
+    w_k = torch.zeros(DI, dm)
+    w_k[torch.arange(DI), pk] = 1.0
+    out = orc.project(x, w_q, w_k, R, DI)
+    xd = x.double().numpy()
+    for r in range(R):
+        for d in range(DI):
+            assert np.array_equal(out["q_idx"][:, r, :, d], xd[:, :, int(pq[r * DI + d])]), (r, d)
+    for d in range(DI):
+        assert np.array_equal(out["k_idx"][:, :, d], xd[:, :, int(pk[d])]), d
+
+
+def pin_project_integer_bruteforce(orc):
+    """Small integer inputs: exact sums, against explicit Python loops over the definition."""
+    B, n, dm, R, DI = 1, 3, 7, 2, 3
+    g = torch.Generator().manual_seed(52)
+    x = torch.randint(-3, 4, (B, n, dm), generator=g).float()
+    w_q = torch.randint(-2, 3, (R * DI, dm), generator=g).float()
+    w_k = torch.randint(-2, 3, (DI, dm), generator=g).float()
+    out = orc.project(x, w_q, w_k, R, DI)
+    for b in range(B):
+        for t in range(n):
+            for r in range(R):
+                for d in range(DI):
+                    want = sum(float(x[b, t, i]) * float(w_q[r * DI + d, i]) for i in range(dm))
+                    assert out["q_idx"][b, r, t, d] == want
+            for d in range(DI):
+                want = sum(float(x[b, t, i]) * float(w_k[d, i]) for i in range(dm))
+                assert out["k_idx"][b, t, d] == want
+
+
+def pin_project_matmul(orc):
+    """Gaussian inputs in bf16 storage against numpy's fp64 matrix product of the same
+    bf16 values (widened by torch): the whole reduction, nothing dropped."""
+    B, n, dm, R, DI = 2, 9, 96, 4, 8
+    g = torch.Generator().manual_seed(53)
+    x = torch.randn(B, n, dm, generator=g).bfloat16()
+    w_q = (torch.randn(R * DI, dm, generator=g) / 8).bfloat16()
+    w_k = (torch.randn(DI, dm, generator=g) / 8).bfloat16()
+    out = orc.project(x, w_q, w_k, R, DI)
+    xd, wq, wk = (a.double().numpy() for a in (x, w_q, w_k))
+    want_q = np.matmul(xd, wq.T).reshape(B, n, R, DI).transpose(0, 2, 1, 3)
+    want_k = np.matmul(xd, wk.T)
+    assert np.abs(out["q_idx"] - want_q).max() <= 1e-12 * np.abs(want_q).max()
+    assert np.abs(out["k_idx"] - want_k).max() <= 1e-12 * np.abs(want_k).max()
+
+
 PINS = [pin_block_scores_exact, pin_topk_bruteforce, pin_dense_when_k_covers,
         pin_local_block_only, pin_token_level, pin_zero_query_closed_form,
         pin_group_map_and_ones, pin_entry_point_consistency, pin_bf16_storage_widening,
         pin_general_sparse, pin_kl_two_tokens_closed_form, pin_kl_student_equals_teacher,
-        pin_kl_uniform_teacher, pin_kl_dense_scipy, pin_bwd_autograd, pin_bwd_finite_difference]
+        pin_kl_uniform_teacher, pin_kl_dense_scipy, pin_bwd_autograd, pin_bwd_finite_difference,
+        pin_project_selector_weights, pin_project_integer_bruteforce, pin_project_matmul]

@@ -97,6 +97,14 @@ MUTANTS = [
                                  "dq[d] += dz * elem(v_plane, key[j] * d_h + d, type) * scale;")]),
     ("gradients land in the next group's planes", [("const int64_t kv_off = ((int64_t)b * h_kv + r) * (int64_t)n_k * d_h;\n      const void *kp",
                                                     "const int64_t kv_off = ((int64_t)b * h_kv + (r + 1) % h_kv) * (int64_t)n_k * d_h;\n      const void *kp")]),
+    ("projection weights read column-major", [("elem(w_q, wo + i, type)",
+                                               "elem(w_q, (int64_t)i * h_kv * d_idx + (int64_t)r * d_idx + d, type)")]),
+    ("index queries stored row-major over groups", [("q_idx[((b * h_kv + r) * n + t) * d_idx + d] = s;",
+                                                    "q_idx[((b * n + t) * h_kv + r) * d_idx + d] = s;")]),
+    ("index key projected with the query weights", [("s += elem(x, xo + i, type) * elem(w_k, (int64_t)d * d_model + i, type);",
+                                                    "s += elem(x, xo + i, type) * elem(w_q, (int64_t)d * d_model + i, type);")]),
+    ("projection drops the last input coordinate", [("for (int i = 0; i < d_model; ++i) s += elem(x, xo + i, type) * elem(w_q",
+                                                    "for (int i = 0; i < d_model - 1; ++i) s += elem(x, xo + i, type) * elem(w_q")]),
     ("query position ignores q_start", [("const int64_t t = rows[i], p = (int64_t)q_start + t;\n      const int64_t qoff = (((int64_t)b * h_kv",
                                          "const int64_t t = rows[i], p = t;\n      const int64_t qoff = (((int64_t)b * h_kv")]),
 ]
