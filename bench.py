@@ -3,12 +3,13 @@
 Headline (``value``): causal prefill tokens/s at N = 131072 (32 query heads / 4 KV
 groups, d_h 128, index d_idx 64, blocks of 64, top_k 32, bf16): one step is the index
 branch (block scores, top-k) plus the sparse prefill attention over all 131072 rows.
-The same line carries the 1M-token decode result (batch 4, one new token each, same
-heads) under ``decode``, and the index branch's alignment loss (msa_index_kl) on the
-prefill's selection under ``index_kl`` and the main branch's backward (dq, dk, dv for
-that selection) under ``attn_backward`` (both timed apart from the step), each with the
-roofline of its dominant kernel and the fp64 oracle timed on a bounded sample on the
-host cores.
+The same line carries, each with the roofline of its dominant kernel and the fp64
+oracle timed on a bounded sample on the host cores:
+  decode         the 1M-token decode (batch 4, one new token each, same heads);
+  index_kl       the index branch's alignment loss on the prefill's selection;
+  attn_backward  the main branch's backward (dq, dk, dv) for that selection;
+  index_project  the index branch's two projections from hidden states of width h_q * d_h.
+The last three are timed apart from the step.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing starts. Kernel
 durations come from HIP events recorded on the stream the library launches on.
@@ -65,6 +66,17 @@ def bwd_work(w):
     b = p // w.block_size
     t_p = (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
     return float(w.batch * w.h_q * np.sum(t_p) * 10 * w.d_h)
+
+
+def project_work(w, d_model):
+    """Algorithmic work of msa_index_project: FLOPs 2*d_model per output, (h_kv + 1)*d_idx
+    outputs per row; bytes: x, both weights and both outputs once each."""
+    es = 2 if w.dtype == "bf16" else 4
+    cols = (w.h_kv + 1) * w.d_idx
+    rows = w.batch * w.n_q
+    flops = float(2 * rows * d_model * cols)
+    nbytes = float(es * (rows * d_model + cols * d_model + rows * cols))
+    return flops, nbytes
 
 
 def decode_work(w):
@@ -187,6 +199,23 @@ def time_step(w, inputs, steps, warmup, decode):
         torch.cuda.synchronize()
         times["attn_backward"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
         del dout, dq, dk, dv, ws_bwd
+        # the index branch's projections of the step's rows (hidden width h_q * d_h)
+        from block_sparse_gqa_msa_amd.inputs import generate_hidden
+        hid = generate_hidden(w, w.h_q * w.d_h, device="cuda")
+        q_idx_p = torch.empty_like(inputs["q_idx"])
+        k_idx_p = torch.empty_like(inputs["k_idx"])
+        proj_call = lambda: msa.msa_index_project(s, hid["x"], hid["w_q"], hid["w_k"], q_idx_p,
+                                                  k_idx_p)
+        for _ in range(max(1, warmup)):
+            proj_call()
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(steps):
+            proj_call()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        times["index_project"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
+        del hid, q_idx_p, k_idx_p
     return wall, times
 
 
@@ -262,6 +291,34 @@ def cpu_baseline_bwd(w, inputs, target_s=12.0):
                 sample=f"the last {m} rows of the {w.n_q}-row prefill, all {w.h_kv} groups and "
                        f"{w.h_q} heads (dq of those rows, their dk and dv contributions; "
                        f"selections computed first and not timed); {dt:.1f} s")
+
+
+def cpu_baseline_project(w, d_model, target_s=6.0, seed=4):
+    """The oracle's projections of uniformly drawn rows of the step's hidden states."""
+    import oracle
+    import torch
+    from block_sparse_gqa_msa_amd.inputs import generate_hidden
+    orc = oracle.get()
+    hid = generate_hidden(w, d_model, device="cuda")
+    wq, wk = hid["w_q"].cpu(), hid["w_k"].cpu()
+    rng = np.random.default_rng(seed)
+
+    def rows_x(m):
+        rows = torch.as_tensor(np.sort(rng.choice(w.n_q, size=m, replace=False)), device="cuda")
+        return hid["x"][:, rows].cpu()
+
+    x = rows_x(256)
+    t0 = time.perf_counter()
+    orc.project(x, wq, wk, w.h_kv, w.d_idx)
+    dt = time.perf_counter() - t0
+    m = int(min(w.n_q, max(256, 256 * target_s / max(dt, 1e-3))))
+    x = rows_x(m)
+    t0 = time.perf_counter()
+    orc.project(x, wq, wk, w.h_kv, w.d_idx)
+    dt = time.perf_counter() - t0
+    return dict(value=w.batch * m / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+                sample=f"{m} rows drawn uniformly (seed {seed}) from the {w.n_q}-row prefill's "
+                       f"hidden states (d_model {d_model}); {dt:.1f} s")
 
 
 def cpu_baseline_decode(w, inputs, target_s=6.0):
@@ -392,6 +449,23 @@ def main():
                              traffic=measured_traffic("kv_bwd", wp.name),
                              per_launch_flops=f_bwd, avg_launch_ms=t_bwd * 1e3))
     log(f"[bench] attention backward {t_bwd * 1e3:.2f} ms/call")
+    t_pj = kt.pop("index_project")
+    d_model = wp.h_q * wp.d_h
+    f_pj, b_pj = project_work(wp, d_model)
+    # the bound is the larger of the two ideal times (bytes at the HBM peak, FLOPs at MFMA's)
+    if b_pj / PEAK_HBM_BYTES >= f_pj / PEAK_BF16_FLOPS:
+        pj_roof = dict(kernel="index_project", bound="hbm", achieved=b_pj / t_pj / 1e9,
+                       peak=PEAK_HBM_BYTES / 1e9, unit="GB/s", frac=b_pj / t_pj / PEAK_HBM_BYTES,
+                       per_launch_bytes=b_pj)
+    else:
+        pj_roof = dict(kernel="index_project", bound="mfma", achieved=f_pj / t_pj / 1e12,
+                       peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                       frac=f_pj / t_pj / PEAK_BF16_FLOPS, per_launch_flops=f_pj)
+    pj_roof.update(traffic=measured_traffic("index_project", wp.name), avg_launch_ms=t_pj * 1e3,
+                   tflops=f_pj / t_pj / 1e12, mfma_frac=f_pj / t_pj / PEAK_BF16_FLOPS)
+    proj = dict(workload=wp.name, d_model=d_model, value=wp.batch * wp.n_q / t_pj, unit="tok/s",
+                ms_per_call=t_pj * 1e3, roofline=pj_roof)
+    log(f"[bench] index projections {t_pj * 1e3:.3f} ms/call")
     cpu_p = None
     if not args.no_cpu:
         log("[bench] oracle CPU baseline (prefill sample)")
@@ -400,6 +474,8 @@ def main():
         kl["cpu_baseline"] = cpu_baseline_kl(wp, inp)
         log("[bench] oracle CPU baseline (backward sample)")
         bwd["cpu_baseline"] = cpu_baseline_bwd(wp, inp)
+        log("[bench] oracle CPU baseline (projection sample)")
+        proj["cpu_baseline"] = cpu_baseline_project(wp, d_model)
     del inp
     torch.cuda.empty_cache()
 
@@ -444,6 +520,7 @@ def main():
         "cpu_baseline": cpu_p,
         "index_kl": kl,
         "attn_backward": bwd,
+        "index_project": proj,
         "decode": {
             "workload": wd.name, "value": wd.batch / dwall, "unit": "tok/s",
             "steps": args.decode_steps, "ms_per_step": dwall * 1e3,

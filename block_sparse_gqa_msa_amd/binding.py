@@ -25,6 +25,7 @@ EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_s
            "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_partials",
            "msa_sparse_attn_prefill_merge", "msa_sparse_attn_decode", "msa_index_kl",
            "msa_sparse_attn_backward_workspace_size", "msa_sparse_attn_backward",
+           "msa_index_project",
            "msa_last_error", "msa_abi_version")
 
 
@@ -75,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_decode.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_index_kl.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_backward_workspace_size.argtypes = [S, sz]
+    lib.msa_index_project.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P]
     lib.msa_sparse_attn_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     for f in EXPORTS:
         if f == "msa_last_error":
@@ -278,6 +280,18 @@ def msa_sparse_attn_backward(shape: MsaShape, q, k, v, sel, o, lse, dout, dq, dk
         _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"), _ptr(lse, torch.float32, "lse"),
         _ptr(dout, et, "dout"), _ptr(dq, et, "dq"), _ptr(dk, et, "dk"), _ptr(dv, et, "dv"),
         wp, wn, _stream(stream, dq)))
+
+
+def msa_index_project(shape: MsaShape, x, w_qidx, w_kidx, q_idx, k_idx, stream=None) -> None:
+    """x [B, n_q, d_model]; writes q_idx [B, h_kv, n_q, d_idx] and the k_idx cache rows
+    q_start .. q_start + n_q - 1. d_model is taken from x."""
+    et = _elem_dtype(shape)
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, n_q, d_model]")
+    _check(load_library().msa_index_project(
+        ctypes.byref(shape), int(x.shape[-1]), _ptr(x, et, "x"), _ptr(w_qidx, et, "w_qidx"),
+        _ptr(w_kidx, et, "w_kidx"), _ptr(q_idx, et, "q_idx"), _ptr(k_idx, et, "k_idx"),
+        _stream(stream, q_idx)))
 
 
 # ----------------------------------------------------------------- allocation helpers

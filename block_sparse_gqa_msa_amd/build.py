@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 SOURCES = ["msa_api.cpp", "msa_index.hip", "msa_topk.hip", "msa_attn.hip", "msa_kvouter.hip",
-           "msa_kl.hip", "msa_bwd.hip"]
+           "msa_kl.hip", "msa_bwd.hip",
+           "msa_proj.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

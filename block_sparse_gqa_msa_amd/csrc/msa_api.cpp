@@ -485,6 +485,27 @@ int msa_sparse_attn_backward(const msa_shape *shape, const void *q, const void *
   return ok();
 }
 
+int msa_index_project(const msa_shape *shape, int32_t d_model, const void *x, const void *w_qidx,
+                      const void *w_kidx, void *q_idx, void *k_idx, void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if ((rc = check_index_dims(s))) return rc;
+  if (d_model < 64 || d_model % 64)
+    return fail(MSA_ERR_UNSUPPORTED, "d_model %d is not a positive multiple of 64", d_model);
+  if (empty(s)) return ok();
+  if (!x || !w_qidx || !w_kidx || !q_idx || !k_idx)
+    return fail(MSA_ERR_INVALID_ARG, "x, w_qidx, w_kidx, q_idx and k_idx must be non-NULL");
+  if ((long long)s.batch * s.n_q >= (1LL << 36))
+    return fail(MSA_ERR_UNSUPPORTED, "too many rows (%lld) for one call",
+                (long long)s.batch * s.n_q);
+  const msa::ProjArgs a{x, w_qidx, w_kidx, q_idx, k_idx, s.batch, s.n_q, s.q_start, s.h_kv,
+                        d_model, cap_of(s), (s.h_kv + 1) * s.d_idx};
+  hipError_t e = msa::launch_index_project(a, s.dtype, s.d_idx, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "index projection launch");
+  return ok();
+}
+
 int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_cache,
                            const void *v_cache, const int32_t *sel, void *o, float *lse,
                            void *workspace, size_t workspace_bytes, void *stream) {

@@ -92,6 +92,17 @@ int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long group, lon
 size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
                           long d_h, long elem_bytes, KvLayout *lay);
 
+// The index branch's projections from hidden states x [B, n_q, d_model].
+struct ProjArgs {
+  const void *x;    // [B, n_q, d_model]
+  const void *w_q;  // [h_kv * d_idx, d_model], one row per output
+  const void *w_k;  // [d_idx, d_model]
+  void *q_idx;      // [B, h_kv, n_q, d_idx] out
+  void *k_idx;      // [B, cap, d_idx]: rows q_start .. q_start + n_q - 1 written
+  int batch, n_q, q_start, h_kv, d_model, cap;
+  int n_cols;       // (h_kv + 1) * d_idx
+};
+
 // Backward workspace: the prefill lists (KvLayout; part_o holds the dq partials), D per
 // (b, h, t), and one fp32 dK/dV partial per (run, list) segment of the backward kernel.
 struct BwdLayout {
@@ -123,6 +134,7 @@ hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t
 hipError_t launch_index_kl(const KvArgs &a, const KlArgs &k, int dtype, int d_h, int d_idx,
                            hipStream_t s);
 
+hipError_t launch_index_project(const ProjArgs &a, int dtype, int d_idx, hipStream_t s);
 // Main-branch gradients for a fixed selection: lists (plan stage), D, per-block gradients,
 // then the dq merge and the dk/dv reduction.
 hipError_t launch_attn_backward(const KvArgs &a, const BwdLayout &lay, unsigned char *ws, const void *o,

@@ -151,3 +151,34 @@ def generate_dout(w: Workload, device="cpu", seed: Optional[int] = None) -> torc
         out[b].copy_(x)
         del x
     return out
+
+
+def generate_hidden(w: Workload, d_model: int, device="cpu", seed: Optional[int] = None,
+                    integer: bool = False) -> Dict[str, torch.Tensor]:
+    """Hidden states and the index branch's two projection weights for workload ``w``:
+    x [B, n_q, d_model], w_q [h_kv * d_idx, d_model] and w_k [d_idx, d_model] in the
+    storage type, from their own stream (seed + 2 unless ``seed`` is given).
+
+    Default: x ~ N(0, 1) and weights ~ N(0, 1 / d_model), so the projections have unit
+    scale. ``integer=True``: x in [-2, 2] and weights in [-1, 1], integers, so for
+    d_model <= 128 every sum is an integer of magnitude <= 256, exact in fp32 and bf16."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed((w.seed + 2) if seed is None else seed)
+    dt = torch_dtype(w)
+
+    def draw(shape, scale, lo, hi):
+        if integer:
+            v = torch.randint(lo, hi + 1, shape, generator=gen, device=device, dtype=torch.int32)
+        else:
+            v = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+            if scale != 1.0:
+                v.mul_(scale)
+        return v.to(dt)
+
+    x = torch.empty((w.batch, w.n_q, d_model), dtype=dt, device=device)
+    for b in range(w.batch):
+        x[b] = draw((w.n_q, d_model), 1.0, -2, 2)
+    w_q = draw((w.h_kv * w.d_idx, d_model), d_model ** -0.5, -1, 1)
+    w_k = draw((w.d_idx, d_model), d_model ** -0.5, -1, 1)
+    return dict(x=x, w_q=w_q, w_k=w_k)

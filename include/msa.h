@@ -205,6 +205,26 @@ int msa_index_kl(const msa_shape *shape, const void *q, const void *k, const voi
                  float *lse_idx, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The index branch's two projections ("MiniMax-M3: MSA 技术报告速读", section 核心机制,
+ * 索引分支: standard GQA plus an index query with one head per group and an index key
+ * shared by the groups), from the hidden states of the call's rows:
+ *   q_idx[b, r, t, d]          = sum_i x[b, t, i] * w_qidx[r * d_idx + d, i]
+ *   k_idx[b, q_start + t, d]   = sum_i x[b, t, i] * w_kidx[d, i]
+ *   x        [batch, n_q, d_model], dtype; row t is the token at position q_start + t
+ *   w_qidx   [h_kv * d_idx, d_model], dtype, one row per output (a linear layer's weight)
+ *   w_kidx   [d_idx, d_model], dtype
+ *   q_idx    out [batch, h_kv, n_q, d_idx] (the layout msa_index_topk reads)
+ *   k_idx    the index-key cache [batch, kv_capacity, d_idx]: rows q_start .. q_start +
+ *            n_q - 1 are written (the append of the call's tokens; for a decode shape the
+ *            new token's row n_k - 1), every other row is left as it is
+ * fp32 accumulation, results rounded to nearest even for bf16. No workspace. Uses batch,
+ * n_q, q_start, h_kv, d_idx, dtype and kv_capacity of the shape (the rest must still be a
+ * valid shape). Supported: d_idx in {32, 64}, d_model a positive multiple of 64, fewer than
+ * 2^36 rows per call.
+ */
+int msa_index_project(const msa_shape *shape, int32_t d_model, const void *x, const void *w_qidx,
+                      const void *w_kidx, void *q_idx, void *k_idx, void *stream);
+/*
  * Workspace bytes msa_sparse_attn_backward needs for `shape`: the per-block query lists,
  * one partial dq per (row, group, selected block, head) (about batch * h_kv * n_q *
  * top_k * (h_q / h_kv) * d_h * sizeof(dtype) bytes, as for the prefill), D per (b, h, t)

@@ -255,3 +255,28 @@ def test_backward_rejects(lib):
         assert msa.msa_sparse_attn_backward_workspace_size(e) == 0
         assert lib.msa_sparse_attn_backward(ctypes.byref(e), *([None] * 10), None, 0, None) \
             == msa.MSA_OK
+
+
+def test_index_project_rejects(lib):
+    dummy = 1 << 20
+    s = good()
+    sb = ctypes.byref(s)
+    args = [dummy] * 5  # x, w_qidx, w_kidx, q_idx, k_idx
+    for i in range(5):
+        a = list(args)
+        a[i] = None
+        assert lib.msa_index_project(sb, 256, *a, None) == msa.MSA_ERR_INVALID_ARG
+        assert "non-NULL" in msa.msa_last_error()
+    for dm in (0, 32, 96, -64):
+        assert lib.msa_index_project(sb, dm, *args, None) == msa.MSA_ERR_UNSUPPORTED
+        assert "d_model" in msa.msa_last_error()
+    x = good(d_idx=48)
+    assert lib.msa_index_project(ctypes.byref(x), 256, *args, None) == msa.MSA_ERR_UNSUPPORTED
+    x = good(q_start=10)  # q_start + n_q > n_k
+    assert lib.msa_index_project(ctypes.byref(x), 256, *args, None) == msa.MSA_ERR_INVALID_ARG
+    for kw in (dict(batch=0), dict(n_q=0)):
+        e = good(**kw)
+        assert lib.msa_index_project(ctypes.byref(e), 256, *([None] * 5), None) == msa.MSA_OK
+    # the supported set is checked on empty calls too
+    e = good(n_q=0)
+    assert lib.msa_index_project(ctypes.byref(e), 100, *([None] * 5), None) == msa.MSA_ERR_UNSUPPORTED
