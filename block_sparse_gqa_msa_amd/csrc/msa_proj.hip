@@ -8,38 +8,41 @@
 //   k_idx[b, q_start + t, :] = x[b, t] . w_k[d]       (appended to the cache rows of the
 //                                                       call's positions)
 // One product over the concatenated output columns (h_kv + 1) * d_idx: a workgroup takes
-// 64 rows of x and up to four 64-column output tiles (one per wave); x is staged in LDS 64
-// columns of d_model at a time, and each wave reads its weight fragments straight from
-// memory (the weights are a few MB and stay in L2), one stage ahead.
+// 128 rows of x (64 for fp32) and all the output columns up to 320, a quarter per wave;
+// x is staged in LDS 64 columns of d_model at a time, and each wave reads its weight
+// fragments straight from memory (the weights are a few MB and stay in L2). Every
+// workgroup reads the whole weight once per row range, so more rows per workgroup means
+// less L2 traffic.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
 
 namespace msa {
 namespace {
 
-constexpr int PJ_M = 64;  // rows per workgroup
 constexpr int PJ_K = 64;  // d_model columns per staged tile
-constexpr int PJ_N = 64;  // output columns per wave
 
-template <typename E, int DI>
+// MT 16-row tiles per workgroup (all four waves share them) and NT 16-column output tiles
+// per wave: a workgroup covers 16 * MT rows and 64 * NT output columns.
+template <typename E, int DI, int MT, int NT>
 __global__ __launch_bounds__(256) void index_project(ProjArgs a) {
   using F = typename Frag<E>::type;
   constexpr int ES = (int)sizeof(E);
+  constexpr int PM = 16 * MT;                   // rows per workgroup
   constexpr int XROW = PJ_K * ES + 16;
   constexpr int PPR = PJ_K * ES / 16;           // 16-byte pieces per staged row
-  constexpr int PT = PJ_M * PPR / 256;          // pieces per thread
-  __shared__ __attribute__((aligned(16))) unsigned char s_x[PJ_M * XROW];
+  constexpr int PT = PM * PPR / 256;            // pieces per thread
+  __shared__ __attribute__((aligned(16))) unsigned char s_x[2][PM * XROW];
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const long rows = (long)a.batch * a.n_q;
-  const long row0 = (long)blockIdx.x * PJ_M;
-  const int col0 = (blockIdx.y * 4 + wv) * PJ_N;
+  const long row0 = (long)blockIdx.x * PM;
+  const int col0 = (blockIdx.y * 4 + wv) * 16 * NT;
   const bool active = col0 < a.n_cols;  // uniform over the wave
   const int qcols = a.h_kv * DI;
   const E *x = reinterpret_cast<const E *>(a.x);
-  const E *wrow[4];
+  const E *wrow[NT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     const int c = min(col0 + nt * 16 + c16, a.n_cols - 1);
     wrow[nt] = c < qcols ? reinterpret_cast<const E *>(a.w_q) + (long)c * a.d_model
                          : reinterpret_cast<const E *>(a.w_k) + (long)(c - qcols) * a.d_model;
@@ -55,94 +58,128 @@ __global__ __launch_bounds__(256) void index_project(ProjArgs a) {
           reinterpret_cast<const unsigned char *>(x + gr * a.d_model + k0) + (pc % PPR) * 16));
     }
   };
-  F wf[2][4], wn[2][4];
-  auto load_w = [&](int k0, F (&dst)[2][4]) {
+  // this wave's weight fragments of one staged tile; loaded right after the previous
+  // tile's last use so they arrive over the barrier and the staging
+  F wf[2][NT];
+  auto load_w = [&](int k0) {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) dst[kc][nt] = load_frag(wrow[nt] + k0 + kc * 32 + g * 8);
+      for (int nt = 0; nt < NT; ++nt) wf[kc][nt] = load_frag(wrow[nt] + k0 + kc * 32 + g * 8);
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_x(0);
-  load_w(0, wf);
-  for (int k0 = 0; k0 < a.d_model; k0 += PJ_K) {
-    __syncthreads();  // the previous tile's reads are done
+  // x tiles are double-buffered in LDS: tile s + 1 is written while tile s is read, and the
+  // loads of tile s + 2 have a whole tile's products to arrive in.
+  auto store_x = [&](unsigned char *dst) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int pc = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(s_x + (pc / PPR) * XROW + (pc % PPR) * 16) = xp[i];
+      *reinterpret_cast<u32x4 *>(dst + (pc / PPR) * XROW + (pc % PPR) * 16) = xp[i];
     }
-    __syncthreads();
-    // the next tile's loads stay in flight over this one (the last tile reloads itself)
-    const int kn = k0 + PJ_K < a.d_model ? k0 + PJ_K : k0;
-    load_x(kn);
-    load_w(kn, wn);
+  };
+  const int n_tiles = a.d_model / PJ_K;
+  load_x(0);
+  load_w(0);
+  store_x(s_x[0]);
+  load_x(n_tiles > 1 ? PJ_K : 0);
+  __syncthreads();
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const unsigned char *cur = s_x[tile & 1];
     if (active) {
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        F af[4];
+      for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          af[mt] = load_frag(reinterpret_cast<const E *>(s_x + (mt * 16 + c16) * XROW + (kc * 32 + g * 8) * ES));
+        for (int mt = 0; mt < MT; ++mt) {
+          const F af = load_frag(reinterpret_cast<const E *>(cur + (mt * 16 + c16) * XROW + (kc * 32 + g * 8) * ES));
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_chunk(af[mt], wf[kc][nt], acc[mt][nt]);
-      }
+          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_chunk(af, wf[kc][nt], acc[mt][nt]);
+        }
     }
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) wf[kc][nt] = wn[kc][nt];
+    // unconditional loads: past the last tile they re-read the last one
+    const int k1 = min(tile + 1, n_tiles - 1) * PJ_K, k2 = min(tile + 2, n_tiles - 1) * PJ_K;
+    load_w(k1);
+    store_x(s_x[(tile + 1) & 1]);  // tile + 1 (its buffer was last read before the barrier)
+    load_x(k2);
+    __syncthreads();
   }
-  if (!active) return;
-
-  // lane (c16, g) holds output column 16 nt + c16 of rows 16 mt + 4 g + i
+  // Outputs go through LDS one 16-row tile at a time (a wave-private slice of the x
+  // buffers, free after the last barrier), then out as 16-byte pieces of 8 (bf16) or 4
+  // (fp32) consecutive columns: a piece never straddles a group's d_idx columns or the
+  // query / key boundary.
+  constexpr int OROW = 16 * NT * ES + 16;
+  static_assert(4 * 16 * OROW <= 2 * PM * XROW, "output staging fits the x buffers");
+  unsigned char *so = s_x[0] + wv * 16 * OROW;
+  constexpr int PE = 16 / ES, PPO = 16 * NT / PE;  // elements per piece, pieces per row
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int c = col0 + nt * 16 + c16;
-    if (c >= a.n_cols) continue;
-    const bool is_q = c < qcols;
-    const int r = c / DI, d = c % DI, dk = c - qcols;
+  for (int mt = 0; mt < MT; ++mt) {
+    if (active) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long gr = row0 + mt * 16 + 4 * g + i;
-        if (gr >= rows) continue;
+        for (int i = 0; i < 4; ++i) {
+          unsigned char *dst = so + (4 * g + i) * OROW + (nt * 16 + c16) * ES;
+          if constexpr (ES == 2)
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(pack_bf16x2(acc[mt][nt][i], 0.f) & 0xffffu);
+          else
+            *reinterpret_cast<float *>(dst) = acc[mt][nt][i];
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // wave-private: in-order LDS
+      for (int pc = lane; pc < 16 * PPO; pc += 64) {
+        const int rr = pc / PPO, c = col0 + (pc % PPO) * PE;
+        const long gr = row0 + mt * 16 + rr;
+        if (c >= a.n_cols || gr >= rows) continue;
         const long b = gr / a.n_q, t = gr % a.n_q;
-        const long off = is_q ? (((b * a.h_kv + r) * a.n_q + t) * DI + d)
-                              : ((b * a.cap + a.q_start + t) * DI + dk);
-        E *dst = reinterpret_cast<E *>(is_q ? a.q_idx : a.k_idx) + off;
-        if constexpr (ES == 2)
-          *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(pack_bf16x2(acc[mt][nt][i], 0.f) & 0xffffu);
-        else
-          *reinterpret_cast<float *>(dst) = acc[mt][nt][i];
+        const long off = c < qcols ? (((b * a.h_kv + c / DI) * a.n_q + t) * DI + c % DI)
+                                   : ((b * a.cap + a.q_start + t) * DI + (c - qcols));
+        E *dst = reinterpret_cast<E *>(c < qcols ? a.q_idx : a.k_idx) + off;
+        *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(so + rr * OROW + (pc % PPO) * 16);
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next tile's writes
+    }
+  }
+}
+
+template <typename E, int DI, int MT, int NT>
+void launch_pj(const ProjArgs &a, hipStream_t s) {
+  const long rows = (long)a.batch * a.n_q;
+  const dim3 grid((unsigned)((rows + 16 * MT - 1) / (16 * MT)),
+                  (unsigned)((a.n_cols + 64 * NT - 1) / (64 * NT)));
+  hipLaunchKernelGGL((index_project<E, DI, MT, NT>), grid, dim3(256), 0, s, a);
+}
+
+// Column tiles per wave: the output columns spread over the four waves, at most five
+// 16-column tiles each (wider outputs take several workgroups per row range).
+template <typename E, int DI, int MT>
+void launch_pj_cols(const ProjArgs &a, hipStream_t s) {
+  const int per_wave = (a.n_cols + 63) / 64;
+  switch (per_wave < 5 ? per_wave : 5) {
+    case 1: launch_pj<E, DI, MT, 1>(a, s); break;
+    case 2: launch_pj<E, DI, MT, 2>(a, s); break;
+    case 3: launch_pj<E, DI, MT, 3>(a, s); break;
+    case 4: launch_pj<E, DI, MT, 4>(a, s); break;
+    default: launch_pj<E, DI, MT, 5>(a, s); break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_index_project(const ProjArgs &a, int dtype, int d_idx, hipStream_t s) {
-  const long rows = (long)a.batch * a.n_q;
-  const dim3 grid((unsigned)((rows + PJ_M - 1) / PJ_M), (unsigned)((a.n_cols + 4 * PJ_N - 1) / (4 * PJ_N)));
-  if (dtype == 0) {
+  if (dtype == 0) {  // fp32 fragments are twice the registers: half the rows per workgroup
     if (d_idx == 32)
-      hipLaunchKernelGGL((index_project<float, 32>), grid, dim3(256), 0, s, a);
+      launch_pj_cols<float, 32, 4>(a, s);
     else
-      hipLaunchKernelGGL((index_project<float, 64>), grid, dim3(256), 0, s, a);
+      launch_pj_cols<float, 64, 4>(a, s);
   } else {
     if (d_idx == 32)
-      hipLaunchKernelGGL((index_project<bf16_t, 32>), grid, dim3(256), 0, s, a);
+      launch_pj_cols<bf16_t, 32, 8>(a, s);
     else
-      hipLaunchKernelGGL((index_project<bf16_t, 64>), grid, dim3(256), 0, s, a);
+      launch_pj_cols<bf16_t, 64, 8>(a, s);
   }
   return hipGetLastError();
 }
