@@ -197,6 +197,23 @@ def time_step(w, inputs, steps, warmup, decode):
             bwd_call()
         ev[1].record(stream)
         torch.cuda.synchronize()
+        # the same backward as its three staged calls, with an event around each, so the
+        # per-block gradient kernel is timed alone
+        bst = [("bwd_plan", lambda: msa.msa_sparse_attn_backward_plan(s, sel, o, dout, ws_bwd)),
+               ("bwd_partials", lambda: msa.msa_sparse_attn_backward_partials(
+                   s, inputs["q"], inputs["k"], inputs["v"], lse, dout, ws_bwd)),
+               ("bwd_merge", lambda: msa.msa_sparse_attn_backward_merge(s, sel, dq, dk, dv,
+                                                                        ws_bwd))]
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bst) + 1)]
+               for _ in range(steps)]
+        for i in range(steps):
+            for j, (_, call) in enumerate(bst):
+                sev[i][j].record(stream)
+                call()
+            sev[i][-1].record(stream)
+        torch.cuda.synchronize()
+        for j, (name, _) in enumerate(bst):
+            times[name] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in sev])) * 1e-3
         times["attn_backward"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
         del dout, dq, dk, dv, ws_bwd
         # the index branch's projections of the step's rows (hidden width h_q * d_h)
@@ -440,14 +457,18 @@ def main():
                             per_launch_flops=f_kl, avg_launch_ms=t_kl * 1e3))
     log(f"[bench] alignment loss {t_kl * 1e3:.2f} ms/call")
     t_bwd = kt.pop("attn_backward")
+    t_bst = {k: kt.pop(k) for k in ("bwd_plan", "bwd_partials", "bwd_merge")}
+    t_kvb = t_bst["bwd_partials"]  # the kv_bwd kernel alone
     f_bwd = bwd_work(wp)
     bwd = dict(workload=wp.name, value=wp.batch * wp.n_q / t_bwd, unit="tok/s",
                ms_per_call=t_bwd * 1e3,
-               roofline=dict(kernel="kv_bwd", bound="mfma", achieved=f_bwd / t_bwd / 1e12,
+               roofline=dict(kernel="kv_bwd", bound="mfma", achieved=f_bwd / t_kvb / 1e12,
                              peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                             frac=f_bwd / t_bwd / PEAK_BF16_FLOPS,
+                             frac=f_bwd / t_kvb / PEAK_BF16_FLOPS,
                              traffic=measured_traffic("kv_bwd", wp.name),
-                             per_launch_flops=f_bwd, avg_launch_ms=t_bwd * 1e3))
+                             per_launch_flops=f_bwd, avg_launch_ms=t_kvb * 1e3),
+               call_mfma=dict(tflops=f_bwd / t_bwd / 1e12, mfma_frac=f_bwd / t_bwd / PEAK_BF16_FLOPS),
+               stage_ms={k: v * 1e3 for k, v in t_bst.items()})
     log(f"[bench] attention backward {t_bwd * 1e3:.2f} ms/call")
     t_pj = kt.pop("index_project")
     d_model = wp.h_q * wp.d_h

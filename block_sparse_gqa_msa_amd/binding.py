@@ -25,7 +25,8 @@ EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_s
            "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_partials",
            "msa_sparse_attn_prefill_merge", "msa_sparse_attn_decode", "msa_index_kl",
            "msa_sparse_attn_backward_workspace_size", "msa_sparse_attn_backward",
-           "msa_index_project",
+           "msa_sparse_attn_backward_plan", "msa_sparse_attn_backward_partials",
+           "msa_sparse_attn_backward_merge", "msa_index_project",
            "msa_last_error", "msa_abi_version")
 
 
@@ -77,6 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_index_kl.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_backward_workspace_size.argtypes = [S, sz]
     lib.msa_index_project.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P]
+    lib.msa_sparse_attn_backward_plan.argtypes = [S, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_sparse_attn_backward_partials.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_sparse_attn_backward_merge.argtypes = [S, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     for f in EXPORTS:
         if f == "msa_last_error":
@@ -280,6 +284,36 @@ def msa_sparse_attn_backward(shape: MsaShape, q, k, v, sel, o, lse, dout, dq, dk
         _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"), _ptr(lse, torch.float32, "lse"),
         _ptr(dout, et, "dout"), _ptr(dq, et, "dq"), _ptr(dk, et, "dk"), _ptr(dv, et, "dv"),
         wp, wn, _stream(stream, dq)))
+
+
+def msa_sparse_attn_backward_plan(shape: MsaShape, sel, o, dout, workspace=None,
+                                  stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_sparse_attn_backward_plan(
+        ctypes.byref(shape), _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"),
+        _ptr(dout, et, "dout"), wp, wn, _stream(stream, dout)))
+
+
+def msa_sparse_attn_backward_partials(shape: MsaShape, q, k, v, lse, dout, workspace=None,
+                                      stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_sparse_attn_backward_partials(
+        ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k, et, "k"), _ptr(v, et, "v"),
+        _ptr(lse, torch.float32, "lse"), _ptr(dout, et, "dout"), wp, wn, _stream(stream, q)))
+
+
+def msa_sparse_attn_backward_merge(shape: MsaShape, sel, dq, dk, dv, workspace=None,
+                                   stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_sparse_attn_backward_merge(
+        ctypes.byref(shape), _ptr(sel, torch.int32, "sel"), _ptr(dq, et, "dq"),
+        _ptr(dk, et, "dk"), _ptr(dv, et, "dv"), wp, wn, _stream(stream, dq)))
 
 
 def msa_index_project(shape: MsaShape, x, w_qidx, w_kidx, q_idx, k_idx, stream=None) -> None:

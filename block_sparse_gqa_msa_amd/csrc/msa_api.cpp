@@ -456,6 +456,32 @@ int msa_sparse_attn_backward_workspace_size(const msa_shape *shape, size_t *byte
   return ok();
 }
 
+// Validates a backward call and fills the kernel arguments over the caller's workspace
+// (the lists live at its start, laid out as for the prefill).
+static int backward_args(const msa_shape *shape, void *workspace, size_t workspace_bytes,
+                         msa::KvArgs *a, msa::BwdLayout *lay) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if ((rc = check_attn_dims(s))) return rc;
+  if ((rc = check_prefill_limits(s))) return rc;
+  const size_t need = attn_backward_ws(s, lay);
+  if (!workspace || workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  return prefill_args(shape, workspace, workspace_bytes, a);
+}
+
+static int run_backward(const msa_shape &s, const msa::KvArgs &a, const msa::BwdLayout &lay,
+                        void *workspace, const void *o, const void *dout, const float *lse,
+                        void *dq, void *dk, void *dv, int stages, void *stream) {
+  hipError_t e = msa::launch_attn_backward(a, lay, reinterpret_cast<unsigned char *>(workspace), o,
+                                           dout, lse, dq, dk, dv, s.dtype, s.d_h, stages,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return ok();
+}
+
 int msa_sparse_attn_backward(const msa_shape *shape, const void *q, const void *k, const void *v,
                              const int32_t *sel, const void *o, const float *lse, const void *dout,
                              void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
@@ -466,23 +492,61 @@ int msa_sparse_attn_backward(const msa_shape *shape, const void *q, const void *
   if (empty(s)) return empty_attn_call(s);
   if (!q || !k || !v || !sel || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(MSA_ERR_INVALID_ARG, "q, k, v, sel, o, lse, dout, dq, dk and dv must be non-NULL");
-  if ((rc = check_attn_dims(s))) return rc;
-  if ((rc = check_prefill_limits(s))) return rc;
-  msa::BwdLayout lay;
-  const size_t need = attn_backward_ws(s, &lay);
-  if (!workspace || workspace_bytes < need)
-    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace ? workspace_bytes : (size_t)0);
   msa::KvArgs a;
-  // the lists live at the start of the backward workspace, laid out as for the prefill
-  if ((rc = prefill_args(shape, workspace, workspace_bytes, &a))) return rc;
+  msa::BwdLayout lay;
+  if ((rc = backward_args(shape, workspace, workspace_bytes, &a, &lay))) return rc;
   a.q = q; a.k = k; a.v = v; a.sel = sel;
   if ((rc = run_prefill(s, a, msa::KV_STAGE_PLAN, stream))) return rc;
-  hipError_t e = msa::launch_attn_backward(a, lay, reinterpret_cast<unsigned char *>(workspace), o, dout,
-                                           lse, dq, dk, dv, s.dtype, s.d_h,
-                                           reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
-  return ok();
+  return run_backward(s, a, lay, workspace, o, dout, lse, dq, dk, dv, msa::BWD_STAGE_ALL, stream);
+}
+
+int msa_sparse_attn_backward_plan(const msa_shape *shape, const int32_t *sel, const void *o,
+                                  const void *dout, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if (empty(s)) return empty_attn_call(s);
+  if (!sel || !o || !dout) return fail(MSA_ERR_INVALID_ARG, "sel, o and dout must be non-NULL");
+  msa::KvArgs a;
+  msa::BwdLayout lay;
+  if ((rc = backward_args(shape, workspace, workspace_bytes, &a, &lay))) return rc;
+  a.sel = sel;
+  if ((rc = run_prefill(s, a, msa::KV_STAGE_PLAN, stream))) return rc;
+  return run_backward(s, a, lay, workspace, o, dout, nullptr, nullptr, nullptr, nullptr,
+                      msa::BWD_STAGE_ROWDOT, stream);
+}
+
+int msa_sparse_attn_backward_partials(const msa_shape *shape, const void *q, const void *k,
+                                      const void *v, const float *lse, const void *dout,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if (empty(s)) return empty_attn_call(s);
+  if (!q || !k || !v || !lse || !dout)
+    return fail(MSA_ERR_INVALID_ARG, "q, k, v, lse and dout must be non-NULL");
+  msa::KvArgs a;
+  msa::BwdLayout lay;
+  if ((rc = backward_args(shape, workspace, workspace_bytes, &a, &lay))) return rc;
+  a.q = q; a.k = k; a.v = v;
+  return run_backward(s, a, lay, workspace, nullptr, dout, lse, nullptr, nullptr, nullptr,
+                      msa::BWD_STAGE_BLOCKS, stream);
+}
+
+int msa_sparse_attn_backward_merge(const msa_shape *shape, const int32_t *sel, void *dq, void *dk,
+                                   void *dv, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if (empty(s)) return empty_attn_call(s);
+  if (!sel || !dq || !dk || !dv) return fail(MSA_ERR_INVALID_ARG, "sel, dq, dk and dv must be non-NULL");
+  msa::KvArgs a;
+  msa::BwdLayout lay;
+  if ((rc = backward_args(shape, workspace, workspace_bytes, &a, &lay))) return rc;
+  a.sel = sel;
+  return run_backward(s, a, lay, workspace, nullptr, nullptr, nullptr, dq, dk, dv,
+                      msa::BWD_STAGE_MERGE, stream);
 }
 
 int msa_index_project(const msa_shape *shape, int32_t d_model, const void *x, const void *w_qidx,

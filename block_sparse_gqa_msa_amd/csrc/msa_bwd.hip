@@ -563,11 +563,14 @@ __global__ __launch_bounds__(256) void dkv_reduce(KvArgs a, BwdArgs w) {
 
 template <typename E, int DH, int BS>
 hipError_t run_bwd(const KvArgs &a, const BwdArgs &w, const void *o, int log2g, long max_runs,
-                   hipStream_t s) {
-  const long hrows = (long)a.batch * a.h_q * a.n_q;
-  hipLaunchKernelGGL((bwd_rowdot<E, DH>), dim3((unsigned)((hrows * (DH / 8) + 255) / 256)), dim3(256), 0,
-                     s, reinterpret_cast<const E *>(o), reinterpret_cast<const E *>(w.dout),
-                     const_cast<float *>(w.dsum), hrows);
+                   int stages, hipStream_t s) {
+  if (stages & BWD_STAGE_ROWDOT) {
+    const long hrows = (long)a.batch * a.h_q * a.n_q;
+    hipLaunchKernelGGL((bwd_rowdot<E, DH>), dim3((unsigned)((hrows * (DH / 8) + 255) / 256)), dim3(256),
+                       0, s, reinterpret_cast<const E *>(o), reinterpret_cast<const E *>(w.dout),
+                       const_cast<float *>(w.dsum), hrows);
+  }
+  if (!(stages & (BWD_STAGE_BLOCKS | BWD_STAGE_MERGE))) return hipGetLastError();
   static const int per_cu = [] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kv_bwd<E, DH, BS>, BwdLds<E, DH, BS>::NT, 0) !=
@@ -580,7 +583,9 @@ hipError_t run_bwd(const KvArgs &a, const BwdArgs &w, const void *o, int log2g, 
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   const unsigned grid = (unsigned)std::max(1L, std::min(max_runs, 2L * per_cu * cus));
-  hipLaunchKernelGGL((kv_bwd<E, DH, BS>), dim3(grid), dim3(BwdLds<E, DH, BS>::NT), 0, s, a, w, log2g);
+  if (stages & BWD_STAGE_BLOCKS)
+    hipLaunchKernelGGL((kv_bwd<E, DH, BS>), dim3(grid), dim3(BwdLds<E, DH, BS>::NT), 0, s, a, w, log2g);
+  if (!(stages & BWD_STAGE_MERGE)) return hipGetLastError();
   const long threads = (long)a.batch * a.h_kv * a.n_q * ((long)DH << log2g) / 8;
   hipLaunchKernelGGL((dq_merge<E, DH>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, w,
                      log2g);
@@ -614,14 +619,14 @@ size_t kv_bwd_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long 
 
 hipError_t launch_attn_backward(const KvArgs &a, const BwdLayout &lay, unsigned char *ws, const void *o,
                                 const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                                int dtype, int d_h, hipStream_t s) {
+                                int dtype, int d_h, int stages, hipStream_t s) {
   int lg = 0;
   while ((1 << lg) < a.h_q / a.h_kv) ++lg;
   BwdArgs w{dout, lse, reinterpret_cast<const float *>(ws + lay.dsum), reinterpret_cast<float *>(ws + lay.dkv),
             dq, dk, dv, (float)(1.0 / std::sqrt((double)d_h)), lay.run, lay.max_runs};
 #define MSA_BWD(E, DH)                                                                  \
-  if (a.block_size == 32) return run_bwd<E, DH, 32>(a, w, o, lg, lay.max_runs, s);      \
-  return run_bwd<E, DH, 64>(a, w, o, lg, lay.max_runs, s);
+  if (a.block_size == 32) return run_bwd<E, DH, 32>(a, w, o, lg, lay.max_runs, stages, s); \
+  return run_bwd<E, DH, 64>(a, w, o, lg, lay.max_runs, stages, s);
   if (dtype == 0) {
     if (d_h == 64) { MSA_BWD(float, 64) }
     MSA_BWD(float, 128)

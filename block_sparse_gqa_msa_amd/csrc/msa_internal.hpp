@@ -135,10 +135,11 @@ hipError_t launch_index_kl(const KvArgs &a, const KlArgs &k, int dtype, int d_h,
                            hipStream_t s);
 
 hipError_t launch_index_project(const ProjArgs &a, int dtype, int d_idx, hipStream_t s);
-// Main-branch gradients for a fixed selection: lists (plan stage), D, per-block gradients,
-// then the dq merge and the dk/dv reduction.
+// Main-branch gradients for a fixed selection, after the list build (plan stage): D per
+// (b, h, t), the per-block gradients, then the dq merge and the dk/dv reduction.
+enum { BWD_STAGE_ROWDOT = 1, BWD_STAGE_BLOCKS = 2, BWD_STAGE_MERGE = 4, BWD_STAGE_ALL = 7 };
 hipError_t launch_attn_backward(const KvArgs &a, const BwdLayout &lay, unsigned char *ws, const void *o,
                                 const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                                int dtype, int d_h, hipStream_t s);
+                                int dtype, int d_h, int stages, hipStream_t s);
 
 }  // namespace msa

@@ -260,6 +260,25 @@ int msa_sparse_attn_backward(const msa_shape *shape, const void *q, const void *
                              const int32_t *sel, const void *o, const float *lse, const void *dout,
                              void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
                              void *stream);
+/*
+ * The backward in three calls, for callers that schedule or time the stages apart. Called
+ * in this order with the same shape and workspace (whose contents carry over) on one
+ * stream, they compute what msa_sparse_attn_backward computes (dq bit for bit; dk and dv
+ * up to the last-bit effect of the list order described above).
+ *   _plan      reads sel, o and dout: builds the per-block query lists and D = dout . o.
+ *   _partials  reads q, k, v, lse, dout and the lists: writes the dq partials and the
+ *              dk/dv block partials.
+ *   _merge     reads sel and the partials: writes dq, dk and dv.
+ * Arguments mean what they mean for msa_sparse_attn_backward; the same errors apply.
+ */
+int msa_sparse_attn_backward_plan(const msa_shape *shape, const int32_t *sel, const void *o,
+                                  const void *dout, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+int msa_sparse_attn_backward_partials(const msa_shape *shape, const void *q, const void *k,
+                                      const void *v, const float *lse, const void *dout,
+                                      void *workspace, size_t workspace_bytes, void *stream);
+int msa_sparse_attn_backward_merge(const msa_shape *shape, const int32_t *sel, void *dq, void *dk,
+                                   void *dv, void *workspace, size_t workspace_bytes, void *stream);
 /* Text of the last error on the calling thread (empty after a successful call). */
 const char *msa_last_error(void);
 

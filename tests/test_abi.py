@@ -280,3 +280,23 @@ def test_index_project_rejects(lib):
     # the supported set is checked on empty calls too
     e = good(n_q=0)
     assert lib.msa_index_project(ctypes.byref(e), 100, *([None] * 5), None) == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_backward_stage_calls_reject(lib):
+    dummy = 1 << 20
+    s = good()
+    need = msa.msa_sparse_attn_backward_workspace_size(s)
+    sb = ctypes.byref(s)
+    calls = [(lib.msa_sparse_attn_backward_plan, 3), (lib.msa_sparse_attn_backward_partials, 5),
+             (lib.msa_sparse_attn_backward_merge, 4)]
+    for fn, n in calls:
+        for i in range(n):
+            a = [dummy] * n
+            a[i] = None
+            assert fn(sb, *a, dummy, need, None) == msa.MSA_ERR_INVALID_ARG
+            assert "non-NULL" in msa.msa_last_error()
+        assert fn(sb, *([dummy] * n), dummy, need - 1, None) == msa.MSA_ERR_WORKSPACE
+        x = good(d_h=96)
+        assert fn(ctypes.byref(x), *([dummy] * n), dummy, need, None) == msa.MSA_ERR_UNSUPPORTED
+        e = good(n_q=0)
+        assert fn(ctypes.byref(e), *([None] * n), None, 0, None) == msa.MSA_OK

@@ -146,6 +146,29 @@ def test_bwd_kv_capacity_stride():
     check(w, "dv", dv[:, :, : w.n_k], ref["dv"], w.name)
 
 
+def test_bwd_staged_calls_equal_single_call():
+    """_plan, _partials and _merge on one workspace give the single call's dq bit for bit,
+    and its dk, dv up to the order of a list's rows (the list build's atomics)."""
+    w = W("bwd_staged", batch=2, n_q=700, n_k=900, q_start=200, h_q=16, h_kv=2, top_k=6,
+          needles=3)
+    inp = generate(w, device="cuda")
+    dout = generate_dout(w, device="cuda")
+    buf = run_gpu(w, inp)
+    dq, dk, dv = gpu_bwd(w, inp, buf, dout)
+    s = msa.shape_of(w)
+    ws = torch.empty(msa.msa_sparse_attn_backward_workspace_size(s), dtype=torch.uint8,
+                     device="cuda")
+    dq2, dk2, dv2 = (torch.full_like(x, float("nan")) for x in (dq, dk, dv))
+    msa.msa_sparse_attn_backward_plan(s, buf.sel, buf.o, dout, ws)
+    msa.msa_sparse_attn_backward_partials(s, inp["q"], inp["k"], inp["v"], buf.lse, dout, ws)
+    msa.msa_sparse_attn_backward_merge(s, buf.sel, dq2, dk2, dv2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2), "staged dq differs"
+    for a, b in ((dk, dk2), (dv, dv2)):
+        assert torch.isfinite(b).all()
+        assert (a.float() - b.float()).abs().max().item() <= 1e-2 * a.float().abs().max().item()
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def row_problem(w, cpu, dout_cpu, sel_row, b, r, t):
