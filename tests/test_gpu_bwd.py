@@ -96,6 +96,12 @@ SMALL = [
       d_idx=64, block_size=64, top_k=7, needles=5),
     W("bwd_bf16_d64_bs64_g8", n_q=900, n_k=900, h_q=32, h_kv=4, d_h=64, d_idx=32,
       block_size=64, top_k=10, needles=4),
+    # one row at the end of a long cache (the decode shape): a single entry per list
+    W("bwd_decode_row", batch=3, n_q=1, n_k=5000, q_start=4999, top_k=16, needles=4),
+    # one group and many rows: the longest list (block 0, 1132 entries) spans more than one
+    # run of 8 chunks x 128 entries; the first rows' selections are shorter than top_k
+    W("bwd_long_list_runs", n_q=2600, n_k=2600, h_q=8, h_kv=1, d_h=64, d_idx=32,
+      block_size=32, top_k=12, needles=1),
 ]
 
 
