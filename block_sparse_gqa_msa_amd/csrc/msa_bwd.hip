@@ -455,7 +455,7 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
 
 // Each (b, r, row) is summed by LPR = G * DH / 8 consecutive threads, 8 outputs of one head
 // each, over the row's valid slots in slot order.
-template <typename E, int DH>
+template <typename E, int DH, int U>
 __global__ __launch_bounds__(256) void dq_merge(KvArgs a, BwdArgs w, int log2g) {
   const int G = 1 << log2g;
   const int lpr_log2 = log2g + (DH == 128 ? 4 : 3);
@@ -481,26 +481,47 @@ __global__ __launch_bounds__(256) void dq_merge(KvArgs a, BwdArgs w, int log2g) 
   float acc[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+  // U slots' loads in flight together, added in slot order (the same bits as one at a time)
   uint64_t v = mask;
   while (v) {
-    const int sl = __builtin_ctzll(v);
-    v &= v - 1;
-    const E *p = pbase + (long)sl * G * DH;
+    int sl[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      sl[u] = v ? __builtin_ctzll(v) : -1;
+      v &= v - 1;  // no-op once v is 0
+    }
     if constexpr (sizeof(E) == 2) {
-      const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+      u32x4 x[U];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += __uint_as_float(x[e] << 16);
-        acc[2 * e + 1] += __uint_as_float(x[e] & 0xffff0000u);
-      }
+      for (int u = 0; u < U; ++u)
+        x[u] = sl[u] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(pbase + (long)sl[u] * G * DH))
+                          : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (sl[u] >= 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += __uint_as_float(x[u][e] << 16);
+            acc[2 * e + 1] += __uint_as_float(x[u][e] & 0xffff0000u);
+          }
+        }
     } else {
-      const f32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-      const f32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + 1);
+      f32x4 lo[U], hi[U];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += lo[e];
-        acc[4 + e] += hi[e];
+      for (int u = 0; u < U; ++u) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(pbase + (long)(sl[u] >= 0 ? sl[u] : 0) * G * DH);
+        lo[u] = sl[u] >= 0 ? __builtin_nontemporal_load(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+        hi[u] = sl[u] >= 0 ? __builtin_nontemporal_load(p + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (sl[u] >= 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] += lo[u][e];
+            acc[4 + e] += hi[u][e];
+          }
+        }
     }
   }
   const int t = (int)(row % a.n_q);
@@ -587,7 +608,7 @@ hipError_t run_bwd(const KvArgs &a, const BwdArgs &w, const void *o, int log2g, 
     hipLaunchKernelGGL((kv_bwd<E, DH, BS>), dim3(grid), dim3(BwdLds<E, DH, BS>::NT), 0, s, a, w, log2g);
   if (!(stages & BWD_STAGE_MERGE)) return hipGetLastError();
   const long threads = (long)a.batch * a.h_kv * a.n_q * ((long)DH << log2g) / 8;
-  hipLaunchKernelGGL((dq_merge<E, DH>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, w,
+  hipLaunchKernelGGL((dq_merge<E, DH, 8>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, w,
                      log2g);
   hipLaunchKernelGGL((dkv_reduce<E, DH, BS>), dim3((unsigned)((long)a.batch * a.h_kv * a.n_blocks)),
                      dim3(256), 0, s, a, w);
