@@ -11,9 +11,10 @@
 // probabilities are exp(S^(l)_j - lse_l) with no second normalisation pass.
 //
 // Organised like the prefill attention, KV-block-outer over the same per-block row lists:
-//   kv_kl     each chunk stages one block's K and K_idx rows in LDS and, per 16-row tile
-//             (16/G rows x the G heads), computes S = Q K^T and S_idx = Q_idx K_idx^T on the
-//             matrix cores, the teacher weights t_j (the head mean), and per (row, slot)
+//   kv_kl     each chunk stages one block's K and K_idx rows in LDS; per 16 entry rows it
+//             computes S_idx = Q_idx K_idx^T once on the matrix cores (one index head per
+//             group, so the G heads of a row share it) and, per 16-row tile (16/G rows x
+//             the G heads), S = Q K^T, the teacher weights t_j (the head mean), and per (row, slot)
 //             the block's sums A = sum t ln t, B = sum t S^idx, T = sum t and the index
 //             scores' (max, sum of 2^(z - max)) in log2 units.
 //   kl_merge  per (b, r, row), one wave over the row's slots: L = A - B + lse_idx * T with
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   __shared__ int32_t s_list[KV_CHUNK];
   __shared__ float4 s_part[KV_CHUNK];  // the chunk's results, stored once per chunk: a store
   __shared__ float2 s_ml[KV_CHUNK];    // per tile would be waited for with the next loads
+  __shared__ float s_sx[4][16][BS + 1];  // per wave: index scores of 16 entry rows x BS keys
 
   const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
   const int n_chunks = a.coff[NB];
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
     // unconditional (lanes past the chunk's entries read entry 0's row and are masked), so
     // no load sits under a branch.
     struct TileIn {
-      F q[DC], qi[DCI];
+      F q[DC];
       float lse[4];
     };
     // Tile row of accumulator slot ii: the slots of one row are 1 << LG consecutive i, so
@@ -143,9 +145,6 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
       const E *src = q + (((long)b * a.h_q + r * G + hd) * a.n_q + t) * DH + g * 8;
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) d.q[dc] = load_frag(src + dc * 32);
-      const E *srci = qx + (((long)b * a.h_kv + r) * a.n_q + t) * DI + g * 8;
-#pragma unroll
-      for (int dc = 0; dc < DCI; ++dc) d.qi[dc] = load_frag(srci + dc * 32);
       const int t0 = row_of(tt, row_slot(0)) >> 6;  // slot rows: one lookup per row
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -153,10 +152,49 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
         d.lse[ii] = lse_r[(long)((4 * g + ii) & (G - 1)) * a.n_q + tr];
       }
     };
+    // Index scores of entry rows 16 gi .. 16 gi + 15 (the G tiles of row group gi) against
+    // the block's keys, into this wave's LDS tile: s_sx[w][row][key]. The index query is
+    // one head per group, so a tile's G heads share their row's scores and the product is
+    // computed once per row instead of once per head.
+    auto group_scores = [&](int gi) {
+      const int e = gi * 16 + c16;
+      const int t = s_list[e < n_e ? e : 0] >> 6;  // rows past the entries: entry 0, unused
+      const E *srci = qx + (((long)b * a.h_kv + r) * a.n_q + t) * DI + g * 8;
+      F aq[DCI];
+#pragma unroll
+      for (int dc = 0; dc < DCI; ++dc) aq[dc] = load_frag(srci + dc * 32);
+      f32x4 sx[KTN];
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt) sx[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < DCI; ++dc) {
+        F kif[KTN];
+#pragma unroll
+        for (int kt = 0; kt < KTN; ++kt)
+          kif[kt] = load_frag(reinterpret_cast<const E *>(s_ki + (kt * 16 + c16) * IROW +
+                                                         (dc * 32 + g * 8) * ES));
+#pragma unroll
+        for (int kt = 0; kt < KTN; ++kt) sx[kt] = mfma_chunk(aq[dc], kif[kt], sx[kt]);
+      }
+#pragma unroll
+      for (int kt = 0; kt < KTN; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_sx[w][4 * g + i][kt * 16 + c16] = sx[kt][i];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // wave-private tile: in-order LDS
+    };
+    // Wave w takes row groups w, w + 4, ... and the G tiles of each in turn.
+    const int n_grp = (n_e + 15) / 16;
+    int gi = w, u = 0, tt = w * G;
     TileIn cur, nxt;
-    load_tile(w, cur);
-    for (int tt = w; tt < n_tiles; tt += 4) {
-      load_tile(tt + 4, nxt);
+    load_tile(tt, cur);
+    while (gi < n_grp) {  // uniform over the wave
+      if (u == 0) group_scores(gi);
+      int gn = gi, un = u + 1;
+      if (un == G || gn * G + un >= n_tiles) {
+        gn = gi + 4;
+        un = 0;
+      }
+      load_tile(gn * G + un, nxt);
       // an opaque zero offset keeps the compiler from hoisting the fragment reads below
       // out of the loop (kept in registers they would cost about a hundred VGPRs and a
       // third of the resident waves)
@@ -165,12 +203,9 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
       // The KTN key tiles' products run as independent accumulation chains, one
       // d-chunk at a time (a chunk's fragments of every key tile are read first), so that
       // consecutive matrix-core operations do not wait on each other's results.
-      f32x4 s[KTN], si[KTN];
+      f32x4 s[KTN];
 #pragma unroll
-      for (int kt = 0; kt < KTN; ++kt) {
-        s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        si[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int kt = 0; kt < KTN; ++kt) s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc) {
         F kf[KTN];
@@ -181,15 +216,13 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
 #pragma unroll
         for (int kt = 0; kt < KTN; ++kt) s[kt] = mfma_chunk(cur.q[dc], kf[kt], s[kt]);
       }
+      // this lane's index scores: row slot j's row of the group, key kt * 16 + c16
+      float sv[KTN][R4];
 #pragma unroll
-      for (int dc = 0; dc < DCI; ++dc) {
-        F kif[KTN];
+      for (int j = 0; j < R4; ++j) {
+        const int rho = u * QPT + row_slot(j << LG);
 #pragma unroll
-        for (int kt = 0; kt < KTN; ++kt)
-          kif[kt] = load_frag(reinterpret_cast<const E *>(s_ki + lds0 + (kt * 16 + c16) * IROW +
-                                                         (dc * 32 + g * 8) * ES));
-#pragma unroll
-        for (int kt = 0; kt < KTN; ++kt) si[kt] = mfma_chunk(cur.qi[dc], kif[kt], si[kt]);
+        for (int kt = 0; kt < KTN; ++kt) sv[kt][j] = s_sx[w][rho][kt * 16 + c16];
       }
       // per value slot: the key offset c16 of each tile is visible to its row iff <= lim
       int lim[4];
@@ -239,12 +272,12 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
         for (int j = 0; j < R4; ++j) {
           const int ii = j << LG;
           const float t = hs[j] * inv_g;
-          const float sidx = si[kt][ii] * k.scale_idx;  // S^idx, natural units
+          const float sidx = sv[kt][j] * k.scale_idx;  // S^idx, natural units
           // t ln t, 0 at t = 0 (the clamp keeps the logarithm finite)
           sa[j] += t * (__builtin_amdgcn_logf(fmaxf(t, 1e-30f)) * 0.69314718055994531f);
           sb[j] += t * sidx;
           st[j] += t;
-          zm[j] = key <= lim[ii] ? fmaxf(zm[j], si[kt][ii] * ci) : zm[j];
+          zm[j] = key <= lim[ii] ? fmaxf(zm[j], sv[kt][j] * ci) : zm[j];
         }
       }
       // the tile's rows: totals over the 16 keys of each key tile (lanes of a row of 16)
@@ -255,7 +288,7 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
         float zl = 0.f;
 #pragma unroll
         for (int kt = 0; kt < KTN; ++kt)
-          zl += kt * 16 + c16 <= lim[ii] ? __builtin_amdgcn_exp2f(si[kt][ii] * ci - M) : 0.f;
+          zl += kt * 16 + c16 <= lim[ii] ? __builtin_amdgcn_exp2f(sv[kt][j] * ci - M) : 0.f;
         zl = sum16(zl);
         const float ta = sum16(sa[j]), tb = sum16(sb[j]), tt_ = sum16(st[j]);
         const int e = tt * QPT + row_slot(ii);
@@ -265,6 +298,9 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
         }
       }
       cur = nxt;
+      gi = gn;
+      u = un;
+      tt = gn * G + un;
     }
     __syncthreads();
     for (int e = tid; e < n_e; e += 256) {
