@@ -5,7 +5,9 @@ groups, d_h 128, index d_idx 64, blocks of 64, top_k 32, bf16): one step is the 
 branch (block scores, top-k) plus the sparse prefill attention over all 131072 rows.
 The same line carries, each with the roofline of its dominant kernel and the fp64
 oracle timed on a bounded sample on the host cores:
-  decode         the 1M-token decode (batch 4, one new token each, same heads);
+  decode         the 1M-token decode (batch 4, one new token each, same heads), as the
+                 two calls msa_index_topk + msa_sparse_attn_decode, and also as one
+                 msa_decode_step call (decode_step_call);
   index_kl       the index branch's alignment loss on the prefill's selection;
   attn_backward  the main branch's backward (dq, dk, dv) for that selection;
   index_project  the index branch's two projections from hidden states of width h_q * d_h.
@@ -234,6 +236,30 @@ def time_step(w, inputs, steps, warmup, decode):
         times["index_project"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
         del hid, q_idx_p, k_idx_p
     return wall, times
+
+
+def time_decode_step(w, inputs, steps, warmup):
+    """Seconds per decode step made as one msa_decode_step call (index kernel, then one
+    kernel for the final selection, the attention and the merge), same inputs."""
+    import torch
+    from block_sparse_gqa_msa_amd import binding as msa
+
+    s = msa.shape_of(w)
+    sel = torch.empty((w.batch, w.h_kv, 1, w.top_k), dtype=torch.int32, device="cuda")
+    o = torch.empty((w.batch, w.h_q, 1, w.d_h), dtype=inputs["q"].dtype, device="cuda")
+    lse = torch.empty((w.batch, w.h_q, 1), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, msa.msa_decode_step_workspace_size(s)), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: msa.msa_decode_step(s, inputs["q"], inputs["k"], inputs["v"],
+                                       inputs["q_idx"], inputs["k_idx"], sel, o, lse, ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -505,6 +531,8 @@ def main():
     inp = generate(wd, device="cuda")
     log(f"[bench] decode {wd.name}: warmup {args.warmup}, steps {args.decode_steps}")
     dwall, dkt = time_step(wd, inp, args.decode_steps, args.warmup, decode=True)
+    fused_ms = time_decode_step(wd, inp, args.decode_steps, args.warmup) * 1e3
+    log(f"[bench] decode as one msa_decode_step call: {fused_ms * 1e3:.1f} us/step")
     d_bytes, d_index_bytes, _ = decode_work(wd)
     t_idx = dkt["index_topk"]
     droof = dict(kernel="index_select_decode+topk_merge_wide", bound="hbm",
@@ -552,6 +580,8 @@ def main():
             "path_hbm": dict(bytes=d_bytes, gbs=d_bytes / dwall / 1e9,
                              hbm_frac=d_bytes / dwall / PEAK_HBM_BYTES),
             "kernel_ms": {k: v * 1e3 for k, v in dkt.items()},
+            "decode_step_call": {"ms_per_step": fused_ms, "value": wd.batch / (fused_ms * 1e-3),
+                                 "hbm_frac": d_bytes / (fused_ms * 1e-3) / PEAK_HBM_BYTES},
             "cpu_baseline": cpu_d,
         },
     }

@@ -27,6 +27,7 @@ EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_s
            "msa_sparse_attn_backward_workspace_size", "msa_sparse_attn_backward",
            "msa_sparse_attn_backward_plan", "msa_sparse_attn_backward_partials",
            "msa_sparse_attn_backward_merge", "msa_index_project",
+           "msa_decode_step_workspace_size", "msa_decode_step",
            "msa_last_error", "msa_abi_version")
 
 
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_backward_partials.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_backward_merge.argtypes = [S, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_decode_step_workspace_size.argtypes = [S, sz]
+    lib.msa_decode_step.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     for f in EXPORTS:
         if f == "msa_last_error":
             continue
@@ -253,6 +256,24 @@ def msa_sparse_attn_decode(shape: MsaShape, q, k_cache, v_cache, sel, o, lse=Non
         ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k_cache, et, "k_cache"),
         _ptr(v_cache, et, "v_cache"), _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"),
         _ptr(lse, torch.float32, "lse"), wp, wn, _stream(stream, o)))
+
+
+def msa_decode_step_workspace_size(shape: MsaShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_decode_step_workspace_size(ctypes.byref(shape), ctypes.byref(n)))
+    return int(n.value)
+
+
+def msa_decode_step(shape: MsaShape, q, k_cache, v_cache, q_idx, k_idx, sel, o, lse=None,
+                    workspace=None, stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_decode_step(
+        ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k_cache, et, "k_cache"),
+        _ptr(v_cache, et, "v_cache"), _ptr(q_idx, et, "q_idx"), _ptr(k_idx, et, "k_idx"),
+        _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"), _ptr(lse, torch.float32, "lse"), wp, wn,
+        _stream(stream, o)))
 
 
 def msa_index_kl(shape: MsaShape, q, k, q_idx, k_idx, sel, lse, kl, lse_idx=None,

@@ -145,6 +145,37 @@ size_t attn_decode_ws(const msa_shape &s) {
   return align_up(parts * s.d_h * sizeof(float)) + align_up(parts * 2 * sizeof(float));
 }
 
+// msa_decode_step's workspace: arrival counters, then the index branch's workspace, then
+// the attention's (decode partials).
+struct StepWs {
+  size_t cnt, idx, attn, total;
+};
+int step_ws(const msa_shape &s, StepWs *w) {
+  IndexWs iw;
+  int rc = index_ws(s, true, &iw);
+  if (rc) return rc;
+  w->cnt = align_up((size_t)s.batch * s.h_kv * sizeof(int32_t));
+  w->idx = align_up(iw.total);
+  w->attn = attn_decode_ws(s);
+  w->total = w->cnt + w->idx + w->attn;
+  return MSA_OK;
+}
+
+// Workgroups per (sequence, group) in the fused decode kernel: enough that every wave
+// attends about one selected block, no more than about one workgroup per compute unit.
+int finish_subs(const msa_shape &s) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const long long pairs = (long long)s.batch * s.h_kv;
+  const long long by_blocks = (s.top_k + 3) / 4;
+  const long long by_cus = cus / pairs;
+  long long subs = by_blocks < by_cus ? by_blocks : by_cus;
+  if (subs > msa::FINISH_MAX_SUBS) subs = msa::FINISH_MAX_SUBS;
+  return subs < 1 ? 1 : (int)subs;
+}
+
 int hip_fail(hipError_t e, const char *what) {
   return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -598,6 +629,72 @@ int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_
                   (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};
   hipError_t e = msa::launch_attn_decode(a, s.dtype, s.d_h, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+  return ok();
+}
+
+int msa_decode_step_workspace_size(const msa_shape *shape, size_t *bytes) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_index_dims(*shape)) || (rc = check_attn_dims(*shape))) return rc;
+  if (!bytes) return fail(MSA_ERR_INVALID_ARG, "bytes is NULL");
+  if (empty(*shape)) {
+    *bytes = 0;
+    return ok();
+  }
+  StepWs w;
+  if ((rc = step_ws(*shape, &w))) return rc;
+  *bytes = w.total;
+  return ok();
+}
+
+int msa_decode_step(const msa_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                    const void *q_idx, const void *k_idx, int32_t *sel, void *o, float *lse,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if ((rc = check_index_dims(s)) || (rc = check_attn_dims(s))) return rc;
+  if (s.n_q != 1 || s.q_start != s.n_k - 1)
+    return fail(MSA_ERR_INVALID_ARG, "decode needs n_q == 1 and q_start == n_k - 1 (got %d, %d, n_k %d)",
+                s.n_q, s.q_start, s.n_k);
+  if (empty(s)) return ok();
+  if (!q || !k_cache || !v_cache || !q_idx || !k_idx || !sel || !o)
+    return fail(MSA_ERR_INVALID_ARG, "q, k_cache, v_cache, q_idx, k_idx, sel and o must be non-NULL");
+  StepWs w;
+  if ((rc = step_ws(s, &w))) return rc;
+  if (!workspace || workspace_bytes < w.total)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
+                workspace ? workspace_bytes : (size_t)0);
+  unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
+  unsigned char *ws_idx = ws + w.cnt, *ws_attn = ws + w.cnt + w.idx;
+  if (!fused_decode_ok(s)) {  // k == 1, or too many candidates for one merge: the two calls
+    if ((rc = msa_index_topk(shape, q_idx, k_idx, sel, nullptr, ws_idx, w.idx, stream))) return rc;
+    return msa_sparse_attn_decode(shape, q, k_cache, v_cache, sel, o, lse, ws_attn, w.attn, stream);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  IndexWs iw;
+  if ((rc = index_ws(s, true, &iw))) return rc;
+  uint32_t *ck = reinterpret_cast<uint32_t *>(ws_idx);
+  int32_t *ci = reinterpret_cast<int32_t *>(ws_idx + iw.dec_cand);
+  int32_t *cnt = reinterpret_cast<int32_t *>(ws);
+  msa::IndexArgs ia{q_idx, k_idx, nullptr, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
+                    (int)n_blocks(s), cap_of(s), 0, ck, ci, s.top_k};
+  ia.zero = cnt;
+  ia.n_zero = s.batch * s.h_kv;
+  hipError_t e = msa::launch_index_select_decode(ia, s.dtype, s.d_idx, s.block_size, st);
+  if (e != hipSuccess) return hip_fail(e, "index-select kernel launch");
+  const int subs = finish_subs(s);
+  const int S = decode_splits(s);
+  const size_t parts = (size_t)s.batch * s.h_q * S;  // >= pairs * subs * G: subs <= top_k
+  msa::AttnArgs a{q, k_cache, v_cache, sel, o, lse,
+                  reinterpret_cast<float *>(ws_attn),
+                  reinterpret_cast<float *>(ws_attn + align_up(parts * s.d_h * sizeof(float))),
+                  s.batch, 1, s.n_k, s.q_start, s.h_q, s.h_kv, s.block_size, s.top_k, cap_of(s),
+                  S, (s.top_k + S - 1) / S,
+                  (float)(1.4426950408889634 / std::sqrt((double)s.d_h))};
+  msa::FinishArgs f{ck, ci, sel, cnt, decode_select_wgs(s), subs};
+  e = msa::launch_decode_finish(a, f, s.dtype, s.d_h, st);
+  if (e != hipSuccess) return hip_fail(e, "decode finish launch");
   return ok();
 }
 

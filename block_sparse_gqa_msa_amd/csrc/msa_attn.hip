@@ -19,6 +19,7 @@
 // log-sum-exp weights. The split is fixed on the host, so no atomics are used.
 #include "msa_device.hpp"
 #include "msa_internal.hpp"
+#include "msa_select.hpp"
 
 namespace msa {
 namespace {
@@ -307,6 +308,195 @@ __global__ __launch_bounds__(256) void attn_decode_merge(AttnArgs a) {
   if (a.lse && lane == 0) a.lse[bh] = (M + __log2f(L)) * 0.69314718055994531f;
 }
 
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+
+template <typename E>
+__device__ __forceinline__ void store1(E *dst, float x) {
+  if constexpr (sizeof(E) == 2)
+    *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+  else
+    *reinterpret_cast<float *>(dst) = x;
+}
+
+// Decode, everything after the index kernel in one launch. Grid: x = (b, r) pair * subs +
+// sub; four waves.
+//   1. Every workgroup of a pair merges the pair's per-range winners into the selection (the
+//      two stages of the wide merge; sub 0 also writes sel). Repeating this small merge in
+//      each of the pair's few workgroups costs less than a launch between them.
+//   2. Wave w attends the selected blocks e0 + w, e0 + w + 4, ... of the sub's share
+//      [e0, e1), one online softmax per wave.
+//   3. The four waves' (o, m, l) are merged in LDS into the sub's partial.
+//   4. With one workgroup per pair it writes o and lse. Otherwise each workgroup stores its
+//      partial and bumps the pair's device-scope counter; the last to arrive merges the
+//      pair's partials in sub order. The counters are cleared by the index kernel of the
+//      same step, so a step needs no clearing launch of its own.
+template <typename E, int DH, int BS>
+__global__ __launch_bounds__(256) void decode_finish(AttnArgs a, FinishArgs f, int log2g) {
+  using F = typename Frag<E>::type;
+  using VS = VStage<E, DH, BS>;
+  constexpr int DC = DH / 32, DT = DH / 16;
+  constexpr int SEL_BYTES = 8 * SELECT_LDS * 4 + 2 * 256 * 4;  // lk, li per wave; w_key, w_idx
+  constexpr int MRG_BYTES = 4 * 16 * DH * 4 + 4 * 16 * 8;      // per wave: o[16][DH], (m, l)[16]
+  constexpr int BUF = cmax(4 * VS::BYTES, cmax(SEL_BYTES, MRG_BYTES));
+  __shared__ __attribute__((aligned(16))) unsigned char s_buf[BUF];
+  __shared__ int32_t s_sel[64];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int G = 1 << log2g, R = a.h_kv, k = a.top_k, m = k - 1;
+  const int pair = blockIdx.x / f.subs, sub = blockIdx.x % f.subs;
+  const int b = pair / R, r = pair % R;
+  const long p = (long)a.q_start;
+  const int local = (int)(p / a.block_size);
+
+  // the query rows (G heads of the pair, rows of a 16-row tile) load while the selection runs
+  const bool row_valid = c16 < G;
+  const int h = r * G + (c16 & (G - 1));
+  const E *q = reinterpret_cast<const E *>(a.q);
+  F bq[DC];
+#pragma unroll
+  for (int dc = 0; dc < DC; ++dc)
+    bq[dc] = load_frag(q + ((long)b * a.h_q + h) * DH + dc * 32 + g * 8);  // rows >= G: masked
+
+  // 1. selection
+  if (local + 1 <= k || m == 0) {  // sees k blocks or fewer, or k == 1 (uniform)
+    if (tid < k) s_sel[tid] = local + 1 <= k ? (tid <= local ? tid : -1) : (tid == 0 ? local : -1);
+  } else {
+    uint32_t *lk = reinterpret_cast<uint32_t *>(s_buf) + w * SELECT_LDS;
+    int32_t *li = reinterpret_cast<int32_t *>(s_buf) + (4 + w) * SELECT_LDS;
+    uint32_t *w_key = reinterpret_cast<uint32_t *>(s_buf) + 8 * SELECT_LDS;
+    int32_t *w_idx = reinterpret_cast<int32_t *>(s_buf) + 8 * SELECT_LDS + 256;
+    const int nch = (local + SEL_NBLK - 1) / SEL_NBLK;  // ranges holding candidates
+    const long base = (long)pair * f.n_wg * m;
+    wide_stage1<4>(f.cand_key + base, f.cand_idx + base, nch * m, m, w, lk, li, w_key, w_idx);
+    __syncthreads();
+    if (w == 0) {
+      wide_stage2<4>(m, w_key, w_idx, lk, li, [&](int j, int32_t c) { s_sel[j] = c; });
+      if (lane == 0) s_sel[m] = local;
+    }
+  }
+  __syncthreads();
+  if (sub == 0 && tid < k) f.sel[(long)pair * k + tid] = s_sel[tid];
+
+  // 2. attention over the sub's share of the selected blocks
+  const long plane = ((long)b * R + r) * (long)a.cap * DH;
+  const E *kp = reinterpret_cast<const E *>(a.k) + plane;
+  const E *vp = reinterpret_cast<const E *>(a.v) + plane;
+  RowState<E, DH, BS> st;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const int per = (k + f.subs - 1) / f.subs;
+  const int e0 = sub * per, e1 = min(e0 + per, k);
+  for (int e = e0 + w; e < e1; e += 4) {
+    const int c = s_sel[e];
+    if (c < 0) continue;  // wave-uniform
+    attend_block<E, DH, BS>(st, bq, kp, vp, (long)c * BS, a.n_k, row_valid, p, a.scale_log2,
+                            s_buf + w * VS::BYTES);
+  }
+
+  // 3. the four waves' partials, merged in LDS (the V^T regions are free once all are done)
+  __syncthreads();
+  float *mo = reinterpret_cast<float *>(s_buf);                       // [4][16][DH]
+  float2 *mml = reinterpret_cast<float2 *>(s_buf + 4 * 16 * DH * 4);  // [4][16]
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<f32x4 *>(mo + (w * 16 + c16) * DH + dt * 16 + g * 4) = st.o[dt];
+  if (g == 0) mml[w * 16 + c16] = make_float2(st.m, st.l);
+  __syncthreads();
+  E *o = reinterpret_cast<E *>(a.o);
+  const int n_out = G * DH;
+  for (int x = tid; x < n_out; x += 256) {
+    const int hh = x / DH, d = x % DH;
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float2 ml = mml[u * 16 + hh];
+      if (ml.y > 0.f) M = fmaxf(M, ml.x);
+    }
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float2 ml = mml[u * 16 + hh];
+      if (ml.y > 0.f) {
+        const float wt = __builtin_amdgcn_exp2f(ml.x - M);
+        L += wt * ml.y;
+        O += wt * mo[(u * 16 + hh) * DH + d];
+      }
+    }
+    const long bh = (long)b * a.h_q + r * G + hh;
+    if (f.subs == 1) {  // the whole selection: final output (the local block makes L > 0)
+      store1(o + bh * DH + d, O / L);
+      if (a.lse && d == 0) a.lse[bh] = (M + __log2f(L)) * 0.69314718055994531f;
+    } else {
+      const long sp = ((long)pair * f.subs + sub) * G + hh;
+      a.part_o[sp * DH + d] = O;
+      if (d == 0) {
+        a.part_ml[sp * 2] = M;
+        a.part_ml[sp * 2 + 1] = L;
+      }
+    }
+  }
+  if (f.subs == 1) return;
+
+  // 4. the last workgroup of the pair to arrive merges the subs' partials. One thread per
+  // workgroup fences: a device-scope fence writes back (release) or invalidates (acquire)
+  // the XCD's L2, so one per thread would repeat that 256 times; the barrier before it
+  // makes the other threads' stores part of what it releases, the one after it orders the
+  // other threads' loads after what it acquires.
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();  // the workgroup's partials are visible device-wide before its count
+    s_last = atomicAdd(f.cnt + pair, 1) == f.subs - 1;
+    if (s_last) __threadfence();  // the other workgroups' partials are read after their counts
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // Four consecutive outputs of one head per thread; every sub's (m, l) and partial of them
+  // load together (subs <= FINISH_MAX_SUBS; past subs the last one is re-read and weighted 0).
+  const float2 *pml = reinterpret_cast<const float2 *>(a.part_ml);
+  for (int x4 = tid; x4 < n_out / 4; x4 += 256) {
+    const int hh = (x4 * 4) / DH, d0 = (x4 * 4) % DH;
+    const long sp0 = (long)pair * f.subs * G + hh;  // sub u's partial: sp0 + u * G
+    float2 ml[FINISH_MAX_SUBS];
+    f32x4 po[FINISH_MAX_SUBS];
+#pragma unroll
+    for (int u = 0; u < FINISH_MAX_SUBS; ++u) {
+      const long sp = sp0 + (long)min(u, f.subs - 1) * G;
+      ml[u] = pml[sp];
+      po[u] = *reinterpret_cast<const f32x4 *>(a.part_o + sp * DH + d0);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < FINISH_MAX_SUBS; ++u)
+      if (u < f.subs && ml[u].y > 0.f) M = fmaxf(M, ml[u].x);
+    float L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < FINISH_MAX_SUBS; ++u) {
+      const float wt = (u < f.subs && ml[u].y > 0.f) ? __builtin_amdgcn_exp2f(ml[u].x - M) : 0.f;
+      L += wt * ml[u].y;
+      O += wt * po[u];
+    }
+    const long bh = (long)b * a.h_q + r * G + hh;
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store1(o + bh * DH + d0 + e, O[e] * inv);
+    if (a.lse && d0 == 0) a.lse[bh] = (M + __log2f(L)) * 0.69314718055994531f;
+  }
+}
+
+template <typename E, int DH>
+hipError_t finish_t(const AttnArgs &a, const FinishArgs &f, int bs, int log2g, hipStream_t s) {
+  const dim3 grid((unsigned)((long)a.batch * a.h_kv * f.subs));
+  if (bs == 32)
+    hipLaunchKernelGGL((decode_finish<E, DH, 32>), grid, dim3(256), 0, s, a, f, log2g);
+  else
+    hipLaunchKernelGGL((decode_finish<E, DH, 64>), grid, dim3(256), 0, s, a, f, log2g);
+  return hipGetLastError();
+}
+
 template <typename E, int DH>
 hipError_t decode_t(const AttnArgs &a, int bs, int log2g, hipStream_t s) {
   const long waves = (long)a.batch * a.h_kv * a.splits;
@@ -329,6 +519,15 @@ int ilog2(int x) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_finish(const AttnArgs &a, const FinishArgs &f, int dtype, int d_h,
+                                hipStream_t s) {
+  const int lg = ilog2(a.h_q / a.h_kv);
+  if (dtype == 0) return d_h == 64 ? finish_t<float, 64>(a, f, a.block_size, lg, s)
+                                   : finish_t<float, 128>(a, f, a.block_size, lg, s);
+  return d_h == 64 ? finish_t<bf16_t, 64>(a, f, a.block_size, lg, s)
+                   : finish_t<bf16_t, 128>(a, f, a.block_size, lg, s);
+}
 
 hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s) {
   const int lg = ilog2(a.h_q / a.h_kv);

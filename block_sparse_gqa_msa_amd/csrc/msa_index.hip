@@ -273,6 +273,9 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
   const int c0 = wg * SEL_NBLK;
 
   for (int x = tid; x < 16 * SEL_NBLK; x += SEL_WAVES * 64) (&s_m[0][0])[x] = -INFINITY;
+  // counters of the kernel that follows in the same decode step start at zero
+  if (wg == 0 && b == 0)
+    for (int x = tid; x < a.n_zero; x += SEL_WAVES * 64) a.zero[x] = 0;
   __syncthreads();
 
   const E *qi = reinterpret_cast<const E *>(a.q_idx);

@@ -17,6 +17,8 @@ struct IndexArgs {
   uint32_t *cand_key;  // [B, R, n_wg, top_k - 1] best blocks of each workgroup's range
   int32_t *cand_idx;
   int top_k;
+  int32_t *zero = nullptr;  // index_select_decode: n_zero words cleared for the next kernel
+  int n_zero = 0;
 };
 
 constexpr int SEL_NBLK = 256;  // key blocks per fused decode index-select workgroup
@@ -45,6 +47,17 @@ struct AttnArgs {
   int splits;          // decode: number of splits S
   int blocks_per_split;
   float scale_log2;    // log2(e) / sqrt(DH)
+};
+
+constexpr int FINISH_MAX_SUBS = 16;  // workgroups per (sequence, group) in decode_finish
+
+struct FinishArgs {          // decode: final selection, attention and merge in one kernel
+  const uint32_t *cand_key;  // [B, R, n_wg, top_k - 1] per-range winners of index_select_decode
+  const int32_t *cand_idx;
+  int32_t *sel;              // [B, R, top_k] out
+  int32_t *cnt;              // [B, R] arrival counters, zero when the kernel starts
+  int n_wg;                  // key ranges per sequence (the candidates' stride)
+  int subs;                  // workgroups per (sequence, group)
 };
 
 struct KvArgs {          // KV-outer prefill attention
@@ -130,6 +143,8 @@ hipError_t launch_index_select_decode(const IndexArgs &a, int dtype, int d_idx, 
 enum { KV_STAGE_PLAN = 1, KV_STAGE_ATTEND = 2, KV_STAGE_MERGE = 4, KV_STAGE_ALL = 7 };
 hipError_t launch_attn_prefill_kv(const KvArgs &a, int dtype, int d_h, int stages, hipStream_t s);
 hipError_t launch_attn_decode(const AttnArgs &a, int dtype, int d_h, hipStream_t s);
+hipError_t launch_decode_finish(const AttnArgs &a, const FinishArgs &f, int dtype, int d_h,
+                                hipStream_t s);
 // Alignment loss from the lists a plan stage built: per-selection sums, then the merge.
 hipError_t launch_index_kl(const KvArgs &a, const KlArgs &k, int dtype, int d_h, int d_idx,
                            hipStream_t s);

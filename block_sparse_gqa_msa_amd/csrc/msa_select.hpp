@@ -14,6 +14,7 @@
 #pragma once
 
 #include "msa_device.hpp"
+#include "msa_internal.hpp"
 
 namespace msa {
 
@@ -154,6 +155,89 @@ __device__ int wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V],
 
 __device__ __forceinline__ bool taken(uint32_t k, int32_t i, uint32_t ks, int32_t is) {
   return k != 0u && (k > ks || (k == ks && i <= is));
+}
+
+// Final merge of one problem whose candidates are the winners of its key ranges (total
+// pairs ck / ci, at most TOPK_CHUNK, in ascending block order), by NW waves of a workgroup.
+// Stage 1 (every wave): wave w keeps the best m of its share, in item order, as entries
+// [w * m, (w + 1) * m) of w_key / w_idx (NW * 64 entries), padded with key 0. lk / li: the
+// wave's own SELECT_LDS entries of scratch.
+template <int NW>
+__device__ __forceinline__ void wide_stage1(const uint32_t *ck, const int32_t *ci, int total,
+                                            int m, int w, uint32_t *lk, int32_t *li,
+                                            uint32_t *w_key, int32_t *w_idx) {
+  constexpr int NV = TOPK_CHUNK / (64 * NW);  // candidates per lane
+  const int lane = lane_id();
+  uint32_t key[NV];
+  int32_t idx[NV];
+  int nv = 0;
+#pragma unroll
+  for (int s = 0; s < NV; ++s) {
+    const int ec = min((w * NV + s) * 64 + lane, total - 1);  // unconditional loads
+    key[s] = ck[ec];
+    idx[s] = ci[ec];
+  }
+#pragma unroll
+  for (int s = 0; s < NV; ++s) {
+    pin(key[s]);
+    pin(idx[s]);
+  }
+#pragma unroll
+  for (int s = 0; s < NV; ++s) {
+    const bool in = (w * NV + s) * 64 + lane < total;
+    key[s] = in ? key[s] : 0u;
+    idx[s] = in ? idx[s] : 0x7fffffff;
+    nv += popc64(ballot(key[s] != 0u));
+  }
+  uint32_t ks = 0;
+  int32_t is = 0x7fffffff;
+  if (nv > m) wave_threshold(key, idx, m, lk, li, ks, is);
+  int pos = 0;
+#pragma unroll
+  for (int s = 0; s < NV; ++s) {
+    const bool pr = taken(key[s], idx[s], ks, is);
+    const uint64_t mk = ballot(pr);
+    if (pr) {
+      w_key[w * m + pos + rank_below(mk)] = key[s];
+      w_idx[w * m + pos + rank_below(mk)] = idx[s];
+    }
+    pos += popc64(mk);
+  }
+  if (lane >= pos && lane < m) {
+    w_key[w * m + lane] = 0u;
+    w_idx[w * m + lane] = 0x7fffffff;
+  }
+}
+
+// Stage 2 (one wave, after the workgroup has synchronised on stage 1): the best m of the
+// NW * m entries, entry j in lane j % 64 (packed this way the winners spread over all
+// lanes, which keeps the lane-maximum bound of the selection tight; a wave-per-slot layout
+// leaves them on m lanes, and the bound admits nearly all). The waves' winners arrive in
+// ascending block order and each wave kept its own in that order, so the winners come out
+// in ascending block order: put(j, block) for j = 0 .. m-1.
+template <int NW, typename Put>
+__device__ __forceinline__ void wide_stage2(int m, const uint32_t *w_key, const int32_t *w_idx,
+                                            uint32_t *lk, int32_t *li, Put put) {
+  const int lane = lane_id();
+  uint32_t k2[NW];
+  int32_t i2[NW];
+#pragma unroll
+  for (int s = 0; s < NW; ++s) {
+    const int j = s * 64 + lane;
+    k2[s] = j < NW * m ? w_key[j] : 0u;
+    i2[s] = j < NW * m ? w_idx[j] : 0x7fffffff;
+  }
+  uint32_t ks = 0;
+  int32_t is = 0x7fffffff;
+  wave_threshold(k2, i2, m, lk, li, ks, is);
+  int pos = 0;
+#pragma unroll
+  for (int s = 0; s < NW; ++s) {
+    const bool pr = taken(k2[s], i2[s], ks, is);
+    const uint64_t mk = ballot(pr);
+    if (pr) put(pos + rank_below(mk), i2[s]);
+    pos += popc64(mk);
+  }
 }
 
 }  // namespace msa

@@ -187,10 +187,9 @@ __global__ __launch_bounds__(256) void topk_pass2(TopkArgs a) {
 
 // Final merge for few problems with many candidates (decode: one problem per (sequence,
 // group), the winners of every key range of the sequence): a workgroup of MW waves per
-// problem. Each wave keeps the best m of its share of the candidates; the first wave then
-// takes the best m of those MW * m and writes them in ascending block order, local block last.
-constexpr int MW = 8;            // waves per problem
-constexpr int MV = TOPK_CHUNK / (64 * MW);  // candidates per lane in the first stage
+// problem runs the two stages of the wide merge and writes the winners in ascending block
+// order, local block last.
+constexpr int MW = 8;  // waves per problem
 
 __global__ __launch_bounds__(MW * 64) void topk_merge_wide(TopkArgs a) {
   __shared__ uint32_t s_key[MW][SELECT_LDS];
@@ -216,74 +215,11 @@ __global__ __launch_bounds__(MW * 64) void topk_merge_wide(TopkArgs a) {
   }
   const int nch = (local + a.chunk_blocks - 1) / a.chunk_blocks;
   const int total = nch * m;  // <= TOPK_CHUNK (checked on the host)
-  const uint32_t *ck = a.cand_key + pid * a.n_chunks * (long)m;
-  const int32_t *ci = a.cand_idx + pid * a.n_chunks * (long)m;
-  // Stage 1: wave w ranks items [w * 64 * MV, (w + 1) * 64 * MV).
-  uint32_t key[MV];
-  int32_t idx[MV];
-  int nv = 0;
-#pragma unroll
-  for (int s = 0; s < MV; ++s) {
-    const int ec = min((w * MV + s) * 64 + lane, total - 1);  // unconditional loads
-    key[s] = ck[ec];
-    idx[s] = ci[ec];
-  }
-#pragma unroll
-  for (int s = 0; s < MV; ++s) {
-    pin(key[s]);
-    pin(idx[s]);
-  }
-#pragma unroll
-  for (int s = 0; s < MV; ++s) {
-    const bool in = (w * MV + s) * 64 + lane < total;
-    key[s] = in ? key[s] : 0u;
-    idx[s] = in ? idx[s] : 0x7fffffff;
-    nv += popc64(ballot(key[s] != 0u));
-  }
-  uint32_t ks = 0;
-  int32_t is = 0x7fffffff;
-  if (nv > m) wave_threshold(key, idx, m, s_key[w], s_idx[w], ks, is);
-  // Wave w's winners (at most m) go to entries [w * m, (w + 1) * m), padded with key 0.
-  int pos = 0;
-#pragma unroll
-  for (int s = 0; s < MV; ++s) {
-    const bool pr = taken(key[s], idx[s], ks, is);
-    const uint64_t mk = ballot(pr);
-    if (pr) {
-      w_key[w * m + pos + rank_below(mk)] = key[s];
-      w_idx[w * m + pos + rank_below(mk)] = idx[s];
-    }
-    pos += popc64(mk);
-  }
-  if (lane >= pos && lane < m) {
-    w_key[w * m + lane] = 0u;
-    w_idx[w * m + lane] = 0x7fffffff;
-  }
+  wide_stage1<MW>(a.cand_key + pid * a.n_chunks * (long)m, a.cand_idx + pid * a.n_chunks * (long)m,
+                  total, m, w, s_key[w], s_idx[w], w_key, w_idx);
   __syncthreads();
   if (w != 0) return;
-  // Stage 2: the best m of the MW * m entries, entry j in lane j % 64. Packed this way the
-  // winners spread over all lanes, which keeps the lane-maximum bound of the selection
-  // tight (a wave-per-slot layout leaves them on m lanes, and the bound admits nearly all).
-  uint32_t k2[MW];
-  int32_t i2[MW];
-#pragma unroll
-  for (int s = 0; s < MW; ++s) {
-    const int j = s * 64 + lane;
-    k2[s] = j < MW * m ? w_key[j] : 0u;
-    i2[s] = j < MW * m ? w_idx[j] : 0x7fffffff;
-  }
-  wave_threshold(k2, i2, m, s_key[0], s_idx[0], ks, is);
-  // Candidates arrive in ascending block order (key range after key range), each wave keeps
-  // its winners in that order and the waves cover consecutive shares: compacting the
-  // winners in entry order gives ascending blocks.
-  pos = 0;
-#pragma unroll
-  for (int s = 0; s < MW; ++s) {
-    const bool pr = taken(k2[s], i2[s], ks, is);
-    const uint64_t mk = ballot(pr);
-    if (pr) out[pos + rank_below(mk)] = i2[s];
-    pos += popc64(mk);
-  }
+  wide_stage2<MW>(m, w_key, w_idx, s_key[0], s_idx[0], [&](int j, int32_t c) { out[j] = c; });
   if (lane == 0) out[m] = local;
 }
 

@@ -180,6 +180,32 @@ int msa_sparse_attn_decode(const msa_shape *shape, const void *q, const void *k_
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * One whole decode step ("MiniMax-M3: MSA 技术报告速读", section 核心机制: the index-branch
+ * score, max-pool and TopK equations with the forced local block, then the main-branch
+ * equation): the same sel as msa_index_topk and the same o and lse, within rounding, as
+ * msa_sparse_attn_decode on that sel, in two launches instead of four. The index kernel
+ * streams k_idx and ranks each key range; one kernel then merges the ranges' winners,
+ * attends the selected blocks and merges the log-sum-exp partials, the last of a (sequence,
+ * group)'s workgroups to finish combining them (the pages' split with a second merge stage,
+ * with a device-scope arrival counter per (sequence, group) that the index kernel of the
+ * same call clears).
+ *   shape   n_q == 1 and q_start == n_k - 1; d_idx, d_h, block_size and top_k as for the
+ *           two calls it replaces (top_k == 1, or more candidate blocks than one merge
+ *           takes, runs those two calls on this workspace instead).
+ *   q, k_cache, v_cache, q_idx, k_idx   as for msa_sparse_attn_decode and msa_index_topk.
+ *   sel     out [batch, h_kv, 1, top_k] int32, as msa_index_topk writes it.
+ *   o, lse  out, as msa_sparse_attn_decode writes them (lse may be NULL).
+ *   workspace  at least msa_decode_step_workspace_size bytes, caller-owned; its first
+ *           bytes hold the counters, which the call clears itself (no zero fill needed).
+ *           Calls that share one workspace must not overlap in time.
+ * Errors: those of msa_index_topk and msa_sparse_attn_decode.
+ */
+int msa_decode_step_workspace_size(const msa_shape *shape, size_t *bytes);
+int msa_decode_step(const msa_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                    const void *q_idx, const void *k_idx, int32_t *sel, void *o, float *lse,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Index-branch alignment loss ("MiniMax-M3: MSA 技术报告速读", section 训练: the equations
  * for P^idx, P^(r) and L_KL), for every (b, group r, row t) over T = the visible tokens of
  * the blocks in sel[b, r, t, :]:
