@@ -121,3 +121,28 @@ def test_decode_step_workload_full_size(name, seqs):
         log(f"  oracle sequence {b} done")
     ref = {k: np.concatenate([o[k] for o in outs], axis=0) for k in ("sel", "o", "lse")}
     compare(w, got, ref, seqs=torch.as_tensor(seqs, device="cuda"), label=f"{name} (decode step)")
+
+
+def test_decode_step_kv_capacity_stride():
+    """Caches allocated longer than the valid length (kv_capacity > n_k), the slack filled
+    with values that would change the result if read."""
+    w = W("step_capacity", batch=2, n_k=9000, top_k=16, needles=3, seed=23)
+    inp = generate(w, device="cuda")
+    cap = w.n_k + 200
+    big = {"q": inp["q"], "q_idx": inp["q_idx"]}
+    for key in ("k", "v"):
+        x = torch.full((w.batch, w.h_kv, cap, w.d_h), 9.0, dtype=inp[key].dtype, device="cuda")
+        x[:, :, : w.n_k] = inp[key]
+        big[key] = x
+    x = torch.full((w.batch, cap, w.d_idx), 4.0, dtype=inp["k_idx"].dtype, device="cuda")
+    x[:, : w.n_k] = inp["k_idx"]
+    big["k_idx"] = x
+    s = msa.shape_of(w, kv_capacity=cap)
+    got = Step(w)
+    got.ws = torch.full((msa.msa_decode_step_workspace_size(s),), 0xff, dtype=torch.uint8,
+                        device="cuda")
+    msa.msa_decode_step(s, big["q"], big["k"], big["v"], big["q_idx"], big["k_idx"], got.sel,
+                        got.o, got.lse, got.ws)
+    torch.cuda.synchronize()
+    ref = oracle_run(w, to_cpu(inp))
+    compare(w, got, ref, label=w.name)
