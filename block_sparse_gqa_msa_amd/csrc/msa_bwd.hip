@@ -10,9 +10,9 @@
 // Organised KV-block-outer over the prefill's per-block row lists (the page's Kernel
 // section gathers the rows that chose a block so a staged block serves all of them):
 //   bwd_rowdot  D per (b, h, t) from o and dout.
-//   kv_bwd      persistent over runs of RUN consecutive chunks. A chunk's block is split
-//               over BS / 16 waves, 16 keys each. Per 32-row-head tile (32 / G rows x the G
-//               heads) every wave computes S = Q K_w^T and dP = dO V_w^T on the matrix cores
+//   kv_bwd      persistent over runs of RUN consecutive chunks, claimed at run time. A
+//               chunk's block is split over BS / 16 waves, 16 keys each. Per 32-row-head
+//               tile (32 / G rows x the G heads) every wave computes S = Q K_w^T and dP = dO V_w^T on the matrix cores
 //               with the row-heads down the accumulator rows; the accumulator layout is then
 //               directly the A operand of dV_w += P^T dO and dK_w += dS^T Q (Q and dO are
 //               staged transposed in LDS for the B operands). dS goes to LDS, and each wave
@@ -228,7 +228,10 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
   const float cs = a.scale_log2, dscale = w.scale;
   constexpr float LOG2E = 1.4426950408889634f;
 
-  for (int run = blockIdx.x; run < n_runs; run += gridDim.x) {  // uniform loop
+  __shared__ int s_next;
+  for (int run = blockIdx.x; run < n_runs; run = s_next) {  // uniform loop
+    __syncthreads();  // every thread has read s_next for this run
+    if (tid == 0) s_next = claim_next(a.claim, n_runs);  // runs are claimed at run time
     const int c0 = run * w.run, c1 = min(c0 + w.run, n_chunks);
     long cur = -1;
     int seg_first = 0, b = 0, r = 0;
@@ -603,9 +606,13 @@ hipError_t run_bwd(const KvArgs &a, const BwdArgs &w, const void *o, int log2g, 
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
-  const unsigned grid = (unsigned)std::max(1L, std::min(max_runs, 2L * per_cu * cus));
-  if (stages & BWD_STAGE_BLOCKS)
-    hipLaunchKernelGGL((kv_bwd<E, DH, BS>), dim3(grid), dim3(BwdLds<E, DH, BS>::NT), 0, s, a, w, log2g);
+  // one round of the workgroups that fit on the device at once; runs are claimed
+  const unsigned grid = (unsigned)std::max(1L, std::min(max_runs, (long)per_cu * cus));
+  if (stages & BWD_STAGE_BLOCKS) {
+    KvArgs b = a;
+    b.claim = a.cnt + 2L * a.n_seg * a.batch * a.h_kv * a.n_blocks;  // zeroed by the plan
+    hipLaunchKernelGGL((kv_bwd<E, DH, BS>), dim3(grid), dim3(BwdLds<E, DH, BS>::NT), 0, s, b, w, log2g);
+  }
   if (!(stages & BWD_STAGE_MERGE)) return hipGetLastError();
   const long threads = (long)a.batch * a.h_kv * a.n_q * ((long)DH << log2g) / 8;
   hipLaunchKernelGGL((dq_merge<E, DH, 8>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, w,

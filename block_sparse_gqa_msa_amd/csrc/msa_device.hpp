@@ -139,4 +139,17 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   return v;
 }
 
+// Dynamic chunk assignment for the persistent KV-outer kernels: the first gridDim.x chunks
+// go by block index, every later one to the workgroup that claims it. A workgroup claims
+// its next chunk when it starts one, so the atomic's round trip overlaps the chunk. Every
+// processed chunk makes exactly one claim, so the claim that returns n_chunks - 1 is the
+// kernel's last: it resets the counter (zeroed by the plan) for the next launch. Static
+// striding left whole rounds of workgroups idle behind the slowest: chunk costs vary with
+// list lengths.
+__device__ __forceinline__ int claim_next(int32_t *claim, int n_chunks) {
+  const int c = atomicAdd(claim, 1);
+  if (c == n_chunks - 1) atomicExch(claim, 0);
+  return c + (int)gridDim.x;
+}
+
 }  // namespace msa

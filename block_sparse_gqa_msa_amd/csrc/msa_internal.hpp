@@ -78,6 +78,8 @@ struct KvArgs {          // KV-outer prefill attention
   int seg_rows;          // lists are keyed (r, row segment, b, block), group-major
   int n_seg;
   float scale_log2;
+  int32_t *claim = nullptr;  // next-chunk counter of the persistent kernels: zeroed by the
+                             // plan (it follows cnt and cursor), reset by the last claim
 };
 
 constexpr int KV_CHUNK = 128;  // list entries per work item of the KV-outer kernels

@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   const float inv_g = 1.f / (float)G;
   const bool writer_g = ((g * 4) & (G - 1)) == 0;  // first lane group of its rows
 
-  for (int chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {  // uniform loop
+  __shared__ int s_next;
+  for (int chunk = blockIdx.x; chunk < n_chunks; chunk = s_next) {  // uniform loop
     const long i = a.cmap[chunk];
     const int c = (int)(i % a.n_blocks);
     const long rsb = i / a.n_blocks;  // (r, seg, b) of the list
@@ -118,7 +119,8 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
     const long kb = (long)c * BS;
     const float *lse_r = k.lse + ((long)b * a.h_q + (long)r * G) * a.n_q;  // head r*G, row 0
 
-    __syncthreads();  // the previous chunk is done with the LDS buffers
+    __syncthreads();  // the previous chunk is done with the LDS buffers and s_next
+    if (tid == 0) s_next = claim_next(a.claim, n_chunks);  // chunks are claimed at run time
     if (tid < n_e) s_list[tid] = a.list[e0 + tid];
     stage_rows<E, DH, BS, KROW>(kp, kb, a.n_k, s_k);
     stage_rows<E, DI, BS, IROW>(kip, kb, a.n_k, s_ki);
@@ -359,8 +361,11 @@ hipError_t run_kl(const KvArgs &a, const KlArgs &k, int log2g, hipStream_t s) {
   const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
   const long entries = (long)a.batch * a.h_kv * a.n_q * a.top_k;
   const long max_chunks = (entries + KV_CHUNK - 1) / KV_CHUNK + NB;
-  const unsigned grid = (unsigned)std::min(max_chunks, 2L * per_cu * cus);
-  hipLaunchKernelGGL((kv_kl<E, DH, DI, BS, LG>), dim3(grid), dim3(256), 0, s, a, k, log2g);
+  // one round of the workgroups that fit on the device at once; chunks are claimed
+  const unsigned grid = (unsigned)std::min(max_chunks, (long)per_cu * cus);
+  KvArgs b = a;
+  b.claim = a.cnt + 2 * NB;  // zeroed by the plan, after cnt and cursor
+  hipLaunchKernelGGL((kv_kl<E, DH, DI, BS, LG>), dim3(grid), dim3(256), 0, s, b, k, log2g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long rows = (long)a.batch * a.h_kv * a.n_q;

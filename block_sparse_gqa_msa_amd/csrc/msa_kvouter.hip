@@ -12,8 +12,9 @@
 //      then a fill. Integer atomics only place entries; their order inside a list does not
 //      change any result. Lists are keyed group-major, then by row segment, so that the
 //      chunks processed at the same time share one group's K/V and a slice of its Q rows.
-//   2. kv_attend (persistent): a workgroup takes chunks of up to CHUNK entries of one list,
-//      stages the block's K (row-major) and V (transposed) in LDS once, and each wave keeps
+//   2. kv_attend (persistent, chunks claimed at run time): a workgroup takes chunks of up
+//      to CHUNK entries of one list, stages the block's K (row-major) and V (transposed) in
+//      LDS once, and each wave keeps
 //      the block's K and V^T fragments in registers while it runs 16-row tiles (16/G rows
 //      x the G heads of the group): S^T = K Q^T, a softmax over the block, O^T = V^T P^T.
 //      It writes, for every (row, slot, head), the block's unnormalised output sum_j p_j v_j
@@ -381,7 +382,8 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
   const E *q = reinterpret_cast<const E *>(a.q);
   const float cs = a.scale_log2;
 
-  for (int chunk = blockIdx.x; chunk < n_chunks; chunk += gridDim.x) {  // uniform loop
+  __shared__ int s_next;
+  for (int chunk = blockIdx.x; chunk < n_chunks; chunk = s_next) {  // uniform loop
     const long i = a.cmap[chunk];
     const int c = (int)(i % a.n_blocks);
     const long rsb = i / a.n_blocks;  // (r, seg, b) of the list
@@ -395,7 +397,8 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
     const long kb = (long)c * BS;
     const int h = r * G + hd;
 
-    __syncthreads();  // the previous chunk is done with the LDS buffers
+    __syncthreads();  // the previous chunk is done with the LDS buffers and s_next
+    if (tid == 0) s_next = claim_next(a.claim, n_chunks);
     if (tid < n_e) s_list[tid] = a.list[e0 + tid];
     stage_block<E, DH, BS>(kp, vp, kb, a.n_k, s_k, s_v);
     __syncthreads();
@@ -638,8 +641,8 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
   const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
   const long entries = (long)a.batch * a.h_kv * a.n_q * a.top_k;
   if (stages & KV_STAGE_PLAN) {
-    hipLaunchKernelGGL(fill_i32, dim3((unsigned)std::min(4096L, (2 * NB + 255) / 256)), dim3(256), 0, s,
-                       a.cnt, 2 * NB, 0);  // cnt and cursor are adjacent
+    hipLaunchKernelGGL(fill_i32, dim3((unsigned)std::min(4096L, (2 * NB + 1 + 255) / 256)), dim3(256), 0, s,
+                       a.cnt, 2 * NB + 1, 0);  // cnt, cursor and the claim counter are adjacent
     if (a.n_blocks <= HIST_MAX_BLOCKS) {
       const long rows_per_wg = std::max(1, HIST_ROWS_ENTRIES / a.top_k);  // divides seg_rows
       const unsigned wgs = (unsigned)((long)a.batch * a.h_kv * ((a.n_q + rows_per_wg - 1) / rows_per_wg));
@@ -656,8 +659,6 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
   }
   if (stages & KV_STAGE_ATTEND) {
     // persistent: a few workgroups per CU loop over the chunks
-    // two rounds of the workgroups that fit on the device at once: each takes every
-    // grid-th chunk, so per-workgroup work evens out over ~max_chunks / grid chunks
     static const int per_cu = [] {
       int n = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kv_attend<E, DH, BS, false>, 256, 0) !=
@@ -669,9 +670,12 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
+    // one round of the workgroups that fit on the device at once; chunks are claimed
     const long max_chunks = (entries + CHUNK - 1) / CHUNK + NB;
-    const unsigned grid = (unsigned)std::min(max_chunks, 2L * per_cu * cus);
-    hipLaunchKernelGGL((kv_attend<E, DH, BS, false>), dim3(grid), dim3(256), 0, s, a, log2g);
+    const unsigned grid = (unsigned)std::min(max_chunks, (long)per_cu * cus);
+    KvArgs b = a;
+    b.claim = a.cnt + 2 * NB;
+    hipLaunchKernelGGL((kv_attend<E, DH, BS, false>), dim3(grid), dim3(256), 0, s, b, log2g);
   }
   if (!(stages & KV_STAGE_MERGE)) return hipGetLastError();
   const long threads = (long)a.batch * a.h_kv * a.n_q * ((long)DH << log2g) / 8;
@@ -704,7 +708,7 @@ size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_bl
   const size_t max_chunks = (slots + CHUNK - 1) / CHUNK + NB;
   KvLayout L;
   size_t o = 0;
-  L.cnt = o;     o += al(2 * NB * 4);  // cnt, then cursor
+  L.cnt = o;     o += al((2 * NB + 1) * 4);  // cnt, then cursor, then the chunk claim counter
   L.boff = o;    o += al((NB + 1) * 4);
   L.coff = o;    o += al((NB + 1) * 4);
   L.cmap = o;    o += al(max_chunks * 4);
