@@ -12,10 +12,11 @@
 //   bwd_rowdot  D per (b, h, t) from o and dout.
 //   kv_bwd      persistent over runs of RUN consecutive chunks, claimed at run time. A
 //               chunk's block is split over BS / 16 waves, 16 keys each. Per 32-row-head
-//               tile (32 / G rows x the G heads) every wave computes S = Q K_w^T and dP = dO V_w^T on the matrix cores
-//               with the row-heads down the accumulator rows; the accumulator layout is then
-//               directly the A operand of dV_w += P^T dO and dK_w += dS^T Q (Q and dO are
-//               staged transposed in LDS for the B operands). dS goes to LDS, and each wave
+//               tile (32 / G rows x the G heads) every wave computes S = Q K_w^T and
+//               dP = dO V_w^T on the matrix cores with the row-heads down the accumulator
+//               rows; the accumulator layout is then directly the A operand of
+//               dV_w += P^T dO and dK_w += dS^T Q (Q and dO are staged transposed in LDS
+//               for the B operands). dS goes to LDS, and each wave
 //               computes dq for its slice of d over the whole block, written as one partial
 //               per (row, slot, head). dK_w and dV_w stay in registers while a run stays on
 //               one list and are written as one fp32 partial per (run, list) segment.
