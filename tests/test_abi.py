@@ -300,3 +300,35 @@ def test_backward_stage_calls_reject(lib):
         assert fn(ctypes.byref(x), *([dummy] * n), dummy, need, None) == msa.MSA_ERR_UNSUPPORTED
         e = good(n_q=0)
         assert fn(ctypes.byref(e), *([None] * n), None, 0, None) == msa.MSA_OK
+
+
+def test_decode_step_rejects(lib):
+    """msa_decode_step: decode shape only, every pointer required (lse optional), workspace
+    sized by msa_decode_step_workspace_size and at least the two calls' workspaces it
+    contains, supported set of both halves checked."""
+    dummy = 1 << 20
+    d = good(batch=2, n_q=1, n_k=5000, q_start=4999, top_k=16)
+    need = msa.msa_decode_step_workspace_size(d)
+    assert need >= msa.msa_index_topk_workspace_size(d) + msa.msa_sparse_attn_workspace_size(d)
+    db = ctypes.byref(d)
+    args = lambda ws_bytes, **none: [db] + [None if k in none else dummy for k in (
+        "q", "k", "v", "q_idx", "k_idx", "sel", "o")] + [None, dummy, ws_bytes, None]
+    assert lib.msa_decode_step(*args(need - 1)) == msa.MSA_ERR_WORKSPACE
+    for name in ("q", "k", "v", "q_idx", "k_idx", "sel", "o"):
+        assert lib.msa_decode_step(*args(need, **{name: True})) == msa.MSA_ERR_INVALID_ARG, name
+    p = good(n_q=64, n_k=5000, q_start=100)  # not a decode shape
+    assert lib.msa_decode_step(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                               None, dummy, need, None) == msa.MSA_ERR_INVALID_ARG
+    for kw in (dict(d_h=96), dict(d_idx=48), dict(block_size=16), dict(top_k=65)):
+        bad = good(batch=2, n_q=1, n_k=5000, q_start=4999, **{"top_k": 16, **kw})
+        assert lib.msa_decode_step(ctypes.byref(bad), dummy, dummy, dummy, dummy, dummy, dummy,
+                                   dummy, None, dummy, need, None) == msa.MSA_ERR_UNSUPPORTED, kw
+        n = ctypes.c_size_t()
+        assert lib.msa_decode_step_workspace_size(ctypes.byref(bad), ctypes.byref(n)) \
+            == msa.MSA_ERR_UNSUPPORTED, kw
+    assert lib.msa_decode_step_workspace_size(db, None) == msa.MSA_ERR_INVALID_ARG
+    # empty calls: size 0, no pointer touched
+    e = good(batch=0, n_q=1, n_k=5000, q_start=4999)
+    assert msa.msa_decode_step_workspace_size(e) == 0
+    assert lib.msa_decode_step(ctypes.byref(e), None, None, None, None, None, None, None, None,
+                               None, 0, None) == msa.MSA_OK
