@@ -442,9 +442,11 @@ __global__ __launch_bounds__(256) void decode_finish(AttnArgs a, FinishArgs f, i
 
   // 4. the last workgroup of the pair to arrive merges the subs' partials. One thread per
   // workgroup fences: a device-scope fence writes back (release) or invalidates (acquire)
-  // the XCD's L2, so one per thread would repeat that 256 times; the barrier before it
-  // makes the other threads' stores part of what it releases, the one after it orders the
-  // other threads' loads after what it acquires.
+  // the XCD's L2, so one per thread would repeat that 256 times. Each wave first waits for
+  // its own partial stores to complete (the workgroup barrier alone does not wait for
+  // global stores), so that they are in L2 when thread 0's release writes it back; the
+  // barrier after the count orders the other threads' loads after what thread 0 acquires.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
     __threadfence();  // the workgroup's partials are visible device-wide before its count
