@@ -291,7 +291,7 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
       const int e0 = a.boff[cur] + (chunk - a.coff[cur]) * CHUNK;
       const int n_e = min(e0 + CHUNK, a.boff[cur + 1]) - e0;
       __syncthreads();  // the previous chunk is done with s_list
-      if (tid < n_e) s_list[tid] = a.list[e0 + tid];
+      for (int e = tid; e < n_e; e += NT) s_list[e] = a.list[e0 + e];  // NT may be < CHUNK
       __syncthreads();
       const int n_tiles = (n_e + RPT - 1) / RPT;
       const long head0 = (long)b * a.h_q + (long)r * G;

@@ -82,7 +82,7 @@ struct KvArgs {          // KV-outer prefill attention
                              // plan (it follows cnt and cursor), reset by the last claim
 };
 
-constexpr int KV_CHUNK = 128;  // list entries per work item of the KV-outer kernels
+constexpr int KV_CHUNK = 256;  // list entries per work item of the KV-outer kernels
 
 // The alignment loss over the KV-outer lists (the KvArgs of the same shape carry q, k, sel,
 // the lists and the sizes).
