@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
 
     __syncthreads();  // the previous chunk is done with the LDS buffers and s_next
     if (tid == 0) s_next = claim_next(a.claim, n_chunks);  // chunks are claimed at run time
-    if (tid < n_e) s_list[tid] = a.list[e0 + tid];
+    for (int e = tid; e < n_e; e += 256) s_list[e] = a.list[e0 + e];  // any KV_CHUNK
     stage_rows<E, DH, BS, KROW>(kp, kb, a.n_k, s_k);
     stage_rows<E, DI, BS, IROW>(kip, kb, a.n_k, s_ki);
     __syncthreads();

@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
 
     __syncthreads();  // the previous chunk is done with the LDS buffers and s_next
     if (tid == 0) s_next = claim_next(a.claim, n_chunks);
-    if (tid < n_e) s_list[tid] = a.list[e0 + tid];
+    for (int e = tid; e < n_e; e += 256) s_list[e] = a.list[e0 + e];  // any CHUNK
     stage_block<E, DH, BS>(kp, vp, kb, a.n_k, s_k, s_v);
     __syncthreads();
 
