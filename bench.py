@@ -10,13 +10,16 @@ oracle timed on a bounded sample on the host cores:
                  msa_decode_step call (decode_step_call);
   index_kl       the index branch's alignment loss on the prefill's selection;
   attn_backward  the main branch's backward (dq, dk, dv) for that selection;
-  index_project  the index branch's two projections from hidden states of width h_q * d_h.
-The last three are timed apart from the step.
+  index_project  the index branch's two projections from hidden states of width h_q * d_h;
+  chunked_prefill  the last 8192 rows of a 1M-token context against all 1M keys (the same
+                 step as the headline; here the index kernel holds 94% of the FLOPs).
+index_kl, attn_backward and index_project are timed apart from the step.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing starts. Kernel
 durations come from HIP events recorded on the stream the library launches on.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps KD] [--no-cpu]
+                    [--sections prefill,chunk,decode]
 """
 from __future__ import annotations
 
@@ -98,7 +101,7 @@ def decode_work(w):
 
 # ------------------------------------------------------------------ GPU timing
 
-def time_step(w, inputs, steps, warmup, decode):
+def time_step(w, inputs, steps, warmup, decode, extras=True):
     import torch
     from block_sparse_gqa_msa_amd import binding as msa
 
@@ -165,7 +168,7 @@ def time_step(w, inputs, steps, warmup, decode):
     torch.cuda.synchronize()
     times = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) * 1e-3
              for i, (name, _) in enumerate(stages)}
-    if not decode:
+    if not decode and extras:
         # the alignment loss of the same step (sel and lse from the last step above)
         kl = torch.empty((w.batch, R, n), dtype=torch.float32, device="cuda")
         kl_call = lambda: msa.msa_index_kl(s, inputs["q"], inputs["k"], inputs["q_idx"],
@@ -423,6 +426,35 @@ def copy_calibration(n_bytes=1 << 30, reps=5):
 
 # ------------------------------------------------------------------ main
 
+def run_chunk(args, wc, time_step, generate, log):
+    """The headline step on a chunked prefill: timing, per-stage times and the index
+    kernel's roofline (its FLOPs dominate there)."""
+    import torch
+    inp = generate(wc, device="cuda")
+    log(f"[bench] chunked prefill {wc.name}: warmup {args.warmup}, steps {args.steps}")
+    cwall, ckt = time_step(wc, inp, args.steps, args.warmup, decode=False, extras=False)
+    c_index, c_main = prefill_work(wc)
+    t_ci = ckt["index_scores"]
+    chunk = dict(
+        workload=wc.name, value=wc.batch * wc.n_q / cwall, unit="tok/s",
+        ms_per_step=cwall * 1e3,
+        config={"batch": wc.batch, "rows": wc.n_q, "q_start": wc.q_start, "kv_len": wc.n_k,
+                "top_k": wc.top_k},
+        roofline=dict(kernel="index_pool_prefill", bound="mfma", achieved=c_index / t_ci / 1e12,
+                      peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                      frac=c_index / t_ci / PEAK_BF16_FLOPS,
+                      traffic=measured_traffic("index_pool_prefill", wc.name),
+                      per_launch_flops=c_index, avg_launch_ms=t_ci * 1e3),
+        path_mfma=dict(flops=c_index + c_main, tflops=(c_index + c_main) / cwall / 1e12,
+                       mfma_frac=(c_index + c_main) / cwall / PEAK_BF16_FLOPS),
+        kernel_ms={k: v * 1e3 for k, v in ckt.items()})
+    log(f"[bench] chunked prefill {cwall * 1e3:.2f} ms/step, kernels (ms): "
+        + ", ".join(f"{k} {v * 1e3:.3f}" for k, v in ckt.items()))
+    del inp
+    torch.cuda.empty_cache()
+    return chunk
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -431,6 +463,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--prefill", default="prefill_128k")
+    ap.add_argument("--chunk", default="chunk_1m")
+    ap.add_argument("--sections", default="prefill,chunk,decode",
+                    help="comma-separated subset of prefill, chunk, decode (for profiling runs; "
+                         "the JSON line needs prefill)")
     ap.add_argument("--decode", default="decode_1m_b4")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (to scale the HBM byte counters)")
@@ -450,6 +486,21 @@ def main():
 
     msa.load_library()
     log = lambda m: print(m, file=sys.stderr, flush=True)
+    sections = set(args.sections.split(","))
+    if not sections <= {"prefill", "chunk", "decode"}:
+        ap.error(f"unknown section in --sections {args.sections}")
+    if "prefill" in sections and "decode" not in sections:
+        ap.error("the JSON line carries prefill and decode: --sections needs both or no prefill")
+    if "prefill" not in sections:  # a profiling run: time the other sections, print no line
+        if "chunk" in sections:
+            log(json.dumps(run_chunk(args, WORKLOADS[args.chunk], time_step, generate, log)))
+        if "decode" in sections:
+            wd = WORKLOADS[args.decode]
+            inp = generate(wd, device="cuda")
+            dwall, dkt = time_step(wd, inp, args.decode_steps, args.warmup, decode=True)
+            fused = time_decode_step(wd, inp, args.decode_steps, args.warmup)
+            log(f"[bench] decode {dwall * 1e6:.1f} us/step, one call {fused * 1e6:.1f} us/step")
+        return
 
     # ---- prefill at 128K
     wp = WORKLOADS[args.prefill]
@@ -526,6 +577,11 @@ def main():
     del inp
     torch.cuda.empty_cache()
 
+    # ---- chunked prefill: the last rows of a 1M context (the index kernel dominates)
+    chunk = None
+    if "chunk" in sections:
+        chunk = run_chunk(args, WORKLOADS[args.chunk], time_step, generate, log)
+
     # ---- decode at 1M
     wd = WORKLOADS[args.decode]
     inp = generate(wd, device="cuda")
@@ -570,6 +626,7 @@ def main():
         "index_kl": kl,
         "attn_backward": bwd,
         "index_project": proj,
+        "chunked_prefill": chunk,
         "decode": {
             "workload": wd.name, "value": wd.batch / dwall, "unit": "tok/s",
             "steps": args.decode_steps, "ms_per_step": dwall * 1e3,
