@@ -476,6 +476,12 @@ def main():
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    sections = set(args.sections.split(","))
+    if not sections <= {"prefill", "chunk", "decode"}:
+        ap.error(f"unknown section in --sections {args.sections}")
+    if "prefill" in sections and "decode" not in sections:
+        ap.error("the JSON line carries prefill and decode: --sections needs both or no prefill")
+
     if args.calibrate_copy:
         copy_calibration()
         return
@@ -486,11 +492,6 @@ def main():
 
     msa.load_library()
     log = lambda m: print(m, file=sys.stderr, flush=True)
-    sections = set(args.sections.split(","))
-    if not sections <= {"prefill", "chunk", "decode"}:
-        ap.error(f"unknown section in --sections {args.sections}")
-    if "prefill" in sections and "decode" not in sections:
-        ap.error("the JSON line carries prefill and decode: --sections needs both or no prefill")
     if "prefill" not in sections:  # a profiling run: time the other sections, print no line
         if "chunk" in sections:
             log(json.dumps(run_chunk(args, WORKLOADS[args.chunk], time_step, generate, log)))
