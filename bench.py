@@ -3,29 +3,35 @@
 Headline (``value``): causal prefill tokens/s at N = 131072 (32 query heads / 4 KV
 groups, d_h 128, index d_idx 64, blocks of 64, top_k 32, bf16): one step is the index
 branch (block scores, top-k) plus the sparse prefill attention over all 131072 rows.
-The same line carries, each with the roofline of its dominant kernel and the fp64
-oracle timed on a bounded sample on the host cores:
-  decode         the 1M-token decode (batch 4, one new token each, same heads), as the
-                 two calls msa_index_topk + msa_sparse_attn_decode, and also as one
-                 msa_decode_step call (decode_step_call);
-  index_kl       the index branch's alignment loss on the prefill's selection;
-  attn_backward  the main branch's backward (dq, dk, dv) for that selection;
-  index_project  the index branch's two projections from hidden states of width h_q * d_h;
-  chunked_prefill  the last 8192 rows of a 1M-token context against all 1M keys (the same
-                 step as the headline; here the index kernel holds 94% of the FLOPs).
-index_kl, attn_backward and index_project are timed apart from the step.
+Every workload of the measured set has a leg of its own in the same line, each with its
+throughput, the roofline of its dominant kernel, the fp64 oracle timed on a bounded sample
+on the host cores, and a correctness block comparing the outputs of the timed run with
+the oracle on that sample:
+  prefill_512_f32    the tiny fp32 prefill (parity only: no roofline applies)
+  prefill_8k         causal prefill N = 8192, top_k 16
+  prefill_128k       the headline (top-level keys), plus, on its selection and outputs:
+                     index_kl (alignment loss), attn_backward (dq, dk, dv) and
+                     index_project (the index branch's two projections)
+  prefill_128k_hot   the same step with every row choosing the same blocks (all index
+                     inputs zero: ties everywhere, lowest block index first), the
+                     most skewed block popularity there is
+  chunk_1m           the last 8192 rows of a 1M-token context against all 1M keys
+  decode_256k_b32    decode, 32 sequences of 262144 cached tokens
+  decode_1m_b4       decode, 4 sequences of 1048576 cached tokens (the metric's
+                     "decode tok/s @1M"); also as one msa_decode_step call
+Step times are medians over at least 20 repetitions: prefill steps one by one, decode
+steps in repetitions of 10 (HIP events on the library's stream); the mean over the
+timed region's wall clock is reported beside them.
 
-Inputs are seeded synthetic tensors already resident in HBM when timing starts. Kernel
-durations come from HIP events recorded on the stream the library launches on.
+Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps KD] [--no-cpu]
-                    [--sections prefill,chunk,decode]
+                    [--sections LEG,...] [--no-extras]
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -38,16 +44,33 @@ sys.path.insert(0, ROOT)
 METRIC = "MSA attn: prefill tok/s @128K, decode tok/s @1M; % of MFMA/HBM roofline"
 PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
 PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E
+DECODE_REP = 10            # decode steps per timed repetition
+
+# Legs in the order they run, and the short names --sections also accepts.
+LEGS = ["prefill_128k", "prefill_128k_hot", "chunk_1m", "prefill_8k", "prefill_512_f32",
+        "decode_256k_b32", "decode_1m_b4"]
+ALIASES = {"prefill": "prefill_128k", "hot": "prefill_128k_hot", "chunk": "chunk_1m",
+           "c1": "prefill_512_f32", "c2": "prefill_8k", "c3": "prefill_128k",
+           "c4": "decode_256k_b32", "c5a": "chunk_1m", "c5b": "decode_1m_b4",
+           "decode": "decode_1m_b4"}
+HEADLINE, HEADLINE_DECODE = "prefill_128k", "decode_1m_b4"
+PARITY_ONLY = {"prefill_512_f32"}
+# Output tolerances the correctness blocks are judged against (O max-abs, O mean-abs).
+TOL = {"f32": dict(o_max_abs=1e-5, o_mean_abs=1e-5), "bf16": dict(o_max_abs=2e-2, o_mean_abs=1e-2)}
 
 
 # ------------------------------------------------------------------ algorithmic work
 
+def _visible_tokens(w):
+    p = w.q_start + np.arange(w.n_q, dtype=np.int64)
+    b = p // w.block_size
+    return p, (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
+
+
 def prefill_work(w):
     """Algorithmic FLOPs of one step: index scores R*(p+1)*2*d_idx per row plus main
     branch H_q*T_p*4*d_h, T_p = visible tokens of the selected blocks."""
-    p = w.q_start + np.arange(w.n_q, dtype=np.int64)
-    b = p // w.block_size
-    t_p = (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
+    p, t_p = _visible_tokens(w)
     index = float(w.batch * w.h_kv * np.sum(p + 1) * 2 * w.d_idx)
     main = float(w.batch * w.h_q * np.sum(t_p) * 4 * w.d_h)
     return index, main
@@ -56,9 +79,7 @@ def prefill_work(w):
 def kl_work(w):
     """Algorithmic FLOPs of msa_index_kl: per (row, group) and selected visible token, the
     G heads' q.k (2*d_h each) and the index score q_idx.k_idx (2*d_idx)."""
-    p = w.q_start + np.arange(w.n_q, dtype=np.int64)
-    b = p // w.block_size
-    t_p = (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
+    _, t_p = _visible_tokens(w)
     G = w.h_q // w.h_kv
     return float(w.batch * w.h_kv * np.sum(t_p) * (2 * w.d_h * G + 2 * w.d_idx))
 
@@ -67,9 +88,7 @@ def bwd_work(w):
     """Algorithmic FLOPs of msa_sparse_attn_backward: per (row, head) and selected visible
     token, q.k (recomputed), dout.v, and the three products that give dv, dk and dq
     (2*d_h each)."""
-    p = w.q_start + np.arange(w.n_q, dtype=np.int64)
-    b = p // w.block_size
-    t_p = (np.minimum(w.top_k, b + 1) - 1) * w.block_size + (p - b * w.block_size + 1)
+    _, t_p = _visible_tokens(w)
     return float(w.batch * w.h_q * np.sum(t_p) * 10 * w.d_h)
 
 
@@ -101,189 +120,193 @@ def decode_work(w):
 
 # ------------------------------------------------------------------ GPU timing
 
-def time_step(w, inputs, steps, warmup, decode, extras=True):
+def timed_reps(step, steps, warmup, per=1):
+    """Run `warmup` untimed steps, then exactly `steps` timed ones (synchronised on both
+    sides) with a HIP event on the current stream before every `per` steps. Returns the
+    median seconds per step over the repetitions, the mean from the wall clock, and the
+    number of repetitions."""
     import torch
-    from block_sparse_gqa_msa_amd import binding as msa
-
-    s = msa.shape_of(w)
-    R, n = w.h_kv, w.n_q
-    nb = -(-w.n_k // w.block_size)
-    scores = torch.empty((w.batch, R, n, nb), dtype=torch.float32, device="cuda")
-    sel = torch.empty((w.batch, R, n, w.top_k), dtype=torch.int32, device="cuda")
-    o = torch.empty((w.batch, w.h_q, n, w.d_h), dtype=inputs["q"].dtype, device="cuda")
-    lse = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device="cuda")
-    ws_topk = torch.empty(max(1, msa.msa_topk_workspace_size(s)), dtype=torch.uint8, device="cuda")
-    ws_attn = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(s)), dtype=torch.uint8,
-                          device="cuda")
-    attn = msa.msa_sparse_attn_decode if decode else msa.msa_sparse_attn_prefill
     stream = torch.cuda.current_stream()
-
-    ws_index = torch.empty(max(1, msa.msa_index_topk_workspace_size(s)), dtype=torch.uint8,
-                           device="cuda")
-
-    if decode:
-        # msa_index_topk runs the first selection stage inside the index kernel
-        # (index_select_decode) and merges the per-range winners in topk_pass2
-        stages = [
-            ("index_topk", lambda: msa.msa_index_topk(s, inputs["q_idx"], inputs["k_idx"], sel,
-                                                       None, ws_index)),
-            ("attention", lambda: msa.msa_sparse_attn_decode(s, inputs["q"], inputs["k"],
-                                                             inputs["v"], sel, o, lse, ws_attn)),
-        ]
-    else:
-        # prefill: every stage is its own call so each kernel is timed alone
-        stages = [
-            ("index_scores", lambda: msa.msa_index_block_scores(s, inputs["q_idx"],
-                                                                inputs["k_idx"], scores)),
-            ("topk", lambda: msa.msa_topk_from_block_scores(s, scores, sel, ws_topk)),
-            ("attn_plan", lambda: msa.msa_sparse_attn_prefill_plan(s, sel, ws_attn)),
-            ("attn_partials", lambda: msa.msa_sparse_attn_prefill_partials(
-                s, inputs["q"], inputs["k"], inputs["v"], ws_attn)),
-            ("attn_merge", lambda: msa.msa_sparse_attn_prefill_merge(s, sel, o, lse, ws_attn)),
-        ]
-
-    def step(ev=None):
-        for i, (_, call) in enumerate(stages):
-            if ev:
-                ev[i].record(stream)
-            call()
-        if ev:
-            ev[-1].record(stream)
-
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # The timed region: exactly `steps` steps with nothing else enqueued between them.
+    n_rep = steps // per
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_rep + 1)]
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(n_rep * per):
+        if i % per == 0:
+            ev[i // per].record(stream)
         step()
+    ev[n_rep].record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    # Per-stage times from a second pass with an event before each stage (the events and
-    # their host-side cost stay out of the timed region above).
-    n_ev = len(stages) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
-    for i in range(steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    times = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in events])) * 1e-3
-             for i, (name, _) in enumerate(stages)}
-    if not decode and extras:
-        # the alignment loss of the same step (sel and lse from the last step above)
-        kl = torch.empty((w.batch, R, n), dtype=torch.float32, device="cuda")
-        kl_call = lambda: msa.msa_index_kl(s, inputs["q"], inputs["k"], inputs["q_idx"],
-                                           inputs["k_idx"], sel, lse, kl, None, ws_attn)
-        for _ in range(max(1, warmup)):
-            kl_call()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        for _ in range(steps):
-            kl_call()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        times["index_kl"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
-        del kl
-        # the main branch's backward for the same selection, o and lse
-        from block_sparse_gqa_msa_amd.inputs import generate_dout
-        dout = generate_dout(w, device="cuda")
-        dq = torch.empty_like(inputs["q"])
-        dk = torch.empty_like(inputs["k"])
-        dv = torch.empty_like(inputs["v"])
-        ws_bwd = torch.empty(msa.msa_sparse_attn_backward_workspace_size(s), dtype=torch.uint8,
-                             device="cuda")
-        bwd_call = lambda: msa.msa_sparse_attn_backward(s, inputs["q"], inputs["k"], inputs["v"],
-                                                        sel, o, lse, dout, dq, dk, dv, ws_bwd)
-        for _ in range(max(1, warmup)):
-            bwd_call()
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        for _ in range(steps):
-            bwd_call()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        # the same backward as its three staged calls, with an event around each, so the
-        # per-block gradient kernel is timed alone
-        bst = [("bwd_plan", lambda: msa.msa_sparse_attn_backward_plan(s, sel, o, dout, ws_bwd)),
-               ("bwd_partials", lambda: msa.msa_sparse_attn_backward_partials(
-                   s, inputs["q"], inputs["k"], inputs["v"], lse, dout, ws_bwd)),
-               ("bwd_merge", lambda: msa.msa_sparse_attn_backward_merge(s, sel, dq, dk, dv,
-                                                                        ws_bwd))]
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bst) + 1)]
-               for _ in range(steps)]
-        for i in range(steps):
-            for j, (_, call) in enumerate(bst):
-                sev[i][j].record(stream)
-                call()
-            sev[i][-1].record(stream)
-        torch.cuda.synchronize()
-        for j, (name, _) in enumerate(bst):
-            times[name] = float(np.mean([e[j].elapsed_time(e[j + 1]) for e in sev])) * 1e-3
-        times["attn_backward"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
-        del dout, dq, dk, dv, ws_bwd
-        # the index branch's projections of the step's rows (hidden width h_q * d_h)
-        from block_sparse_gqa_msa_amd.inputs import generate_hidden
-        hid = generate_hidden(w, w.h_q * w.d_h, device="cuda")
-        q_idx_p = torch.empty_like(inputs["q_idx"])
-        k_idx_p = torch.empty_like(inputs["k_idx"])
-        proj_call = lambda: msa.msa_index_project(s, hid["x"], hid["w_q"], hid["w_k"], q_idx_p,
-                                                  k_idx_p)
-        for _ in range(max(1, warmup)):
-            proj_call()
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        for _ in range(steps):
-            proj_call()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        times["index_project"] = ev[0].elapsed_time(ev[1]) * 1e-3 / steps
-        del hid, q_idx_p, k_idx_p
-    return wall, times
+    wall = (time.perf_counter() - t0) / (n_rep * per)
+    reps = [ev[i].elapsed_time(ev[i + 1]) * 1e-3 / per for i in range(n_rep)]
+    return float(np.median(reps)), wall, n_rep
 
 
-def time_decode_step(w, inputs, steps, warmup):
-    """Seconds per decode step made as one msa_decode_step call (index kernel, then one
-    kernel for the final selection, the attention and the merge), same inputs."""
+def stage_medians(stages, steps):
+    """Per-stage medians from a pass of `steps` steps with an event before each stage (kept
+    out of the timed region: recording many events per short step costs host time)."""
     import torch
-    from block_sparse_gqa_msa_amd import binding as msa
-
-    s = msa.shape_of(w)
-    sel = torch.empty((w.batch, w.h_kv, 1, w.top_k), dtype=torch.int32, device="cuda")
-    o = torch.empty((w.batch, w.h_q, 1, w.d_h), dtype=inputs["q"].dtype, device="cuda")
-    lse = torch.empty((w.batch, w.h_q, 1), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, msa.msa_decode_step_workspace_size(s)), dtype=torch.uint8,
-                     device="cuda")
-    call = lambda: msa.msa_decode_step(s, inputs["q"], inputs["k"], inputs["v"],
-                                       inputs["q_idx"], inputs["k_idx"], sel, o, lse, ws)
-    for _ in range(warmup):
-        call()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(steps)]
+    for i in range(steps):
+        for j, (_, call) in enumerate(stages):
+            ev[i][j].record(stream)
+            call()
+        ev[i][-1].record(stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        call()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    return {name: float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e-3
+            for j, (name, _) in enumerate(stages)}
 
 
-# ------------------------------------------------------------------ CPU baseline
+class PrefillRun:
+    """Output buffers and the five staged calls of one prefill step (each stage its own
+    call so that every kernel is timed alone; together they are the whole step)."""
 
-def cpu_baseline_prefill(w, inputs, target_s=12.0, seed=0):
+    def __init__(self, w, inputs):
+        import torch
+        from block_sparse_gqa_msa_amd import binding as msa
+        self.w, self.inputs, s = w, inputs, msa.shape_of(w)
+        self.s = s
+        R, n, nb = w.h_kv, w.n_q, -(-w.n_k // w.block_size)
+        dev = "cuda"
+        self.scores = torch.empty((w.batch, R, n, nb), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((w.batch, R, n, w.top_k), dtype=torch.int32, device=dev)
+        self.o = torch.empty((w.batch, w.h_q, n, w.d_h), dtype=inputs["q"].dtype, device=dev)
+        self.lse = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device=dev)
+        self.ws_topk = torch.empty(max(1, msa.msa_topk_workspace_size(s)), dtype=torch.uint8,
+                                   device=dev)
+        self.ws_attn = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(s)),
+                                   dtype=torch.uint8, device=dev)
+        i = inputs
+        self.stages = [
+            ("index_scores", lambda: msa.msa_index_block_scores(s, i["q_idx"], i["k_idx"],
+                                                                self.scores)),
+            ("topk", lambda: msa.msa_topk_from_block_scores(s, self.scores, self.sel,
+                                                            self.ws_topk)),
+            ("attn_plan", lambda: msa.msa_sparse_attn_prefill_plan(s, self.sel, self.ws_attn)),
+            ("attn_partials", lambda: msa.msa_sparse_attn_prefill_partials(
+                s, i["q"], i["k"], i["v"], self.ws_attn)),
+            ("attn_merge", lambda: msa.msa_sparse_attn_prefill_merge(s, self.sel, self.o,
+                                                                     self.lse, self.ws_attn)),
+        ]
+
+    def step(self):
+        for _, call in self.stages:
+            call()
+
+
+class DecodeRun:
+    """Buffers and calls of one decode step: msa_index_topk + msa_sparse_attn_decode, and
+    the same step as one msa_decode_step call."""
+
+    def __init__(self, w, inputs):
+        import torch
+        from block_sparse_gqa_msa_amd import binding as msa
+        self.w, self.inputs, s = w, inputs, msa.shape_of(w)
+        self.s = s
+        dev = "cuda"
+        self.sel = torch.empty((w.batch, w.h_kv, 1, w.top_k), dtype=torch.int32, device=dev)
+        self.o = torch.empty((w.batch, w.h_q, 1, w.d_h), dtype=inputs["q"].dtype, device=dev)
+        self.lse = torch.empty((w.batch, w.h_q, 1), dtype=torch.float32, device=dev)
+        self.ws_index = torch.empty(max(1, msa.msa_index_topk_workspace_size(s)),
+                                    dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(s)),
+                                   dtype=torch.uint8, device=dev)
+        self.ws_step = torch.empty(max(1, msa.msa_decode_step_workspace_size(s)),
+                                   dtype=torch.uint8, device=dev)
+        i = inputs
+        self.stages = [
+            ("index_topk", lambda: msa.msa_index_topk(s, i["q_idx"], i["k_idx"], self.sel, None,
+                                                      self.ws_index)),
+            ("attention", lambda: msa.msa_sparse_attn_decode(s, i["q"], i["k"], i["v"], self.sel,
+                                                             self.o, self.lse, self.ws_attn)),
+        ]
+        self.one_call = lambda: msa.msa_decode_step(s, i["q"], i["k"], i["v"], i["q_idx"],
+                                                    i["k_idx"], self.sel, self.o, self.lse,
+                                                    self.ws_step)
+
+    def step(self):
+        for _, call in self.stages:
+            call()
+
+
+# ------------------------------------------------------------------ oracle: baseline and parity
+
+def correctness(w, sel, o, lse, rows, ref, seqs=None):
+    """The timed run's outputs against the oracle's at the sampled rows (prefill) or
+    sequences (decode): (row, group) selections that differ, O max / mean abs error,
+    LSE max abs error."""
+    import torch
+    if seqs is not None:
+        idx = torch.as_tensor(seqs, device=sel.device, dtype=torch.long)
+        sel, o, lse = sel[idx], o[idx], lse[idx]
+    if rows is not None:
+        idx = torch.as_tensor(rows, device=sel.device, dtype=torch.long)
+        sel, o, lse = sel[:, :, idx], o[:, :, idx], lse[:, :, idx]
+    g_sel = sel.cpu().numpy()
+    err = np.abs(o.float().cpu().numpy().astype(np.float64) - ref["o"])
+    lerr = np.abs(lse.cpu().numpy().astype(np.float64) - ref["lse"])
+    tol = TOL[w.dtype]
+    out = dict(rows_checked=int(g_sel.shape[0] * g_sel.shape[1] * g_sel.shape[2]),
+               sel_mismatch=int((g_sel != ref["sel"]).any(-1).sum()),
+               o_max_abs=float(err.max()), o_mean_abs=float(err.mean()),
+               lse_max_abs=float(lerr.max()), tol=tol)
+    out["pass"] = bool(out["sel_mismatch"] == 0 and out["o_max_abs"] <= tol["o_max_abs"]
+                       and out["o_mean_abs"] <= tol["o_mean_abs"])
+    return out
+
+
+def oracle_prefill(w, inputs, target_s, seed=0, full=False):
+    """The oracle on uniformly drawn rows of the prefill (all rows when `full`), sized for
+    about `target_s` seconds from a 16-row probe. Returns the baseline record, the rows
+    and the oracle's outputs for them."""
     import oracle
     orc = oracle.get()
     cpu = {k: inputs[k].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
     rng = np.random.default_rng(seed)
-    probe = np.sort(rng.choice(w.n_q, size=16, replace=False))
+    if full:
+        rows = np.arange(w.n_q)
+    else:
+        probe = np.sort(rng.choice(w.n_q, size=min(16, w.n_q), replace=False))
+        t0 = time.perf_counter()
+        orc.run(w, cpu, rows=probe)
+        dt = time.perf_counter() - t0
+        n = int(min(w.n_q, max(16, 16 * target_s / max(dt, 1e-3))))
+        rows = np.sort(rng.choice(w.n_q, size=n, replace=False))
     t0 = time.perf_counter()
-    orc.run(w, cpu, rows=probe)
+    ref = orc.run(w, cpu, rows=rows)
     dt = time.perf_counter() - t0
-    n = int(min(w.n_q, max(16, 16 * target_s / max(dt, 1e-3))))
-    rows = np.sort(rng.choice(w.n_q, size=n, replace=False))
-    t0 = time.perf_counter()
-    orc.run(w, cpu, rows=rows)
-    dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
-                sample=f"{n} query rows drawn uniformly (seed {seed}) from the {w.n_q}-row "
-                       f"prefill, all {w.h_kv} groups and {w.h_q} heads; {dt:.1f} s")
+    what = (f"all {w.n_q} rows" if len(rows) == w.n_q else
+            f"{len(rows)} query rows drawn uniformly (seed {seed}) from the {w.n_q}-row prefill")
+    base = dict(value=w.batch * len(rows) / dt, unit="tok/s", cores=orc.max_threads(),
+                kind="oracle", sample=f"{what}, all {w.h_kv} groups and {w.h_q} heads; {dt:.1f} s")
+    return base, rows, ref
+
+
+def oracle_decode(w, inputs, target_s, seqs):
+    """Baseline: the oracle's step of sequence 0 repeated for about `target_s` seconds.
+    Parity: the oracle once on the sequences `seqs`."""
+    import oracle
+    orc = oracle.get()
+    idx = list(seqs)
+    cpu = {k: inputs[k][idx].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
+    ref = orc.run(w.replace(batch=len(idx)), cpu)
+    one = {k: v[0:1] for k, v in cpu.items()}
+    wb = w.replace(batch=1)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        orc.run(wb, one)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= target_s:
+            break
+    base = dict(value=n / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+                sample=f"sequence 0 of {w.batch} (one decode token over {w.n_k} cached tokens), "
+                       f"{n} repetitions in {dt:.1f} s")
+    return base, ref
 
 
 def cpu_baseline_kl(w, inputs, target_s=6.0, seed=1):
@@ -308,7 +331,7 @@ def cpu_baseline_kl(w, inputs, target_s=6.0, seed=1):
                        f"computed first and not timed); {dt:.1f} s")
 
 
-def cpu_baseline_bwd(w, inputs, target_s=12.0):
+def cpu_baseline_bwd(w, inputs, target_s=10.0):
     """The oracle's backward on the last m rows of the prefill (their selections computed
     first, untimed), m sized for about target_s seconds."""
     import oracle
@@ -339,7 +362,7 @@ def cpu_baseline_bwd(w, inputs, target_s=12.0):
                        f"selections computed first and not timed); {dt:.1f} s")
 
 
-def cpu_baseline_project(w, d_model, target_s=6.0, seed=4):
+def cpu_baseline_project(w, d_model, target_s=5.0, seed=4):
     """The oracle's projections of uniformly drawn rows of the step's hidden states."""
     import oracle
     import torch
@@ -365,23 +388,6 @@ def cpu_baseline_project(w, d_model, target_s=6.0, seed=4):
     return dict(value=w.batch * m / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
                 sample=f"{m} rows drawn uniformly (seed {seed}) from the {w.n_q}-row prefill's "
                        f"hidden states (d_model {d_model}); {dt:.1f} s")
-
-
-def cpu_baseline_decode(w, inputs, target_s=6.0):
-    import oracle
-    orc = oracle.get()
-    wb = w.replace(batch=1)
-    cpu = {k: inputs[k][0:1].cpu() for k in ("q", "k", "v", "q_idx", "k_idx")}
-    n, t0 = 0, time.perf_counter()
-    while True:  # the step of one sequence, repeated for a few seconds
-        orc.run(wb, cpu)
-        n += 1
-        dt = time.perf_counter() - t0
-        if dt >= target_s:
-            break
-    return dict(value=n / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
-                sample=f"sequence 0 of {w.batch} (one decode token over {w.n_k} cached tokens), "
-                       f"{n} repetitions in {dt:.1f} s")
 
 
 # ------------------------------------------------------------------ counters
@@ -424,50 +430,214 @@ def copy_calibration(n_bytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes_read": n_bytes, "copy_bytes_written": n_bytes, "reps": reps}))
 
 
+def mfma_roofline(kernel, flops, seconds, workload):
+    return dict(kernel=kernel, bound="mfma", achieved=flops / seconds / 1e12,
+                peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s", frac=flops / seconds / PEAK_BF16_FLOPS,
+                traffic=measured_traffic(kernel, workload), per_launch_flops=flops,
+                avg_launch_ms=seconds * 1e3)
+
+
+# ------------------------------------------------------------------ legs
+
+def prefill_leg(w, args, log, cpu_s=8.0, extras=False):
+    """One prefill workload: median step time, per-stage medians, the dominant kernel's
+    roofline, the whole step's MFMA fraction, the oracle baseline and parity."""
+    import torch
+    from block_sparse_gqa_msa_amd.inputs import generate
+    inp = generate(w, device="cuda")
+    run = PrefillRun(w, inp)
+    log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
+    med, wall, reps = timed_reps(run.step, args.steps, args.warmup)
+    kt = stage_medians(run.stages, args.steps)
+    f_index, f_main = prefill_work(w)
+    leg = dict(workload=w.name, value=w.batch * w.n_q / med, unit="tok/s",
+               ms_per_step=med * 1e3, ms_per_step_mean=wall * 1e3, reps=reps,
+               config={"batch": w.batch, "rows": w.n_q, "q_start": w.q_start, "kv_len": w.n_k,
+                       "h_q": w.h_q, "h_kv": w.h_kv, "d_h": w.d_h, "d_idx": w.d_idx,
+                       "block_size": w.block_size, "top_k": w.top_k, "dtype": w.dtype},
+               kernel_ms={k: v * 1e3 for k, v in kt.items()})
+    if w.name in PARITY_ONLY:
+        leg["roofline"] = None
+        leg["parity_only"] = True
+    else:
+        # dominant kernel by time: the index kernel (index FLOPs) or kv_attend (main FLOPs)
+        cand = [("index_pool_prefill", "index_scores", f_index), ("kv_attend", "attn_partials", f_main)]
+        kern, stage, flops = max(cand, key=lambda c: kt[c[1]])
+        leg["roofline"] = mfma_roofline(kern, flops, kt[stage], w.name)
+        leg["path_mfma"] = dict(flops=f_index + f_main, tflops=(f_index + f_main) / med / 1e12,
+                                mfma_frac=(f_index + f_main) / med / PEAK_BF16_FLOPS)
+    log(f"[bench] {w.name} {med * 1e3:.3f} ms/step (mean {wall * 1e3:.3f}), kernels (ms): "
+        + ", ".join(f"{k} {v * 1e3:.3f}" for k, v in kt.items()))
+    if extras:
+        leg.update(prefill_extras(w, inp, run, args, log))
+    if not args.no_cpu:
+        log(f"[bench] oracle on {w.name}")
+        base, rows, ref = oracle_prefill(w, inp, cpu_s, full=w.name in PARITY_ONLY)
+        leg["cpu_baseline"] = base
+        leg["correctness"] = correctness(w, run.sel, run.o, run.lse, rows, ref)
+        log(f"[bench] {w.name} parity: {json.dumps(leg['correctness'])}")
+    del run, inp
+    torch.cuda.empty_cache()
+    return leg
+
+
+def prefill_extras(w, inp, run, args, log):
+    """The alignment loss, the backward and the index projections on the prefill's last
+    step (its selection, o and lse)."""
+    import torch
+    from block_sparse_gqa_msa_amd import binding as msa
+    from block_sparse_gqa_msa_amd.inputs import generate_dout, generate_hidden
+    s, R, n = run.s, w.h_kv, w.n_q
+    out = {}
+    # the alignment loss of the same step
+    kl = torch.empty((w.batch, R, n), dtype=torch.float32, device="cuda")
+    kl_call = lambda: msa.msa_index_kl(s, inp["q"], inp["k"], inp["q_idx"], inp["k_idx"], run.sel,
+                                       run.lse, kl, None, run.ws_attn)
+    t_kl, _, reps = timed_reps(kl_call, args.steps, max(1, args.warmup))
+    del kl
+    f_kl = kl_work(w)
+    out["index_kl"] = dict(workload=w.name, value=w.batch * n / t_kl, unit="tok/s",
+                           ms_per_call=t_kl * 1e3, reps=reps,
+                           roofline=mfma_roofline("kv_kl", f_kl, t_kl, w.name))
+    log(f"[bench] alignment loss {t_kl * 1e3:.2f} ms/call")
+    # the main branch's backward for the same selection, o and lse
+    dout = generate_dout(w, device="cuda")
+    dq, dk, dv = (torch.empty_like(inp[x]) for x in ("q", "k", "v"))
+    ws_bwd = torch.empty(msa.msa_sparse_attn_backward_workspace_size(s), dtype=torch.uint8,
+                         device="cuda")
+    bwd_call = lambda: msa.msa_sparse_attn_backward(s, inp["q"], inp["k"], inp["v"], run.sel,
+                                                    run.o, run.lse, dout, dq, dk, dv, ws_bwd)
+    t_bwd, _, reps = timed_reps(bwd_call, args.steps, max(1, args.warmup))
+    # the same backward as its three staged calls, so the per-block kernel is timed alone
+    bst = [("bwd_plan", lambda: msa.msa_sparse_attn_backward_plan(s, run.sel, run.o, dout, ws_bwd)),
+           ("bwd_partials", lambda: msa.msa_sparse_attn_backward_partials(
+               s, inp["q"], inp["k"], inp["v"], run.lse, dout, ws_bwd)),
+           ("bwd_merge", lambda: msa.msa_sparse_attn_backward_merge(s, run.sel, dq, dk, dv, ws_bwd))]
+    t_bst = stage_medians(bst, args.steps)
+    del dout, dq, dk, dv, ws_bwd
+    f_bwd = bwd_work(w)
+    out["attn_backward"] = dict(
+        workload=w.name, value=w.batch * n / t_bwd, unit="tok/s", ms_per_call=t_bwd * 1e3,
+        reps=reps, roofline=mfma_roofline("kv_bwd", f_bwd, t_bst["bwd_partials"], w.name),
+        call_mfma=dict(tflops=f_bwd / t_bwd / 1e12, mfma_frac=f_bwd / t_bwd / PEAK_BF16_FLOPS),
+        stage_ms={k: v * 1e3 for k, v in t_bst.items()})
+    log(f"[bench] attention backward {t_bwd * 1e3:.2f} ms/call")
+    # the index branch's projections of the step's rows (hidden width h_q * d_h)
+    d_model = w.h_q * w.d_h
+    hid = generate_hidden(w, d_model, device="cuda")
+    q_idx_p, k_idx_p = torch.empty_like(inp["q_idx"]), torch.empty_like(inp["k_idx"])
+    proj_call = lambda: msa.msa_index_project(s, hid["x"], hid["w_q"], hid["w_k"], q_idx_p, k_idx_p)
+    t_pj, _, reps = timed_reps(proj_call, args.steps, max(1, args.warmup))
+    del hid, q_idx_p, k_idx_p
+    f_pj, b_pj = project_work(w, d_model)
+    # the bound is the larger of the two ideal times (bytes at the HBM peak, FLOPs at MFMA's)
+    if b_pj / PEAK_HBM_BYTES >= f_pj / PEAK_BF16_FLOPS:
+        roof = dict(kernel="index_project", bound="hbm", achieved=b_pj / t_pj / 1e9,
+                    peak=PEAK_HBM_BYTES / 1e9, unit="GB/s", frac=b_pj / t_pj / PEAK_HBM_BYTES,
+                    per_launch_bytes=b_pj)
+    else:
+        roof = dict(kernel="index_project", bound="mfma", achieved=f_pj / t_pj / 1e12,
+                    peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                    frac=f_pj / t_pj / PEAK_BF16_FLOPS, per_launch_flops=f_pj)
+    roof.update(traffic=measured_traffic("index_project", w.name), avg_launch_ms=t_pj * 1e3,
+                tflops=f_pj / t_pj / 1e12, mfma_frac=f_pj / t_pj / PEAK_BF16_FLOPS)
+    out["index_project"] = dict(workload=w.name, d_model=d_model, value=w.batch * n / t_pj,
+                                unit="tok/s", ms_per_call=t_pj * 1e3, reps=reps, roofline=roof)
+    log(f"[bench] index projections {t_pj * 1e3:.3f} ms/call")
+    if not args.no_cpu:
+        log("[bench] oracle baselines of the alignment loss, the backward, the projections")
+        out["index_kl"]["cpu_baseline"] = cpu_baseline_kl(w, inp)
+        out["attn_backward"]["cpu_baseline"] = cpu_baseline_bwd(w, inp)
+        out["index_project"]["cpu_baseline"] = cpu_baseline_project(w, d_model)
+    torch.cuda.empty_cache()
+    return out
+
+
+def decode_leg(w, args, log, parity_seqs, cpu_s=5.0):
+    """One decode workload: median step time (repetitions of DECODE_REP steps), the index
+    kernel's HBM roofline, the whole step's HBM fraction, the step as one call, the oracle
+    baseline and parity on `parity_seqs`."""
+    import torch
+    from block_sparse_gqa_msa_amd.inputs import generate
+    inp = generate(w, device="cuda")
+    run = DecodeRun(w, inp)
+    steps = max(DECODE_REP, args.decode_steps // DECODE_REP * DECODE_REP)
+    log(f"[bench] {w.name}: warmup {args.warmup}, steps {steps}")
+    med, wall, reps = timed_reps(run.step, steps, args.warmup, per=DECODE_REP)
+    kt = stage_medians(run.stages, steps)
+    one, one_wall, _ = timed_reps(run.one_call, steps, args.warmup, per=DECODE_REP)
+    d_bytes, d_index_bytes, _ = decode_work(w)
+    t_idx = kt["index_topk"]
+    leg = dict(
+        workload=w.name, value=w.batch / med, unit="tok/s", steps=steps, reps=reps,
+        ms_per_step=med * 1e3, ms_per_step_mean=wall * 1e3,
+        config={"batch": w.batch, "kv_len": w.n_k, "h_q": w.h_q, "h_kv": w.h_kv, "d_h": w.d_h,
+                "d_idx": w.d_idx, "block_size": w.block_size, "top_k": w.top_k},
+        roofline=dict(kernel="index_select_decode+topk_merge_wide", bound="hbm",
+                      achieved=d_index_bytes / t_idx / 1e9, peak=PEAK_HBM_BYTES / 1e9,
+                      unit="GB/s", frac=d_index_bytes / t_idx / PEAK_HBM_BYTES,
+                      traffic=measured_traffic("index_select_decode", w.name),
+                      per_launch_bytes=d_index_bytes, avg_launch_ms=t_idx * 1e3),
+        path_hbm=dict(bytes=d_bytes, gbs=d_bytes / med / 1e9, hbm_frac=d_bytes / med / PEAK_HBM_BYTES),
+        kernel_ms={k: v * 1e3 for k, v in kt.items()},
+        decode_step_call={"ms_per_step": one * 1e3, "ms_per_step_mean": one_wall * 1e3,
+                          "value": w.batch / one, "hbm_frac": d_bytes / one / PEAK_HBM_BYTES})
+    log(f"[bench] {w.name} {med * 1e6:.1f} us/step (mean {wall * 1e6:.1f}), one call "
+        f"{one * 1e6:.1f} us/step, kernels (us): "
+        + ", ".join(f"{k} {v * 1e6:.1f}" for k, v in kt.items()))
+    if not args.no_cpu:
+        log(f"[bench] oracle on {w.name}")
+        run.step()  # the two-call step's outputs (the one-call loop ran last)
+        torch.cuda.synchronize()
+        base, ref = oracle_decode(w, inp, cpu_s, parity_seqs)
+        leg["cpu_baseline"] = base
+        leg["correctness"] = correctness(w, run.sel, run.o, run.lse, None, ref, seqs=parity_seqs)
+        leg["correctness"]["sequences"] = list(parity_seqs)
+        log(f"[bench] {w.name} parity: {json.dumps(leg['correctness'])}")
+    del run, inp
+    torch.cuda.empty_cache()
+    return leg
+
+
+def run_leg(name, args, log):
+    from block_sparse_gqa_msa_amd.inputs import WORKLOADS
+    w = WORKLOADS[name]
+    if w.decode:
+        seqs = list(range(w.batch)) if w.batch <= 4 else list(range(0, w.batch, w.batch // 8))
+        return decode_leg(w, args, log, seqs)
+    cpu_s = {"prefill_128k": 8.0, "prefill_128k_hot": 3.0, "chunk_1m": 6.0, "prefill_8k": 6.0}.get(name, 2.0)
+    return prefill_leg(w, args, log, cpu_s=cpu_s,
+                       extras=(name == HEADLINE and not args.no_extras))
+
+
 # ------------------------------------------------------------------ main
 
-def run_chunk(args, wc, time_step, generate, log):
-    """The headline step on a chunked prefill: timing, per-stage times and the index
-    kernel's roofline (its FLOPs dominate there)."""
-    import torch
-    inp = generate(wc, device="cuda")
-    log(f"[bench] chunked prefill {wc.name}: warmup {args.warmup}, steps {args.steps}")
-    cwall, ckt = time_step(wc, inp, args.steps, args.warmup, decode=False, extras=False)
-    c_index, c_main = prefill_work(wc)
-    t_ci = ckt["index_scores"]
-    chunk = dict(
-        workload=wc.name, value=wc.batch * wc.n_q / cwall, unit="tok/s",
-        ms_per_step=cwall * 1e3,
-        config={"batch": wc.batch, "rows": wc.n_q, "q_start": wc.q_start, "kv_len": wc.n_k,
-                "top_k": wc.top_k},
-        roofline=dict(kernel="index_pool_prefill", bound="mfma", achieved=c_index / t_ci / 1e12,
-                      peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                      frac=c_index / t_ci / PEAK_BF16_FLOPS,
-                      traffic=measured_traffic("index_pool_prefill", wc.name),
-                      per_launch_flops=c_index, avg_launch_ms=t_ci * 1e3),
-        path_mfma=dict(flops=c_index + c_main, tflops=(c_index + c_main) / cwall / 1e12,
-                       mfma_frac=(c_index + c_main) / cwall / PEAK_BF16_FLOPS),
-        kernel_ms={k: v * 1e3 for k, v in ckt.items()})
-    log(f"[bench] chunked prefill {cwall * 1e3:.2f} ms/step, kernels (ms): "
-        + ", ".join(f"{k} {v * 1e3:.3f}" for k, v in ckt.items()))
-    del inp
-    torch.cuda.empty_cache()
-    return chunk
+def parse_sections(text, ap):
+    if text == "all":
+        return list(LEGS)
+    want = []
+    for part in text.split(","):
+        name = ALIASES.get(part, part)
+        if name not in LEGS:
+            ap.error(f"unknown leg {part!r} in --sections (legs: {', '.join(LEGS)}, "
+                     f"or {', '.join(ALIASES)})")
+        want.append(name)
+    return [n for n in LEGS if n in want]
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--prefill", default="prefill_128k")
-    ap.add_argument("--chunk", default="chunk_1m")
-    ap.add_argument("--sections", default="prefill,chunk,decode",
-                    help="comma-separated subset of prefill, chunk, decode (for profiling runs; "
-                         "the JSON line needs prefill)")
-    ap.add_argument("--decode", default="decode_1m_b4")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the oracle (CPU baselines and correctness blocks)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the alignment loss, backward and projections of the 128K prefill")
+    ap.add_argument("--sections", default="all",
+                    help="comma-separated legs to run (for profiling runs; the JSON line needs "
+                         f"{HEADLINE} and {HEADLINE_DECODE}, otherwise each leg is logged)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (to scale the HBM byte counters)")
     args = ap.parse_args()
@@ -475,174 +645,57 @@ def main():
         print("bench.py measures one GPU: the MSA library has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
-
-    sections = set(args.sections.split(","))
-    if not sections <= {"prefill", "chunk", "decode"}:
-        ap.error(f"unknown section in --sections {args.sections}")
-    if "prefill" in sections and "decode" not in sections:
-        ap.error("the JSON line carries prefill and decode: --sections needs both or no prefill")
+    legs = parse_sections(args.sections, ap)
+    if args.steps < 1 or args.decode_steps < 1:
+        ap.error("--steps and --decode-steps must be positive")
 
     if args.calibrate_copy:
         copy_calibration()
         return
 
-    import torch
     from block_sparse_gqa_msa_amd import binding as msa
-    from block_sparse_gqa_msa_amd.inputs import WORKLOADS, generate
-
     msa.load_library()
     log = lambda m: print(m, file=sys.stderr, flush=True)
-    if "prefill" not in sections:  # a profiling run: time the other sections, print no line
-        if "chunk" in sections:
-            log(json.dumps(run_chunk(args, WORKLOADS[args.chunk], time_step, generate, log)))
-        if "decode" in sections:
-            wd = WORKLOADS[args.decode]
-            inp = generate(wd, device="cuda")
-            dwall, dkt = time_step(wd, inp, args.decode_steps, args.warmup, decode=True)
-            fused = time_decode_step(wd, inp, args.decode_steps, args.warmup)
-            log(f"[bench] decode {dwall * 1e6:.1f} us/step, one call {fused * 1e6:.1f} us/step")
-        return
+    out = {}
+    for name in legs:
+        out[name] = run_leg(name, args, log)
+        if HEADLINE not in legs or HEADLINE_DECODE not in legs:
+            log(json.dumps({name: out[name]}))
+    if HEADLINE not in legs or HEADLINE_DECODE not in legs:
+        return  # a profiling run: no headline line
 
-    # ---- prefill at 128K
-    wp = WORKLOADS[args.prefill]
-    inp = generate(wp, device="cuda")
-    log(f"[bench] prefill {wp.name}: warmup {args.warmup}, steps {args.steps}")
-    wall, kt = time_step(wp, inp, args.steps, args.warmup, decode=False)
-    f_index, f_main = prefill_work(wp)
-    tok_s = wp.batch * wp.n_q / wall
-    # dominant kernel by time: the index kernel (index FLOPs) or kv_attend (main-branch FLOPs)
-    cand = [dict(kernel="index_pool_prefill", stage="index_scores", flops=f_index),
-            dict(kernel="kv_attend", stage="attn_partials", flops=f_main)]
-    dom = max(cand, key=lambda c: kt[c["stage"]])
-    t_dom = kt[dom["stage"]]
-    roof = dict(kernel=dom["kernel"], bound="mfma", achieved=dom["flops"] / t_dom / 1e12,
-                peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                frac=dom["flops"] / t_dom / PEAK_BF16_FLOPS,
-                traffic=measured_traffic(dom["kernel"], wp.name),
-                per_launch_flops=dom["flops"], avg_launch_ms=t_dom * 1e3)
-    path = dict(flops=f_index + f_main, tflops=(f_index + f_main) / wall / 1e12,
-                mfma_frac=(f_index + f_main) / wall / PEAK_BF16_FLOPS)
-    t_kl = kt.pop("index_kl")
-    log(f"[bench] prefill {wall * 1e3:.2f} ms/step, kernels (ms): "
-        + ", ".join(f"{k} {v * 1e3:.3f}" for k, v in kt.items()))
-    f_kl = kl_work(wp)
-    kl = dict(workload=wp.name, value=wp.batch * wp.n_q / t_kl, unit="tok/s",
-              ms_per_call=t_kl * 1e3,
-              roofline=dict(kernel="kv_kl", bound="mfma", achieved=f_kl / t_kl / 1e12,
-                            peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                            frac=f_kl / t_kl / PEAK_BF16_FLOPS,
-                            traffic=measured_traffic("kv_kl", wp.name),
-                            per_launch_flops=f_kl, avg_launch_ms=t_kl * 1e3))
-    log(f"[bench] alignment loss {t_kl * 1e3:.2f} ms/call")
-    t_bwd = kt.pop("attn_backward")
-    t_bst = {k: kt.pop(k) for k in ("bwd_plan", "bwd_partials", "bwd_merge")}
-    t_kvb = t_bst["bwd_partials"]  # the kv_bwd kernel alone
-    f_bwd = bwd_work(wp)
-    bwd = dict(workload=wp.name, value=wp.batch * wp.n_q / t_bwd, unit="tok/s",
-               ms_per_call=t_bwd * 1e3,
-               roofline=dict(kernel="kv_bwd", bound="mfma", achieved=f_bwd / t_kvb / 1e12,
-                             peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                             frac=f_bwd / t_kvb / PEAK_BF16_FLOPS,
-                             traffic=measured_traffic("kv_bwd", wp.name),
-                             per_launch_flops=f_bwd, avg_launch_ms=t_kvb * 1e3),
-               call_mfma=dict(tflops=f_bwd / t_bwd / 1e12, mfma_frac=f_bwd / t_bwd / PEAK_BF16_FLOPS),
-               stage_ms={k: v * 1e3 for k, v in t_bst.items()})
-    log(f"[bench] attention backward {t_bwd * 1e3:.2f} ms/call")
-    t_pj = kt.pop("index_project")
-    d_model = wp.h_q * wp.d_h
-    f_pj, b_pj = project_work(wp, d_model)
-    # the bound is the larger of the two ideal times (bytes at the HBM peak, FLOPs at MFMA's)
-    if b_pj / PEAK_HBM_BYTES >= f_pj / PEAK_BF16_FLOPS:
-        pj_roof = dict(kernel="index_project", bound="hbm", achieved=b_pj / t_pj / 1e9,
-                       peak=PEAK_HBM_BYTES / 1e9, unit="GB/s", frac=b_pj / t_pj / PEAK_HBM_BYTES,
-                       per_launch_bytes=b_pj)
-    else:
-        pj_roof = dict(kernel="index_project", bound="mfma", achieved=f_pj / t_pj / 1e12,
-                       peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                       frac=f_pj / t_pj / PEAK_BF16_FLOPS, per_launch_flops=f_pj)
-    pj_roof.update(traffic=measured_traffic("index_project", wp.name), avg_launch_ms=t_pj * 1e3,
-                   tflops=f_pj / t_pj / 1e12, mfma_frac=f_pj / t_pj / PEAK_BF16_FLOPS)
-    proj = dict(workload=wp.name, d_model=d_model, value=wp.batch * wp.n_q / t_pj, unit="tok/s",
-                ms_per_call=t_pj * 1e3, roofline=pj_roof)
-    log(f"[bench] index projections {t_pj * 1e3:.3f} ms/call")
-    cpu_p = None
-    if not args.no_cpu:
-        log("[bench] oracle CPU baseline (prefill sample)")
-        cpu_p = cpu_baseline_prefill(wp, inp)
-        log("[bench] oracle CPU baseline (alignment loss sample)")
-        kl["cpu_baseline"] = cpu_baseline_kl(wp, inp)
-        log("[bench] oracle CPU baseline (backward sample)")
-        bwd["cpu_baseline"] = cpu_baseline_bwd(wp, inp)
-        log("[bench] oracle CPU baseline (projection sample)")
-        proj["cpu_baseline"] = cpu_baseline_project(wp, d_model)
-    del inp
-    torch.cuda.empty_cache()
-
-    # ---- chunked prefill: the last rows of a 1M context (the index kernel dominates)
-    chunk = None
-    if "chunk" in sections:
-        chunk = run_chunk(args, WORKLOADS[args.chunk], time_step, generate, log)
-
-    # ---- decode at 1M
-    wd = WORKLOADS[args.decode]
-    inp = generate(wd, device="cuda")
-    log(f"[bench] decode {wd.name}: warmup {args.warmup}, steps {args.decode_steps}")
-    dwall, dkt = time_step(wd, inp, args.decode_steps, args.warmup, decode=True)
-    fused_ms = time_decode_step(wd, inp, args.decode_steps, args.warmup) * 1e3
-    log(f"[bench] decode as one msa_decode_step call: {fused_ms * 1e3:.1f} us/step")
-    d_bytes, d_index_bytes, _ = decode_work(wd)
-    t_idx = dkt["index_topk"]
-    droof = dict(kernel="index_select_decode+topk_merge_wide", bound="hbm",
-                 achieved=d_index_bytes / t_idx / 1e9, peak=PEAK_HBM_BYTES / 1e9,
-                 unit="GB/s", frac=d_index_bytes / t_idx / PEAK_HBM_BYTES,
-                 traffic=measured_traffic("index_select_decode", wd.name),
-                 per_launch_bytes=d_index_bytes, avg_launch_ms=t_idx * 1e3)
-    log(f"[bench] decode {dwall * 1e6:.1f} us/step, kernels (us): "
-        + ", ".join(f"{k} {v * 1e6:.1f}" for k, v in dkt.items()))
-    cpu_d = None
-    if not args.no_cpu:
-        log("[bench] oracle CPU baseline (decode sample)")
-        cpu_d = cpu_baseline_decode(wd, inp)
-
+    head = out.pop(HEADLINE)
+    w = head
     line = {
         "metric": METRIC,
-        "value": tok_s,
+        "value": head["value"],
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall * 1e3,
+        "ms_per_step": head["ms_per_step"],
+        "ms_per_step_mean": head["ms_per_step_mean"],
+        "statistic": f"median over {head['reps']} timed steps",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wp.name, "batch": wp.batch, "seq_len": wp.n_q, "h_q": wp.h_q,
-                   "h_kv": wp.h_kv, "d_h": wp.d_h, "d_idx": wp.d_idx,
-                   "block_size": wp.block_size, "top_k": wp.top_k, "parallelism": "none"},
-        "roofline": roof,
-        "path_mfma": path,
-        "kernel_ms": {k: v * 1e3 for k, v in kt.items()},
-        "cpu_baseline": cpu_p,
-        "index_kl": kl,
-        "attn_backward": bwd,
-        "index_project": proj,
-        "chunked_prefill": chunk,
-        "decode": {
-            "workload": wd.name, "value": wd.batch / dwall, "unit": "tok/s",
-            "steps": args.decode_steps, "ms_per_step": dwall * 1e3,
-            "config": {"batch": wd.batch, "kv_len": wd.n_k, "h_q": wd.h_q, "h_kv": wd.h_kv,
-                       "d_h": wd.d_h, "d_idx": wd.d_idx, "block_size": wd.block_size,
-                       "top_k": wd.top_k},
-            "roofline": droof,
-            "path_hbm": dict(bytes=d_bytes, gbs=d_bytes / dwall / 1e9,
-                             hbm_frac=d_bytes / dwall / PEAK_HBM_BYTES),
-            "kernel_ms": {k: v * 1e3 for k, v in dkt.items()},
-            "decode_step_call": {"ms_per_step": fused_ms, "value": wd.batch / (fused_ms * 1e-3),
-                                 "hbm_frac": d_bytes / (fused_ms * 1e-3) / PEAK_HBM_BYTES},
-            "cpu_baseline": cpu_d,
-        },
+        "config": dict(workload=w["workload"], seq_len=w["config"]["rows"],
+                       parallelism="none", **{k: v for k, v in w["config"].items()
+                                              if k not in ("rows", "dtype")}),
+        "roofline": head["roofline"],
+        "path_mfma": head["path_mfma"],
+        "kernel_ms": head["kernel_ms"],
+        "cpu_baseline": head.get("cpu_baseline"),
+        "correctness": head.get("correctness"),
+        "index_kl": head.get("index_kl"),
+        "attn_backward": head.get("attn_backward"),
+        "index_project": head.get("index_project"),
+        "decode": out.pop(HEADLINE_DECODE),
+        "chunked_prefill": out.pop("chunk_1m", None),
     }
+    line.update(out)  # the remaining legs under their workload names
     print(json.dumps(line), flush=True)
 
 

@@ -62,6 +62,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise MsaLibraryMissing(
             f"{path} is missing: build it with `python -m block_sparse_gqa_msa_amd.build`")
+    # torch's HIP runtime first: the library's libamdhip64 dependency then binds to the
+    # same runtime instance that owns the tensors and streams it is handed (a second
+    # runtime loaded beside it sees no device).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, S, I = ctypes.c_void_p, ctypes.POINTER(MsaShape), ctypes.c_int
     sz = ctypes.POINTER(ctypes.c_size_t)

@@ -69,6 +69,11 @@ WORKLOADS: Dict[str, Workload] = {
     # long causal prefill N=131072, 2048 blocks, k=32, 64 needle blocks
     "prefill_128k": Workload("prefill_128k", batch=1, n_q=131072, n_k=131072, q_start=0,
                              top_k=32, needles=64, seed=3, **_COMMON),
+    # the same prefill with every index input zero: all block scores tie, so every row
+    # takes blocks 0..k-2 plus its local block (the most skewed block popularity)
+    "prefill_128k_hot": Workload("prefill_128k_hot", batch=1, n_q=131072, n_k=131072, q_start=0,
+                                 top_k=32, needles=0, seed=3,
+                                 **dict(_COMMON, idx_range=0)),
     # decode: 32 sequences with 262144 cached tokens each, k=32
     "decode_256k_b32": Workload("decode_256k_b32", batch=32, n_q=1, n_k=262144,
                                 q_start=262143, top_k=32, needles=8, seed=4, **_COMMON),

@@ -71,7 +71,41 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
-@pytest.mark.parametrize("sections", ["prefill", "prefill,chunk", "decode,bogus"])
-def test_bench_rejects_section_sets(sections):
+@pytest.mark.parametrize("sections", ["decode,bogus", "prefill_2k", ""])
+def test_bench_rejects_unknown_legs(sections):
     r = _bench("--sections", sections)
     assert r.returncode == 2 and "--sections" in r.stderr
+
+
+def test_bench_sections_run_in_leg_order():
+    import argparse
+    ap = argparse.ArgumentParser()
+    assert bench.parse_sections("c5b,c1,prefill", ap) == ["prefill_128k", "prefill_512_f32",
+                                                          "decode_1m_b4"]
+    assert bench.parse_sections("all", ap) == bench.LEGS
+    from block_sparse_gqa_msa_amd.inputs import WORKLOADS
+    assert all(name in WORKLOADS for name in bench.LEGS)
+
+
+def test_correctness_block_counts_what_differs():
+    """The bench's parity block: a planted selection difference and output error are
+    reported as such, on sampled rows."""
+    import torch
+    w = W(8, 8, 2)
+    B, H, R, n, k, d = w.batch, w.h_q, w.h_kv, w.n_q, w.top_k, w.d_h
+    rng = np.random.default_rng(0)
+    ref = dict(sel=rng.integers(0, 4, (B, R, n, k)).astype(np.int32),
+               o=rng.standard_normal((B, H, n, d)), lse=rng.standard_normal((B, H, n)))
+    sel = torch.as_tensor(ref["sel"]).clone()
+    o = torch.as_tensor(ref["o"], dtype=torch.float32).clone()
+    lse = torch.as_tensor(ref["lse"], dtype=torch.float32).clone()
+    rows = [1, 3, 6]
+    sub = dict(sel=ref["sel"][:, :, rows], o=ref["o"][:, :, rows], lse=ref["lse"][:, :, rows])
+    c = bench.correctness(w, sel, o, lse, rows, sub)
+    assert c["sel_mismatch"] == 0 and c["o_max_abs"] < 1e-6 and c["pass"]
+    sel[0, 1, 3, 0] += 1         # a checked row
+    sel[0, 0, 2, 0] += 1         # a row outside the sample
+    o[0, 2, 6, 5] += 0.5
+    c = bench.correctness(w, sel, o, lse, rows, sub)
+    assert c["rows_checked"] == B * R * len(rows)
+    assert c["sel_mismatch"] == 1 and abs(c["o_max_abs"] - 0.5) < 1e-6 and not c["pass"]
