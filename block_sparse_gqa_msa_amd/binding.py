@@ -27,8 +27,9 @@ EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_s
            "msa_sparse_attn_backward_workspace_size", "msa_sparse_attn_backward",
            "msa_sparse_attn_backward_plan", "msa_sparse_attn_backward_partials",
            "msa_sparse_attn_backward_merge", "msa_index_project",
-           "msa_decode_step_workspace_size", "msa_decode_step",
+           "msa_decode_step_workspace_size", "msa_decode_step", "msa_decode_step_noalloc",
            "msa_last_error", "msa_abi_version")
+DECODE_STEP_SCRATCH_BYTES = 32 << 20  # MSA_DECODE_STEP_SCRATCH_BYTES
 
 
 class MsaShape(ctypes.Structure):
@@ -89,6 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_sparse_attn_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_decode_step_workspace_size.argtypes = [S, sz]
     lib.msa_decode_step.argtypes = [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_decode_step_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P]
     for f in EXPORTS:
         if f == "msa_last_error":
             continue
@@ -277,6 +279,18 @@ def msa_decode_step(shape: MsaShape, q, k_cache, v_cache, q_idx, k_idx, sel, o, 
         ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k_cache, et, "k_cache"),
         _ptr(v_cache, et, "v_cache"), _ptr(q_idx, et, "q_idx"), _ptr(k_idx, et, "k_idx"),
         _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"), _ptr(lse, torch.float32, "lse"), wp, wn,
+        _stream(stream, o)))
+
+
+def msa_decode_step_noalloc(shape: MsaShape, q, k_cache, v_cache, q_idx, k_idx, sel, o, lse=None,
+                            stream=None) -> None:
+    """msa_decode_step on the library's own per-GPU scratch array (no workspace argument)."""
+    import torch
+    et = _elem_dtype(shape)
+    _check(load_library().msa_decode_step_noalloc(
+        ctypes.byref(shape), _ptr(q, et, "q"), _ptr(k_cache, et, "k_cache"),
+        _ptr(v_cache, et, "v_cache"), _ptr(q_idx, et, "q_idx"), _ptr(k_idx, et, "k_idx"),
+        _ptr(sel, torch.int32, "sel"), _ptr(o, et, "o"), _ptr(lse, torch.float32, "lse"),
         _stream(stream, o)))
 
 

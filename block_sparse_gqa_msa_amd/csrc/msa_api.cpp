@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "msa.h"
@@ -196,6 +197,32 @@ int key_chunk_decode(const msa_shape &s) {
   int kc = 4096;
   while (kc > 256 && s.batch * ((keys + kc - 1) / kc) < 2048) kc /= 2;
   return kc;
+}
+
+// The allocation-free decode step's workspace: one array per GPU, held until the process
+// ends. Host code never uses this name as an address (on the host it is only a stand-in);
+// device_scratch() takes each GPU's address once, with that GPU current.
+static __device__ __align__(256) unsigned char scratch[MSA_DECODE_STEP_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int device_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "address of the decode-step scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
 }
 
 }  // namespace
@@ -647,9 +674,10 @@ int msa_decode_step_workspace_size(const msa_shape *shape, size_t *bytes) {
   return ok();
 }
 
-int msa_decode_step(const msa_shape *shape, const void *q, const void *k_cache, const void *v_cache,
-                    const void *q_idx, const void *k_idx, int32_t *sel, void *o, float *lse,
-                    void *workspace, size_t workspace_bytes, void *stream) {
+// Validation shared by the decode-step entry points (nothing is enqueued on failure).
+static int check_decode_step(const msa_shape *shape, const void *q, const void *k_cache,
+                             const void *v_cache, const void *q_idx, const void *k_idx,
+                             const int32_t *sel, const void *o) {
   int rc = check_shape(shape);
   if (rc) return rc;
   const msa_shape &s = *shape;
@@ -657,9 +685,19 @@ int msa_decode_step(const msa_shape *shape, const void *q, const void *k_cache, 
   if (s.n_q != 1 || s.q_start != s.n_k - 1)
     return fail(MSA_ERR_INVALID_ARG, "decode needs n_q == 1 and q_start == n_k - 1 (got %d, %d, n_k %d)",
                 s.n_q, s.q_start, s.n_k);
-  if (empty(s)) return ok();
+  if (empty(s)) return MSA_OK;
   if (!q || !k_cache || !v_cache || !q_idx || !k_idx || !sel || !o)
     return fail(MSA_ERR_INVALID_ARG, "q, k_cache, v_cache, q_idx, k_idx, sel and o must be non-NULL");
+  return MSA_OK;
+}
+
+int msa_decode_step(const msa_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                    const void *q_idx, const void *k_idx, int32_t *sel, void *o, float *lse,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_decode_step(shape, q, k_cache, v_cache, q_idx, k_idx, sel, o);
+  if (rc) return rc;
+  const msa_shape &s = *shape;
+  if (empty(s)) return ok();
   StepWs w;
   if ((rc = step_ws(s, &w))) return rc;
   if (!workspace || workspace_bytes < w.total)
@@ -696,6 +734,24 @@ int msa_decode_step(const msa_shape *shape, const void *q, const void *k_cache, 
   e = msa::launch_decode_finish(a, f, s.dtype, s.d_h, st);
   if (e != hipSuccess) return hip_fail(e, "decode finish launch");
   return ok();
+}
+
+int msa_decode_step_noalloc(const msa_shape *shape, const void *q, const void *k_cache,
+                            const void *v_cache, const void *q_idx, const void *k_idx, int32_t *sel,
+                            void *o, float *lse, void *stream) {
+  int rc = check_decode_step(shape, q, k_cache, v_cache, q_idx, k_idx, sel, o);
+  if (rc) return rc;
+  if (empty(*shape)) return ok();
+  StepWs w;
+  if ((rc = step_ws(*shape, &w))) return rc;
+  if (w.total > MSA_DECODE_STEP_SCRATCH_BYTES)
+    return fail(MSA_ERR_WORKSPACE, "this decode step needs %zu bytes of workspace, more than the "
+                "%zu-byte scratch array of msa_decode_step_noalloc; use msa_decode_step",
+                w.total, (size_t)MSA_DECODE_STEP_SCRATCH_BYTES);
+  void *scratch_ptr = nullptr;
+  if ((rc = device_scratch(&scratch_ptr))) return rc;
+  return msa_decode_step(shape, q, k_cache, v_cache, q_idx, k_idx, sel, o, lse, scratch_ptr,
+                         MSA_DECODE_STEP_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -206,6 +206,27 @@ int msa_decode_step(const msa_shape *shape, const void *q, const void *k_cache, 
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * msa_decode_step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels, the
+ * same results bit for bit, with the workspace taken from a scratch array of
+ * MSA_DECODE_STEP_SCRATCH_BYTES that the library holds in device memory, one per GPU, for
+ * the life of the process. The call allocates and frees nothing.
+ *   Arguments as for msa_decode_step, without the workspace.
+ *   Shapes whose msa_decode_step_workspace_size exceeds MSA_DECODE_STEP_SCRATCH_BYTES are
+ *   rejected with MSA_ERR_WORKSPACE before anything is enqueued (32 MiB covers, e.g.,
+ *   32 sequences of 262144 tokens or 4 of 1048576 at 32 heads, 4 groups, d_h 128, top_k 32).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap in time on the same
+ *   GPU (two streams, two threads) race and give wrong results; the caller serialises
+ *   them. The array keeps the last call's contents; what must start at zero (the arrival
+ *   counters) is cleared by each call's own first kernel.
+ * Errors: those of msa_decode_step; MSA_ERR_HIP when the array's address cannot be taken.
+ */
+#define MSA_DECODE_STEP_SCRATCH_BYTES ((size_t)32 << 20)
+int msa_decode_step_noalloc(const msa_shape *shape, const void *q, const void *k_cache,
+                            const void *v_cache, const void *q_idx, const void *k_idx, int32_t *sel,
+                            void *o, float *lse, void *stream);
+
+/*
  * Index-branch alignment loss ("MiniMax-M3: MSA 技术报告速读", section 训练: the equations
  * for P^idx, P^(r) and L_KL), for every (b, group r, row t) over T = the visible tokens of
  * the blocks in sel[b, r, t, :]:

@@ -332,3 +332,29 @@ def test_decode_step_rejects(lib):
     assert msa.msa_decode_step_workspace_size(e) == 0
     assert lib.msa_decode_step(ctypes.byref(e), None, None, None, None, None, None, None, None,
                                None, 0, None) == msa.MSA_OK
+
+
+def test_decode_step_noalloc_rejects(lib):
+    """msa_decode_step_noalloc: the same validation as msa_decode_step, and shapes whose
+    workspace exceeds its scratch array are refused before anything is enqueued."""
+    dummy = 1 << 20
+    d = good(batch=2, n_q=1, n_k=5000, q_start=4999, top_k=16)
+    db = ctypes.byref(d)
+    args = lambda **none: [db] + [None if k in none else dummy for k in (
+        "q", "k", "v", "q_idx", "k_idx", "sel", "o")] + [None, None]
+    for name in ("q", "k", "v", "q_idx", "k_idx", "sel", "o"):
+        assert lib.msa_decode_step_noalloc(*args(**{name: True})) == msa.MSA_ERR_INVALID_ARG, name
+    p = good(n_q=64, n_k=5000, q_start=100)  # not a decode shape
+    assert lib.msa_decode_step_noalloc(ctypes.byref(p), *([dummy] * 7), None, None) \
+        == msa.MSA_ERR_INVALID_ARG
+    big = good(batch=64, n_q=1, n_k=1 << 20, q_start=(1 << 20) - 1, top_k=32)
+    assert msa.msa_decode_step_workspace_size(big) > msa.DECODE_STEP_SCRATCH_BYTES
+    assert lib.msa_decode_step_noalloc(ctypes.byref(big), *([dummy] * 7), None, None) \
+        == msa.MSA_ERR_WORKSPACE
+    assert b"scratch" in lib.msa_last_error()
+    from block_sparse_gqa_msa_amd.inputs import WORKLOADS
+    for name in ("decode_256k_b32", "decode_1m_b4"):
+        assert msa.msa_decode_step_workspace_size(msa.shape_of(WORKLOADS[name])) \
+            <= msa.DECODE_STEP_SCRATCH_BYTES, name
+    e = good(batch=0, n_q=1, n_k=5000, q_start=4999)
+    assert lib.msa_decode_step_noalloc(ctypes.byref(e), *([None] * 9)) == msa.MSA_OK
