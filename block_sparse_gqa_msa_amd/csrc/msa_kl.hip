@@ -89,6 +89,9 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   __shared__ __attribute__((aligned(16))) unsigned char s_k[BS * KROW];
   __shared__ __attribute__((aligned(16))) unsigned char s_ki[BS * IROW];
   __shared__ int32_t s_list[KV_CHUNK];
+  // The list load below loops over a chunk's entries (any KV_CHUNK), but the tiles assume
+  // the 256-thread workgroup that every KV_CHUNK up to 256 has been tested with.
+  static_assert(KV_CHUNK <= 256, "kv_kl: chunks longer than the workgroup are untested");
   __shared__ float4 s_part[KV_CHUNK];  // the chunk's results, stored once per chunk: a store
   __shared__ float2 s_ml[KV_CHUNK];    // per tile would be waited for with the next loads
   __shared__ float s_sx[4][16][BS + 1];  // per wave: index scores of 16 entry rows x BS keys

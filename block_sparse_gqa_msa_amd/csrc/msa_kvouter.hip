@@ -361,9 +361,9 @@ __device__ __forceinline__ void store4(bf16_t *dst, f32x4 v) {
 }
 __device__ __forceinline__ void store4(float *dst, f32x4 v) { *reinterpret_cast<f32x4 *>(dst) = v; }
 
-// REG_KV: keep the block's K and V^T fragments in registers across tiles (fewer LDS reads,
-// fewer resident waves) instead of re-reading them from LDS per tile.
-template <typename E, int DH, int BS, bool REG_KV>
+// Each wave reads the block's K and V^T fragments from LDS per tile (keeping them in
+// registers across tiles cost resident waves and was not kept).
+template <typename E, int DH, int BS>
 __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
   using F = typename Frag<E>::type;
   using L = KvLds<E, DH, BS>;
@@ -373,6 +373,9 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
   __shared__ __attribute__((aligned(16))) unsigned char s_v[L::V_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char s_o[4][16 * OROW];  // per wave
   __shared__ int32_t s_list[CHUNK];
+  // A chunk's list is loaded by a loop over its entries (any CHUNK), but the tiles below
+  // assume the 256-thread workgroup that every CHUNK up to 256 has been tested with.
+  static_assert(CHUNK <= 256, "kv_attend: chunks longer than the workgroup are untested");
 
   const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
   const int n_chunks = a.coff[NB];
@@ -403,20 +406,6 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
     stage_block<E, DH, BS>(kp, vp, kb, a.n_k, s_k, s_v);
     __syncthreads();
 
-    F kf[REG_KV ? KTN : 1][REG_KV ? DC : 1];
-    F vf[REG_KV ? DT : 1][REG_KV ? KS : 1];
-    if constexpr (REG_KV) {
-#pragma unroll
-      for (int kt = 0; kt < KTN; ++kt)
-#pragma unroll
-        for (int dc = 0; dc < DC; ++dc)
-          kf[kt][dc] = load_frag(reinterpret_cast<const E *>(s_k + (kt * 16 + c16) * L::KROW +
-                                                            (dc * 32 + g * 8) * L::ES));
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) vf[dt][ks] = vt_frag(s_v + (dt * 16 + c16) * L::VROW, ks, g, kp);
-    }
 
     const int n_tiles = (n_e + QPT - 1) / QPT;
     // Q rows of tile tt. The loads are unconditional (lanes past the chunk's entries read
@@ -446,12 +435,8 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          F af;
-          if constexpr (REG_KV)
-            af = kf[kt][dc];
-          else
-            af = load_frag(reinterpret_cast<const E *>(s_k + (kt * 16 + c16) * L::KROW +
-                                                      (dc * 32 + g * 8) * L::ES));
+          const F af = load_frag(reinterpret_cast<const E *>(s_k + (kt * 16 + c16) * L::KROW +
+                                                              (dc * 32 + g * 8) * L::ES));
           acc = mfma_chunk(af, bq[dc], acc);
         }
         s[kt] = acc;
@@ -489,11 +474,7 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
         const F bp = pt_frag(s[2 * ks], s[2 * ks + 1], kp);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          F av;
-          if constexpr (REG_KV)
-            av = vf[dt][ks];
-          else
-            av = vt_frag(s_v + (dt * 16 + c16) * L::VROW, ks, g, kp);
+          const F av = vt_frag(s_v + (dt * 16 + c16) * L::VROW, ks, g, kp);
           o[dt] = mfma_chunk(av, bp, o[dt]);
         }
       }
@@ -661,7 +642,7 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
     // persistent: a few workgroups per CU loop over the chunks
     static const int per_cu = [] {
       int n = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kv_attend<E, DH, BS, false>, 256, 0) !=
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kv_attend<E, DH, BS>, 256, 0) !=
               hipSuccess || n < 1)
         n = 1;
       return n;
@@ -675,7 +656,7 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
     const unsigned grid = (unsigned)std::min(max_chunks, (long)per_cu * cus);
     KvArgs b = a;
     b.claim = a.cnt + 2 * NB;
-    hipLaunchKernelGGL((kv_attend<E, DH, BS, false>), dim3(grid), dim3(256), 0, s, b, log2g);
+    hipLaunchKernelGGL((kv_attend<E, DH, BS>), dim3(grid), dim3(256), 0, s, b, log2g);
   }
   if (!(stages & KV_STAGE_MERGE)) return hipGetLastError();
   const long threads = (long)a.batch * a.h_kv * a.n_q * ((long)DH << log2g) / 8;
