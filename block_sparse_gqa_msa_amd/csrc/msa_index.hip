@@ -256,16 +256,35 @@ __global__ __launch_bounds__(256) void index_pool_decode(IndexArgs a) {
 // z = sequence; SEL_WAVES waves. Each wave pools its share of the blocks for all groups
 // into LDS; then one wave per group ranks the range's blocks before the local block and
 // writes its best top_k - 1 (key, block) pairs; a final merge pass picks the overall best.
+//
+// The k_idx stream is read once, so its loads are non-temporal; that only pays when every
+// load instruction covers whole cache lines (a 512 MiB stream in this launch shape: 6.8 TB/s
+// against 5.9 TB/s with ordinary loads, while non-temporal loads of the matrix-core
+// fragment pattern, 64 bytes of each of 16 rows per instruction, made the kernel slower).
+// So each 64-key tile is read as contiguous 1 KiB pieces, one 16-byte piece per lane, into
+// registers a tile ahead, written to a wave-private LDS tile and read back as fragments.
+template <typename E, int DI>
+struct SelStage {
+  static constexpr int RB = DI * (int)sizeof(E);  // bytes of one key row
+  static constexpr int PPK = RB / 16;             // 16-byte pieces per key
+  static constexpr int PPL = KT * PPK / 64;       // pieces per lane and tile
+  static constexpr int ROW = RB + 16;             // padded LDS row: fragment reads conflict-free
+  static constexpr int WAVE_BYTES = KT * ROW;
+};
+
 template <typename E, int DI, int BS>
 __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs a) {
   using F = typename Frag<E>::type;
+  using ST = SelStage<E, DI>;
   constexpr int DC = DI / 32;
   constexpr int BPT = KT / BS;
   constexpr int MPB = BS / 16;
   constexpr int NBW = SEL_NBLK / SEL_WAVES;  // blocks per wave
+  constexpr int SEL_BYTES = SEL_WAVES * SELECT_LDS * 8;
+  constexpr int RAW = SEL_WAVES * ST::WAVE_BYTES > SEL_BYTES ? SEL_WAVES * ST::WAVE_BYTES : SEL_BYTES;
   __shared__ float s_m[16][SEL_NBLK];
-  __shared__ uint32_t s_key[SEL_WAVES][SELECT_LDS];
-  __shared__ int32_t s_idx[SEL_WAVES][SELECT_LDS];
+  // the stream's staging tiles, then (after the barrier) the ranking's scratch
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[RAW];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const int R = a.h_kv, b = blockIdx.z, wg = blockIdx.x;
   const long p = a.q_start;
@@ -287,19 +306,35 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
                        : zero_frag(qi);
   const long kw0 = (long)(c0 + w * NBW) * BS;  // this wave's first key
   constexpr int NT = NBW * BS / KT;            // key tiles per wave
+  unsigned char *stg = s_raw + w * ST::WAVE_BYTES;
   // Keys past p read key p instead (pool masks them): unconditional loads keep the next
   // tile's loads in flight, where a load under a branch would make the MFMAs wait for all.
-  auto fetch = [&](int tile, F (&dst)[4][DC]) {
+  auto fetch = [&](int tile, u32x4 (&dst)[ST::PPL]) {
     const long k0 = kw0 + (long)tile * KT;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const long j = min(k0 + mt * 16 + c16, p);
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) dst[mt][dc] = load_frag(ki + j * DI + dc * 32 + g * 8);
+    for (int i = 0; i < ST::PPL; ++i) {
+      const int pc = i * 64 + lane;
+      const long j = min(k0 + pc / ST::PPK, p);
+      dst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+          reinterpret_cast<const unsigned char *>(ki + j * DI) + (pc % ST::PPK) * 16));
     }
   };
-  auto pool = [&](int tile, const F (&cur)[4][DC]) {
+  auto pool = [&](int tile, const u32x4 (&src)[ST::PPL]) {
     const long k0 = kw0 + (long)tile * KT;
+    asm volatile("" ::: "memory");  // the previous tile's fragment reads come first
+#pragma unroll
+    for (int i = 0; i < ST::PPL; ++i) {
+      const int pc = i * 64 + lane;
+      *reinterpret_cast<u32x4 *>(stg + (pc / ST::PPK) * ST::ROW + (pc % ST::PPK) * 16) = src[i];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // wave-private tile: in-order LDS
+    F cur[4][DC];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc)
+        cur[mt][dc] = load_frag(reinterpret_cast<const E *>(stg + (mt * 16 + c16) * ST::ROW) +
+                                dc * 32 + g * 8);
     const bool need_mask = k0 + KT - 1 > p;
 #pragma unroll
     for (int blk = 0; blk < BPT; ++blk) {
@@ -318,11 +353,11 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
       if (g == 0 && c16 < R) s_m[c16][w * NBW + tile * BPT + blk] = mx;
     }
   };
-  // double-buffered key tiles: the next tile's fragments load while this one computes
+  // double-buffered key tiles: the next tile's pieces load while this one computes
   const int nt = (int)min((long)NT, (p - kw0) / KT + 1);  // tiles with a visible key
   // The prefetches are unconditional too: past the last tile they re-read the last tile
-  // (a cache hit) rather than branch around the load.
-  F fa[4][DC], fb[4][DC];
+  // rather than branch around the load.
+  u32x4 fa[ST::PPL], fb[ST::PPL];
   if (nt > 0) fetch(0, fa);
   for (int tile = 0; tile < nt; tile += 2) {
     fetch(min(tile + 1, nt - 1), fb);
@@ -347,7 +382,8 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
     }
     uint32_t ks = 0;
     int32_t is = 0x7fffffff;
-    if (nv > m) wave_threshold<4>(key, idx, m, s_key[w], s_idx[w], ks, is);
+    uint32_t *lk = reinterpret_cast<uint32_t *>(s_raw) + w * 2 * SELECT_LDS;
+    if (nv > m) wave_threshold<4>(key, idx, m, lk, reinterpret_cast<int32_t *>(lk + SELECT_LDS), ks, is);
     uint32_t *ck = a.cand_key + (((long)b * R + r) * n_wg + wg) * m;
     int32_t *ci = a.cand_idx + (((long)b * R + r) * n_wg + wg) * m;
     int pos = 0;
