@@ -624,7 +624,16 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
   if (stages & KV_STAGE_PLAN) {
     hipLaunchKernelGGL(fill_i32, dim3((unsigned)std::min(4096L, (2 * NB + 1 + 255) / 256)), dim3(256), 0, s,
                        a.cnt, 2 * NB + 1, 0);  // cnt, cursor and the claim counter are adjacent
-    if (a.n_blocks <= HIST_MAX_BLOCKS) {
+    // per-workgroup LDS histograms while the device's LDS per workgroup holds n_blocks
+    // counters; per-entry global counters otherwise
+    static const long lds_max = [] {
+      int dev = 0, v = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        v = 64 << 10;
+      return (long)v;
+    }();
+    if (a.n_blocks <= HIST_MAX_BLOCKS && (long)a.n_blocks * (long)sizeof(int32_t) <= lds_max) {
       const long rows_per_wg = std::max(1, HIST_ROWS_ENTRIES / a.top_k);  // divides seg_rows
       const unsigned wgs = (unsigned)((long)a.batch * a.h_kv * ((a.n_q + rows_per_wg - 1) / rows_per_wg));
       const size_t lds = (size_t)a.n_blocks * sizeof(int32_t);

@@ -55,6 +55,10 @@ SMALL = [
     # per lane, so the exact m-th comes from the second bitwise search, not the ranking
     W("k48_mid_candidates", n_q=64, n_k=16448, q_start=16384, h_q=8, h_kv=2, d_h=64,
       d_idx=32, block_size=64, top_k=48, needles=8),
+    # 18751 key blocks: the list build's LDS histograms take 73 KiB per workgroup (more
+    # than the 64 KiB of the 1M-context workloads)
+    W("prefill_hist_73k_lds", n_q=48, n_k=600032, q_start=599984, h_q=8, h_kv=2, d_h=64,
+      d_idx=32, block_size=32, top_k=12, needles=8),
     # more than 32768 key blocks: the list build falls back to per-entry counters
     W("prefill_many_blocks", n_q=40, n_k=(1 << 20) + 96, q_start=(1 << 20) + 56, h_q=8,
       h_kv=2, d_h=64, d_idx=32, block_size=32, top_k=16, needles=8),
