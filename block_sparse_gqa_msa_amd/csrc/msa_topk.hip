@@ -33,7 +33,7 @@ __device__ __forceinline__ void select_chunk(const TopkArgs &a, long pid, int ch
   int32_t idx[VI];
   float x[VI];
 #pragma unroll
-  for (int s = 0; s < VI; ++s) x[s] = row[min(base + s * 64 + lane, n_c - 1)];
+  for (int s = 0; s < VI; ++s) x[s] = __builtin_nontemporal_load(row + min(base + s * 64 + lane, n_c - 1));
 #pragma unroll
   for (int s = 0; s < VI; ++s) pin(x[s]);
 #pragma unroll
