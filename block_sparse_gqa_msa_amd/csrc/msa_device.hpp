@@ -133,6 +133,12 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m));
+  return v;
+}
+
 __device__ __forceinline__ int wave_min_i32(int v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m));

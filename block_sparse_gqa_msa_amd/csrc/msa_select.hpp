@@ -23,9 +23,51 @@ constexpr int SELECT_LDS = SELECT_CAP + 64;  // entries of a wave's lk / li: CAP
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// The m-th largest of N keys per lane (over the wave), given lo <= it <= hi: the bits
+// above the highest bit where lo and hi differ are fixed, the rest come from a
+// ballot-counted bitwise search (none at all when lo == hi, as under heavy ties).
+template <int N>
+__device__ __forceinline__ uint32_t mth_key(const uint32_t (&k)[N], int m, uint32_t lo, uint32_t hi) {
+  const uint32_t diff = lo ^ hi;
+  if (!diff) return lo;
+  const int top = 31 - __builtin_clz(diff);
+  uint32_t K = top == 31 ? 0u : lo & ~((2u << top) - 1u);
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t c = K | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < N; ++q) cnt += popc64(ballot(k[q] >= c));
+    if (cnt >= m) K = c;
+  }
+  return K;
+}
+
+// The index of the need-th (1-based) item with key K, counting in item order (slot-major,
+// then lane), which is ascending index order: the cut among the items tied at K.
+template <int N>
+__device__ __forceinline__ int32_t tie_cut(const uint32_t (&k)[N], const int32_t (&ix)[N], uint32_t K,
+                                           int need) {
+  int seen = 0;
+  int32_t X = 0x7fffffff;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const bool eq = k[q] == K;
+    const uint64_t mk = ballot(eq);
+    const int c = popc64(mk);
+    if (seen < need && seen + c >= need) {  // wave-uniform: the cut lies in this slot
+      const uint64_t hit = ballot(eq && rank_below(mk) == need - seen - 1);
+      X = __builtin_amdgcn_readlane(ix[q], __builtin_ctzll(hit));
+    }
+    seen += c;
+  }
+  return X;
+}
+
 // Exact m-th item (1 <= m <= 63) of the wave's items under (key desc, idx asc); at least m
-// slots are non-empty and the non-empty items have distinct indices. lk / li: wave-private LDS of SELECT_LDS entries (the last 64 are
-// write-only spares, one per lane). On return, an
+// slots are non-empty, the non-empty items have distinct indices, and item order (slot-major,
+// then lane) is ascending index order among the non-empty items (every caller's items are
+// blocks in ascending order, or winners kept in that order). lk / li: wave-private LDS of
+// SELECT_LDS entries (the last 64 are write-only spares, one per lane). On return, an
 // item is among the best m iff key > kstar || (key == kstar && idx <= istar).
 // Returns C >= m when the items with key >= a lower bound T (C of them, in item order:
 // slot-major, then lane) are left in lk / li, or -1 when heavy ties sent it to the
@@ -96,60 +138,24 @@ __device__ int wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V],
       ck[q] = j < C ? lk[j] : 0u;
       ci[q] = j < C ? li[j] : 0x7fffffff;
     }
-    // The m-th largest candidate key K, by a ballot-counted bitwise search.
-    uint32_t K = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = K | (1u << bit);
-      int cnt = 0;
+    // The m-th largest candidate key K (between T and the largest key), then the index
+    // cut among the candidates tied at K: they sit in item order, so the `need` lowest
+    // indices are the first `need` of them.
+    const uint32_t K = mth_key(ck, m, T, wave_max_u32(lm));
+    int ngt = 0;
 #pragma unroll
-      for (int q = 0; q < Q; ++q) cnt += popc64(ballot(ck[q] >= c));
-      if (cnt >= m) K = c;
-    }
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      ngt += popc64(ballot(ck[q] > K));
-      neq += popc64(ballot(ck[q] == K));
-    }
-    const int need = m - ngt;  // 1 <= need <= neq
-    int32_t X = 0x7fffffff;    // all items with key K are taken ...
-    if (neq > need) {          // ... unless ties at K: then the `need` lowest indices
-      X = 0;
-      for (int bit = 30; bit >= 0; --bit) {
-        const int32_t c = X | (1 << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int q = 0; q < Q; ++q) cnt += popc64(ballot(ck[q] == K && ci[q] < c));
-        if (cnt < need) X = c;
-      }
-    }
+    for (int q = 0; q < Q; ++q) ngt += popc64(ballot(ck[q] > K));
     kstar = K;
-    istar = X;
+    istar = tie_cut(ck, ci, K, m - ngt);  // 1 <= m - ngt <= the number tied at K
     return C;
   }
-  // Heavy ties: exact search over every item.
-  T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = T | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int s = 0; s < V; ++s) cnt += popc64(ballot(key[s] >= c));
-    if (cnt >= m) T = c;
-  }
+  // Heavy ties: the same over every item (T is still a lower bound of the m-th key).
+  const uint32_t K = mth_key(key, m, T, wave_max_u32(lm));
   int ngt = 0;
 #pragma unroll
-  for (int s = 0; s < V; ++s) ngt += popc64(ballot(key[s] > T));
-  const int need = m - ngt;  // >= 1 items with key == T are taken, lowest indices first
-  int32_t X = 0;
-  for (int bit = 30; bit >= 0; --bit) {
-    const int32_t c = X | (1 << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int s = 0; s < V; ++s) cnt += popc64(ballot(key[s] == T && idx[s] < c));
-    if (cnt < need) X = c;
-  }
-  kstar = T;
-  istar = X;
+  for (int s = 0; s < V; ++s) ngt += popc64(ballot(key[s] > K));
+  kstar = K;
+  istar = tie_cut(key, idx, K, m - ngt);
   return -1;
 }
 
