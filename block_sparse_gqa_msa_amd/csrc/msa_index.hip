@@ -86,18 +86,21 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
 
   const unsigned char *kbase =
       reinterpret_cast<const unsigned char *>(a.k_idx) + (long)b * a.cap * DI * (long)sizeof(E);
-  u32x4 pre[L::PER_THREAD];
-  auto fetch = [&](int tile) {
+  // k_idx tiles arrive two tiles ahead: tile j's pieces load into register set j % 2 while
+  // tiles j-2 and j-1 compute, and are stashed into LDS buffer j % 2 after tile j-1.
+  u32x4 pa[L::PER_THREAD], pb[L::PER_THREAD];
+  // Keys past n_k read key n_k - 1 instead: they lie past every column's position, so the
+  // pooling masks them, and an unconditional load keeps the compiler's waits precise.
+  auto fetch = [&](int tile, u32x4 (&pre)[L::PER_THREAD]) {
     const long k0 = k_begin + (long)tile * KT;
 #pragma unroll
     for (int i = 0; i < L::PER_THREAD; ++i) {
       const int pc = tid + i * 256, key = pc / L::PER_ROW, off = pc % L::PER_ROW;
-      const long j = k0 + key;
-      pre[i] = (j < a.n_k) ? *reinterpret_cast<const u32x4 *>(kbase + j * DI * (long)sizeof(E) + off * 16)
-                           : u32x4{0u, 0u, 0u, 0u};
+      const long j = min(k0 + key, (long)a.n_k - 1);
+      pre[i] = *reinterpret_cast<const u32x4 *>(kbase + j * DI * (long)sizeof(E) + off * 16);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, const u32x4 (&pre)[L::PER_THREAD]) {
 #pragma unroll
     for (int i = 0; i < L::PER_THREAD; ++i) {
       const int pc = tid + i * 256, key = pc / L::PER_ROW, off = pc % L::PER_ROW;
@@ -124,13 +127,12 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
   };
 
   const int my_col = w * 64 + g * 16 + c16;  // the column whose pooled value this lane holds
-  fetch(0);
-  stash(0);
-  __syncthreads();
   int run = 0;  // blocks collected in s_out
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  // One key tile: pooled maxima of LDS buffer `buf` into s_out, the next tile's pieces
+  // (register set `nxt`, loaded a tile earlier) into the other buffer, and the flush of a
+  // full run of blocks.
+  auto tile_step = [&](int tile, u32x4 (&nxt)[L::PER_THREAD]) {
     const int buf = tile & 1;
-    if (tile + 1 < n_tiles) fetch(tile + 1);
     const long k0 = k_begin + (long)tile * KT;
     const int krel = tile * KT;  // k0 - k_begin
     const bool need_mask = k0 + KT - 1 > p_first;
@@ -182,14 +184,32 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
     else
       pool(std::false_type{});
     run += BPT;
-    if (tile + 1 < n_tiles) stash(buf ^ 1);
+    if (tile + 1 < n_tiles) stash(buf ^ 1, nxt);
     __syncthreads();
     if (run == OUT_RUN || tile + 1 == n_tiles) {
       const long c0 = c_begin + (long)(tile + 1) * BPT - run;
       flush(c0, run);
       run = 0;
+      // Wait for the maxima stores here, once per run: with stores of unknown completion
+      // in flight the compiler makes every later wait for a k_idx tile a wait for all
+      // memory operations (loads and stores need not complete in order), which would
+      // also wait for the tile loaded a step later and undo the two-tile distance.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
     }
+    // This set is free again: tile + 3 goes into it (two tiles ahead of its stash). Past
+    // the last tile the loads re-read it (cache hits): unconditional loads let the
+    // compiler wait for exactly the set it stashes, not for every load in flight.
+    fetch(min(tile + 3, n_tiles - 1), nxt);
+  };
+  fetch(0, pa);
+  fetch(min(1, n_tiles - 1), pb);
+  stash(0, pa);
+  fetch(min(2, n_tiles - 1), pa);
+  __syncthreads();
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    tile_step(tile, pb);  // stashes tile + 1 from pb, then loads tile + 3 into pb
+    if (tile + 1 < n_tiles) tile_step(tile + 1, pa);  // stashes tile + 2, loads tile + 4
   }
 }
 
