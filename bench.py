@@ -57,6 +57,11 @@ HEADLINE, HEADLINE_DECODE = "prefill_128k", "decode_1m_b4"
 PARITY_ONLY = {"prefill_512_f32"}
 # Output tolerances the correctness blocks are judged against (O max-abs, O mean-abs).
 TOL = {"f32": dict(o_max_abs=1e-5, o_mean_abs=1e-5), "bf16": dict(o_max_abs=2e-2, o_mean_abs=1e-2)}
+# The loss: |kl - ref| <= atol + rtol |ref|. dq: |dq - ref| <= atol max|ref| + rtol |ref| and
+# mean error <= mean * mean|ref|. Projections: |x - ref| <= rtol |ref| + atol max|ref|.
+KL_TOL = {"f32": dict(atol=2e-5, rtol=2e-5), "bf16": dict(atol=2e-4, rtol=2e-5)}
+BWD_TOL = {"f32": dict(atol=2e-5, rtol=2e-5, mean=2e-5), "bf16": dict(atol=1e-2, rtol=1e-2, mean=6e-3)}
+PROJ_TOL = {"f32": dict(rtol=1e-5, atol=1e-6), "bf16": dict(rtol=4e-3, atol=1e-4)}
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -323,12 +328,13 @@ def cpu_baseline_kl(w, inputs, target_s=6.0, seed=1):
     rows = np.sort(rng.choice(w.n_q, size=n, replace=False))
     sel = orc.run(w, cpu, rows=rows, attention=False)["sel"]
     t0 = time.perf_counter()
-    orc.kl(w, cpu, sel, rows=rows)
+    ref = orc.kl(w, cpu, sel, rows=rows)
     dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+    base = dict(value=n / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
                 sample=f"{n} query rows drawn uniformly (seed {seed}) from the {w.n_q}-row "
                        f"prefill, all {w.h_kv} groups (loss only; their selections are "
                        f"computed first and not timed); {dt:.1f} s")
+    return base, rows, ref
 
 
 def cpu_baseline_bwd(w, inputs, target_s=10.0):
@@ -354,12 +360,13 @@ def cpu_baseline_bwd(w, inputs, target_s=10.0):
     m = int(min(w.n_q, max(32, 32 * target_s / max(dt, 1e-3))))
     ws, cpu, sel, do = sub(m)
     t0 = time.perf_counter()
-    orc.attn_bwd(ws, cpu, sel, do)
+    ref = orc.attn_bwd(ws, cpu, sel, do)
     dt = time.perf_counter() - t0
-    return dict(value=m / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+    base = dict(value=m / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
                 sample=f"the last {m} rows of the {w.n_q}-row prefill, all {w.h_kv} groups and "
                        f"{w.h_q} heads (dq of those rows, their dk and dv contributions; "
                        f"selections computed first and not timed); {dt:.1f} s")
+    return base, m, ref["dq"]
 
 
 def cpu_baseline_project(w, d_model, target_s=5.0, seed=4):
@@ -381,13 +388,15 @@ def cpu_baseline_project(w, d_model, target_s=5.0, seed=4):
     orc.project(x, wq, wk, w.h_kv, w.d_idx)
     dt = time.perf_counter() - t0
     m = int(min(w.n_q, max(256, 256 * target_s / max(dt, 1e-3))))
-    x = rows_x(m)
+    rows = np.sort(rng.choice(w.n_q, size=m, replace=False))
+    x = hid["x"][:, torch.as_tensor(rows, device="cuda")].cpu()
     t0 = time.perf_counter()
-    orc.project(x, wq, wk, w.h_kv, w.d_idx)
+    ref = orc.project(x, wq, wk, w.h_kv, w.d_idx)
     dt = time.perf_counter() - t0
-    return dict(value=w.batch * m / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
+    base = dict(value=w.batch * m / dt, unit="tok/s", cores=orc.max_threads(), kind="oracle",
                 sample=f"{m} rows drawn uniformly (seed {seed}) from the {w.n_q}-row prefill's "
                        f"hidden states (d_model {d_model}); {dt:.1f} s")
+    return base, rows, ref
 
 
 # ------------------------------------------------------------------ counters
@@ -483,7 +492,8 @@ def prefill_leg(w, args, log, cpu_s=8.0, extras=False):
 
 def prefill_extras(w, inp, run, args, log):
     """The alignment loss, the backward and the index projections on the prefill's last
-    step (its selection, o and lse)."""
+    step (its selection, o and lse), each with its oracle baseline and a parity block on
+    the rows the oracle computed."""
     import torch
     from block_sparse_gqa_msa_amd import binding as msa
     from block_sparse_gqa_msa_amd.inputs import generate_dout, generate_hidden
@@ -494,7 +504,6 @@ def prefill_extras(w, inp, run, args, log):
     kl_call = lambda: msa.msa_index_kl(s, inp["q"], inp["k"], inp["q_idx"], inp["k_idx"], run.sel,
                                        run.lse, kl, None, run.ws_attn)
     t_kl, _, reps = timed_reps(kl_call, args.steps, max(1, args.warmup))
-    del kl
     f_kl = kl_work(w)
     out["index_kl"] = dict(workload=w.name, value=w.batch * n / t_kl, unit="tok/s",
                            ms_per_call=t_kl * 1e3, reps=reps,
@@ -514,7 +523,7 @@ def prefill_extras(w, inp, run, args, log):
                s, inp["q"], inp["k"], inp["v"], run.lse, dout, ws_bwd)),
            ("bwd_merge", lambda: msa.msa_sparse_attn_backward_merge(s, run.sel, dq, dk, dv, ws_bwd))]
     t_bst = stage_medians(bst, args.steps)
-    del dout, dq, dk, dv, ws_bwd
+    del dout, dk, dv, ws_bwd
     f_bwd = bwd_work(w)
     out["attn_backward"] = dict(
         workload=w.name, value=w.batch * n / t_bwd, unit="tok/s", ms_per_call=t_bwd * 1e3,
@@ -528,7 +537,7 @@ def prefill_extras(w, inp, run, args, log):
     q_idx_p, k_idx_p = torch.empty_like(inp["q_idx"]), torch.empty_like(inp["k_idx"])
     proj_call = lambda: msa.msa_index_project(s, hid["x"], hid["w_q"], hid["w_k"], q_idx_p, k_idx_p)
     t_pj, _, reps = timed_reps(proj_call, args.steps, max(1, args.warmup))
-    del hid, q_idx_p, k_idx_p
+    del hid
     f_pj, b_pj = project_work(w, d_model)
     # the bound is the larger of the two ideal times (bytes at the HBM peak, FLOPs at MFMA's)
     if b_pj / PEAK_HBM_BYTES >= f_pj / PEAK_BF16_FLOPS:
@@ -545,10 +554,44 @@ def prefill_extras(w, inp, run, args, log):
                                 unit="tok/s", ms_per_call=t_pj * 1e3, reps=reps, roofline=roof)
     log(f"[bench] index projections {t_pj * 1e3:.3f} ms/call")
     if not args.no_cpu:
-        log("[bench] oracle baselines of the alignment loss, the backward, the projections")
-        out["index_kl"]["cpu_baseline"] = cpu_baseline_kl(w, inp)
-        out["attn_backward"]["cpu_baseline"] = cpu_baseline_bwd(w, inp)
-        out["index_project"]["cpu_baseline"] = cpu_baseline_project(w, d_model)
+        log("[bench] oracle baselines and parity of the alignment loss, the backward, the projections")
+        base, rows, ref = cpu_baseline_kl(w, inp)
+        got = kl[:, :, torch.as_tensor(rows, device="cuda")].cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref["kl"])
+        tol = KL_TOL[w.dtype]
+        out["index_kl"]["cpu_baseline"] = base
+        out["index_kl"]["correctness"] = dict(
+            rows_checked=int(got.size), kl_max_abs=float(err.max()),
+            worst_over_bound=float((err / (tol["atol"] + tol["rtol"] * np.abs(ref["kl"]))).max()),
+            tol=tol, **{"pass": bool((err <= tol["atol"] + tol["rtol"] * np.abs(ref["kl"])).all())})
+        base, m, ref_dq = cpu_baseline_bwd(w, inp)
+        got = dq[:, :, -m:].float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref_dq)
+        tol, scale = BWD_TOL[w.dtype], np.abs(ref_dq).max()
+        ok = (err <= tol["atol"] * scale + tol["rtol"] * np.abs(ref_dq)).all() and \
+            err.mean() <= tol["mean"] * np.abs(ref_dq).mean()
+        out["attn_backward"]["cpu_baseline"] = base
+        out["attn_backward"]["correctness"] = dict(
+            rows_checked=int(m * w.batch * w.h_q), tensor="dq of the last rows",
+            dq_max_abs_over_max_ref=float(err.max() / scale),
+            dq_mean_abs_over_mean_ref=float(err.mean() / np.abs(ref_dq).mean()),
+            tol=tol, **{"pass": bool(ok)})
+        base, rows, ref = cpu_baseline_project(w, d_model)
+        ridx = torch.as_tensor(rows, device="cuda")
+        ok, worst = True, 0.0
+        for got_t, want in ((q_idx_p[:, :, ridx], ref["q_idx"]), (k_idx_p[:, ridx], ref["k_idx"])):
+            got = got_t.float().cpu().numpy().astype(np.float64)
+            tol = PROJ_TOL[w.dtype]
+            bound = tol["rtol"] * np.abs(want) + tol["atol"] * np.abs(want).max()
+            worst = max(worst, float((np.abs(got - want) / bound).max()))
+            ok = ok and bool((np.abs(got - want) <= bound).all())
+        out["index_project"]["cpu_baseline"] = base
+        out["index_project"]["correctness"] = dict(rows_checked=int(len(rows) * w.batch),
+                                                   worst_over_bound=worst, tol=PROJ_TOL[w.dtype],
+                                                   **{"pass": ok})
+        for key in ("index_kl", "attn_backward", "index_project"):
+            log(f"[bench] {key} parity: {json.dumps(out[key]['correctness'])}")
+    del kl, dq, q_idx_p, k_idx_p
     torch.cuda.empty_cache()
     return out
 
