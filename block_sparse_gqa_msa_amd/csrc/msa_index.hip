@@ -145,6 +145,12 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
         af[mt][dc] = load_frag(reinterpret_cast<const E *>(
             &lds[buf][(mt * 16 + c16) * L::ROW + (dc * 32 + g * 8) * (int)sizeof(E)]));
     f32x4 acc[4][4];  // [mt][nt]: S^T tile of 16 keys x 16 columns
+    // A wave issuing its matrix-core chain goes first: the compute unit's other waves are
+    // at their pooling, staging or barrier, and an idle matrix core costs more than a
+    // delayed VALU or LDS instruction (the index kernel, 3.21 -> 3.15 ms at 128K, 3.09 ->
+    // 2.95 ms on the 1M-context chunk; over the fragment reads and the pooling as well it
+    // measured slower).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -154,6 +160,7 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
         for (int dc = 0; dc < DC; ++dc) c = mfma_chunk(af[mt][dc], bq[nt][dc], c);
         acc[mt][nt] = c;
       }
+    __builtin_amdgcn_s_setprio(0);
     // Pool each block: max over its keys (rows), then over the four lane groups.
     auto pool = [&](auto masked) {
 #pragma unroll
