@@ -301,6 +301,7 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
       u32x4 px[L::TPT][2];
       float plse = 0.f, pd = 0.f;
       int ppos = -1;
+      bool pok = false;
       auto load_tile = [&](int tt) {
 #pragma unroll
         for (int j = 0; j < L::TPT; ++j) {
@@ -317,16 +318,15 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
                 src + ((head0 + (m & (G - 1))) * a.n_q + t) * DH + dg * L::PE);
           }
         }
-        if (tid < TR) {
-          const int e = tt * RPT + (tid >> log2g);
-          const bool ok = e < n_e;
-          const int t = s_list[ok ? e : 0] >> 6;
-          const long row = (head0 + (tid & (G - 1))) * a.n_q + t;
+        {  // every thread loads (threads past TR repeat a row): no branch around the loads
+          const int mrow = tid & (TR - 1);
+          const int e = tt * RPT + (mrow >> log2g);
+          pok = e < n_e;
+          const int t = s_list[pok ? e : 0] >> 6;
+          const long row = (head0 + (mrow & (G - 1))) * a.n_q + t;
           plse = w.lse[row];
           pd = w.dsum[row];
-          plse = ok ? plse : INFINITY;
-          pd = ok ? pd : 0.f;
-          ppos = ok ? a.q_start + t : -1;
+          ppos = a.q_start + t;
         }
       };
       auto write_tile = [&]() {
@@ -354,18 +354,22 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
           }
         }
         if (tid < TR) {
-          s_lse2[tid] = plse * LOG2E;
-          s_dd[tid] = pd;
-          s_pos[tid] = ppos;
+          s_lse2[tid] = pok ? plse * LOG2E : INFINITY;
+          s_dd[tid] = pok ? pd : 0.f;
+          s_pos[tid] = pok ? ppos : -1;
         }
       };
 
+      // Tile tt + 1 is staged after tile tt's dq stores, and its loads were issued after
+      // tile tt - 1's: at every staging point the same stores are younger than the loads
+      // it waits for, so the wait counts them and leaves them in flight. (Staging at the
+      // top of the loop would merge with the loop entry, where nothing follows the loads,
+      // into a wait for everything.)
       load_tile(0);
+      write_tile();
+      load_tile(min(1, n_tiles - 1));
+      __syncthreads();
       for (int tt = 0; tt < n_tiles; ++tt) {
-        __syncthreads();  // the previous tile is done with the staging buffers
-        write_tile();
-        load_tile(tt + 1 < n_tiles ? tt + 1 : tt);  // in flight over this tile (no branch)
-        __syncthreads();
 
         // S and dP for this wave's 16 keys, row-heads 16 mt + 4 g + i down the rows
         f32x4 s[2], dp[2];
@@ -435,19 +439,36 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // wave-private buffer: in-order LDS
         {
+          // A fixed number of stores per lane with no branch, so that the compiler counts
+          // them: the next tile's wait for its Q / dO loads (issued before these stores)
+          // then leaves the stores in flight instead of waiting for all memory operations.
+          // Row-heads past the chunk's entries store the tile's first row of the same head
+          // again (the same bytes to the same address).
           constexpr int PPR = DSL * L::ES / 16;  // 16-byte pieces per row-head
-          for (int pc = lane; pc < TR * PPR; pc += 64) {
-            const int m = pc / PPR, off = pc % PPR;
-            const int e = tt * RPT + (m >> log2g);
-            if (e < n_e) {
-              const int en = s_list[e];
-              const long pss = ((((long)b * a.h_kv + r) * a.n_q + (en >> 6)) * a.top_k + (en & 63)) * G + (m & (G - 1));
-              __builtin_nontemporal_store(
-                  *reinterpret_cast<const u32x4 *>(so + m * L::OROW + off * 16),
-                  reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.part_o) +
-                                            (pss * DH + wv * DSL) * L::ES + off * 16));
-            }
+          constexpr int NST = TR * PPR / 64;
+          static_assert(TR * PPR % 64 == 0, "dq pieces must fill whole waves");
+          u32x4 val[NST];
+          u32x4 *dst[NST];
+#pragma unroll
+          for (int i = 0; i < NST; ++i) {
+            const int pc = lane + 64 * i, off = pc % PPR;
+            int m = pc / PPR;
+            if (tt * RPT + (m >> log2g) >= n_e) m &= G - 1;
+            const int en = s_list[tt * RPT + (m >> log2g)];
+            const long pss = ((((long)b * a.h_kv + r) * a.n_q + (en >> 6)) * a.top_k + (en & 63)) * G + (m & (G - 1));
+            val[i] = *reinterpret_cast<const u32x4 *>(so + m * L::OROW + off * 16);
+            dst[i] = reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.part_o) +
+                                               (pss * DH + wv * DSL) * L::ES + off * 16);
           }
+#pragma unroll
+          for (int i = 0; i < NST; ++i) __builtin_nontemporal_store(val[i], dst[i]);
+        }
+        if (tt + 1 < n_tiles) {  // uniform
+          // This tile's reads of the staging buffers ended at the barrier before the dq
+          // product, which reads only dS and registers.
+          write_tile();
+          load_tile(min(tt + 2, n_tiles - 1));  // in flight over the next tile (no branch)
+          __syncthreads();
         }
       }
     }

@@ -42,10 +42,18 @@ __device__ __forceinline__ uint32_t mth_key(const uint32_t (&k)[N], int m, uint3
   return K;
 }
 
+// Item indices first + 64 s in slot s (a run of consecutive blocks, one per lane and slot),
+// computed where they are used instead of being held in V registers per lane. Anything
+// indexable by slot serves as the index argument below: such a run or an array.
+struct StridedIdx {
+  int32_t first;  // this lane's index in slot 0
+  __device__ __forceinline__ int32_t operator[](int s) const { return first + 64 * s; }
+};
+
 // The index of the need-th (1-based) item with key K, counting in item order (slot-major,
 // then lane), which is ascending index order: the cut among the items tied at K.
-template <int N>
-__device__ __forceinline__ int32_t tie_cut(const uint32_t (&k)[N], const int32_t (&ix)[N], uint32_t K,
+template <int N, typename IX>
+__device__ __forceinline__ int32_t tie_cut(const uint32_t (&k)[N], const IX &ix, uint32_t K,
                                            int need) {
   int seen = 0;
   int32_t X = 0x7fffffff;
@@ -72,8 +80,8 @@ __device__ __forceinline__ int32_t tie_cut(const uint32_t (&k)[N], const int32_t
 // Returns C >= m when the items with key >= a lower bound T (C of them, in item order:
 // slot-major, then lane) are left in lk / li, or -1 when heavy ties sent it to the
 // exhaustive search (lk / li then hold nothing useful).
-template <int V>
-__device__ int wave_threshold(const uint32_t (&key)[V], const int32_t (&idx)[V], int m,
+template <int V, typename IX>
+__device__ int wave_threshold(const uint32_t (&key)[V], const IX &idx, int m,
                               uint32_t *lk, int32_t *li, uint32_t &kstar, int32_t &istar) {
   constexpr int CAP = SELECT_CAP;
   constexpr int Q = CAP / 64;

@@ -30,18 +30,19 @@ __device__ __forceinline__ void select_chunk(const TopkArgs &a, long pid, int ch
   int32_t *out = a.sel + pid * a.top_k;
   const float *row = a.bmax + pid * (long)a.n_blocks;
   uint32_t key[VI];
-  int32_t idx[VI];
+  const StridedIdx idx{base + lane};  // item (s, lane) is block base + 64 s + lane
   float x[VI];
+  // The row address is the wave's (scalar); each item adds a 32-bit offset, clamped to
+  // the last candidate (items past it are blanked below).
+  const unsigned char *rowb = reinterpret_cast<const unsigned char *>(row);
 #pragma unroll
-  for (int s = 0; s < VI; ++s) x[s] = __builtin_nontemporal_load(row + min(base + s * 64 + lane, n_c - 1));
+  for (int s = 0; s < VI; ++s)
+    x[s] = __builtin_nontemporal_load(
+        reinterpret_cast<const float *>(rowb + (uint32_t)min(idx[s], n_c - 1) * 4u));
 #pragma unroll
   for (int s = 0; s < VI; ++s) pin(x[s]);
 #pragma unroll
-  for (int s = 0; s < VI; ++s) {
-    const int c = base + s * 64 + lane;
-    idx[s] = c;
-    key[s] = c < n_c ? order_key(x[s]) : 0u;
-  }
+  for (int s = 0; s < VI; ++s) key[s] = idx[s] < n_c ? order_key(x[s]) : 0u;
   uint32_t *ck = a.cand_key + (pid * a.n_chunks + chunk) * (long)m;
   int32_t *ci = a.cand_idx + (pid * a.n_chunks + chunk) * (long)m;
   // Write the winners in item order (= ascending block order): to sel for a single chunk,
@@ -86,11 +87,15 @@ __device__ __forceinline__ void select_chunk(const TopkArgs &a, long pid, int ch
   }
 }
 
-// Pass 1. Grid: x = groups of 4 problems (one wave each), y = chunk.
-__global__ __launch_bounds__(256) void topk_pass1(TopkArgs a) {
+// Pass 1. Grid: x = groups of 4 problems (one wave each), y = chunk. A wave ranks one
+// problem, so the loads' latency is hidden by other resident waves: the register budget is
+// held to five waves per SIMD (96 VGPRs, no spills; the unconstrained allocation took 106,
+// four waves). At 128K: 0.66 against 0.77 ms; six waves spill and were slower on long rows.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void topk_pass1(TopkArgs a) {
   __shared__ uint32_t s_key[4][SELECT_LDS];
   __shared__ int32_t s_idx[4][SELECT_LDS];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The wave index is made scalar so that the problem and its row address are too.
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const long n_prob = (long)a.batch * a.h_kv * a.n_q;
   const long pid = (long)blockIdx.x * 4 + w;
   if (pid >= n_prob) return;
