@@ -478,6 +478,11 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
 
 // ---------------------------------------------------------------- dq merge
 
+// Slots whose loads a dq_merge thread issues together: all 32 of a row for bf16 (6.49
+// against 6.67 ms with 8 at 128K; 150 VGPRs, three waves per SIMD), 8 for fp32, whose
+// 32-slot batch would take every register.
+template <typename E> constexpr int DQ_BATCH = sizeof(E) == 2 ? 32 : 8;
+
 // Each (b, r, row) is summed by LPR = G * DH / 8 consecutive threads, 8 outputs of one head
 // each, over the row's valid slots in slot order.
 template <typename E, int DH, int U>
@@ -515,38 +520,49 @@ __global__ __launch_bounds__(256) void dq_merge(KvArgs a, BwdArgs w, int log2g) 
       sl[u] = v ? __builtin_ctzll(v) : -1;
       v &= v - 1;  // no-op once v is 0
     }
+    // Every load is issued (a slot past the row's last reads slot 0 again and is masked
+    // below): loads under branches would go one at a time.
     if constexpr (sizeof(E) == 2) {
       u32x4 x[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        x[u] = sl[u] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(pbase + (long)sl[u] * G * DH))
-                          : u32x4{0u, 0u, 0u, 0u};
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(pbase + (long)max(sl[u], 0) * G * DH));
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (sl[u] >= 0) {
+      for (int u = 0; u < U; ++u) pin(x[u]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += __uint_as_float(x[u][e] << 16);
-            acc[2 * e + 1] += __uint_as_float(x[u][e] & 0xffff0000u);
-          }
+      for (int u = 0; u < U; ++u) {
+        const bool ok = sl[u] >= 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = acc[2 * e] + __uint_as_float(x[u][e] << 16);
+          const float hi = acc[2 * e + 1] + __uint_as_float(x[u][e] & 0xffff0000u);
+          acc[2 * e] = ok ? lo : acc[2 * e];
+          acc[2 * e + 1] = ok ? hi : acc[2 * e + 1];
         }
+      }
     } else {
       f32x4 lo[U], hi[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(pbase + (long)(sl[u] >= 0 ? sl[u] : 0) * G * DH);
-        lo[u] = sl[u] >= 0 ? __builtin_nontemporal_load(p) : f32x4{0.f, 0.f, 0.f, 0.f};
-        hi[u] = sl[u] >= 0 ? __builtin_nontemporal_load(p + 1) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(pbase + (long)max(sl[u], 0) * G * DH);
+        lo[u] = __builtin_nontemporal_load(p);
+        hi[u] = __builtin_nontemporal_load(p + 1);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (sl[u] >= 0) {
+      for (int u = 0; u < U; ++u) {
+        pin(lo[u]);
+        pin(hi[u]);
+      }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[e] += lo[u][e];
-            acc[4 + e] += hi[u][e];
-          }
+      for (int u = 0; u < U; ++u) {
+        const bool ok = sl[u] >= 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a0 = acc[e] + lo[u][e], a1 = acc[4 + e] + hi[u][e];
+          acc[e] = ok ? a0 : acc[e];
+          acc[4 + e] = ok ? a1 : acc[4 + e];
         }
+      }
     }
   }
   const int t = (int)(row % a.n_q);
@@ -637,7 +653,7 @@ hipError_t run_bwd(const KvArgs &a, const BwdArgs &w, const void *o, int log2g, 
   }
   if (!(stages & BWD_STAGE_MERGE)) return hipGetLastError();
   const long threads = (long)a.batch * a.h_kv * a.n_q * ((long)DH << log2g) / 8;
-  hipLaunchKernelGGL((dq_merge<E, DH, 8>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, w,
+  hipLaunchKernelGGL((dq_merge<E, DH, DQ_BATCH<E>>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, w,
                      log2g);
   hipLaunchKernelGGL((dkv_reduce<E, DH, BS>), dim3((unsigned)((long)a.batch * a.h_kv * a.n_blocks)),
                      dim3(256), 0, s, a, w);
