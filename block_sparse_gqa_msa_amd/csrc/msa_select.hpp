@@ -95,19 +95,22 @@ __device__ int wave_threshold(const uint32_t (&key)[V], const IX &idx, int m,
     if (popc64(ballot(lm >= c)) >= m) T = c;
   }
   T = max(T, 1u);
-  // Compact the items >= T into LDS in item order. Every lane writes every step (no branch):
-  // items below T, and positions past CAP, go to the lane's own spare slot.
+  // Compact the items >= T into LDS in item order. A slot with none is skipped (a uniform
+  // branch; usually about a quarter of them); otherwise every lane writes (no divergent
+  // branch): items below T, and positions past CAP, go to the lane's own spare slot.
   int C = 0;
   const int spare = CAP + lane_id();
 #pragma unroll
   for (int s = 0; s < V; ++s) {
     const bool pr = key[s] >= T;
     const uint64_t mk = ballot(pr);
-    const int at = C + rank_below(mk);
-    const int pos = (pr && at < CAP) ? at : spare;
-    lk[pos] = key[s];
-    li[pos] = idx[s];
-    C += popc64(mk);
+    if (mk) {
+      const int at = C + rank_below(mk);
+      const int pos = (pr && at < CAP) ? at : spare;
+      lk[pos] = key[s];
+      li[pos] = idx[s];
+      C += popc64(mk);
+    }
   }
   if (C <= 64) {
     // Few candidates (the usual case): rank each one against all of them. Indices are

@@ -34,15 +34,18 @@ __device__ __forceinline__ void select_chunk(const TopkArgs &a, long pid, int ch
   float x[VI];
   // The row address is the wave's (scalar); each item adds a 32-bit offset, clamped to
   // the last candidate (items past it are blanked below).
+  // A row gets 16 or 32 items per lane only with more than 8 * 64 or 16 * 64 candidates,
+  // so the first half of its slots is always full: no clamp and no blanking there.
+  constexpr int FULL = VI > 8 ? VI / 2 : 0;
   const unsigned char *rowb = reinterpret_cast<const unsigned char *>(row);
 #pragma unroll
   for (int s = 0; s < VI; ++s)
-    x[s] = __builtin_nontemporal_load(
-        reinterpret_cast<const float *>(rowb + (uint32_t)min(idx[s], n_c - 1) * 4u));
+    x[s] = __builtin_nontemporal_load(reinterpret_cast<const float *>(
+        rowb + (uint32_t)(s < FULL ? idx[s] : min(idx[s], n_c - 1)) * 4u));
 #pragma unroll
   for (int s = 0; s < VI; ++s) pin(x[s]);
 #pragma unroll
-  for (int s = 0; s < VI; ++s) key[s] = idx[s] < n_c ? order_key(x[s]) : 0u;
+  for (int s = 0; s < VI; ++s) key[s] = (s < FULL || idx[s] < n_c) ? order_key(x[s]) : 0u;
   uint32_t *ck = a.cand_key + (pid * a.n_chunks + chunk) * (long)m;
   int32_t *ci = a.cand_idx + (pid * a.n_chunks + chunk) * (long)m;
   // Write the winners in item order (= ascending block order): to sel for a single chunk,
