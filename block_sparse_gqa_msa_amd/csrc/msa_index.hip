@@ -306,7 +306,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
   constexpr int DC = DI / 32;
   constexpr int BPT = KT / BS;
   constexpr int MPB = BS / 16;
-  constexpr int NBW = SEL_NBLK / SEL_WAVES;  // blocks per wave
+  constexpr int NTW = SEL_NBLK * BS / KT;    // key tiles of the workgroup's range
   constexpr int SEL_BYTES = SEL_WAVES * SELECT_LDS * 8;
   constexpr int RAW = SEL_WAVES * ST::WAVE_BYTES > SEL_BYTES ? SEL_WAVES * ST::WAVE_BYTES : SEL_BYTES;
   __shared__ float s_m[16][SEL_NBLK];
@@ -318,7 +318,9 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
   const int local = (int)(p / BS);
   const int c0 = wg * SEL_NBLK;
 
+  __shared__ int s_next;  // the range's next unclaimed key tile
   for (int x = tid; x < 16 * SEL_NBLK; x += SEL_WAVES * 64) (&s_m[0][0])[x] = -INFINITY;
+  if (tid == 0) s_next = SEL_WAVES;  // tiles 0 .. SEL_WAVES-1 are the waves' first
   // counters of the kernel that follows in the same decode step start at zero
   if (wg == 0 && b == 0)
     for (int x = tid; x < a.n_zero; x += SEL_WAVES * 64) a.zero[x] = 0;
@@ -331,13 +333,12 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
   for (int dc = 0; dc < DC; ++dc)
     bq[dc] = (c16 < R) ? load_frag(qi + (((long)b * R + c16) * a.n_q) * DI + dc * 32 + g * 8)
                        : zero_frag(qi);
-  const long kw0 = (long)(c0 + w * NBW) * BS;  // this wave's first key
-  constexpr int NT = NBW * BS / KT;            // key tiles per wave
+  const long kb0 = (long)c0 * BS;  // the range's first key
   unsigned char *stg = s_raw + w * ST::WAVE_BYTES;
   // Keys past p read key p instead (pool masks them): unconditional loads keep the next
   // tile's loads in flight, where a load under a branch would make the MFMAs wait for all.
   auto fetch = [&](int tile, u32x4 (&dst)[ST::PPL]) {
-    const long k0 = kw0 + (long)tile * KT;
+    const long k0 = kb0 + (long)tile * KT;
 #pragma unroll
     for (int i = 0; i < ST::PPL; ++i) {
       const int pc = i * 64 + lane;
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
     }
   };
   auto pool = [&](int tile, const u32x4 (&src)[ST::PPL]) {
-    const long k0 = kw0 + (long)tile * KT;
+    const long k0 = kb0 + (long)tile * KT;
     asm volatile("" ::: "memory");  // the previous tile's fragment reads come first
 #pragma unroll
     for (int i = 0; i < ST::PPL; ++i) {
@@ -377,20 +378,36 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
           v[mm * 4 + i] = (need_mask && k0 + mt * 16 + g * 4 + i > p) ? -INFINITY : c[i];
       }
       const float mx = max_groups(max_chain<4 * MPB>(v));
-      if (g == 0 && c16 < R) s_m[c16][w * NBW + tile * BPT + blk] = mx;
+      if (g == 0 && c16 < R) s_m[c16][tile * BPT + blk] = mx;
     }
   };
-  // double-buffered key tiles: the next tile's pieces load while this one computes
-  const int nt = (int)min((long)NT, (p - kw0) / KT + 1);  // tiles with a visible key
-  // The prefetches are unconditional too: past the last tile they re-read the last tile
-  // rather than branch around the load.
+  // Key tiles are claimed at run time from the workgroup's counter (each wave's first is
+  // its own index): with a fixed share per wave the waves of one compute unit finished
+  // their streams up to a third of the kernel apart, the unit's loads in flight thinning
+  // out as they did. A block's maximum does not depend on the wave that pools it.
+  const int ntv = (int)min((long)NTW, (p - kb0) / KT + 1);  // tiles with a visible key
+  auto claim = [&]() {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(t);
+  };
+  // double-buffered key tiles: the next tile's pieces load while this one computes. The
+  // prefetches are unconditional too: a tile past the last re-reads the last one rather
+  // than branch around the load. Claims only grow, so a wave stops at the first tile past
+  // the range, and every tile claimed below it is pooled.
   u32x4 fa[ST::PPL], fb[ST::PPL];
-  if (nt > 0) fetch(0, fa);
-  for (int tile = 0; tile < nt; tile += 2) {
-    fetch(min(tile + 1, nt - 1), fb);
-    pool(tile, fa);
-    fetch(min(tile + 2, nt - 1), fa);
-    if (tile + 1 < nt) pool(tile + 1, fb);
+  int ta = w, tb = claim();
+  fetch(min(ta, ntv - 1), fa);
+  while (ta < ntv) {
+    fetch(min(tb, ntv - 1), fb);
+    const int tc = claim();
+    pool(ta, fa);
+    if (tb >= ntv) break;
+    fetch(min(tc, ntv - 1), fa);
+    const int td = claim();
+    pool(tb, fb);
+    ta = tc;
+    tb = td;
   }
   __syncthreads();
 
