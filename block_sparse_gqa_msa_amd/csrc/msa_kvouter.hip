@@ -490,20 +490,27 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // wave-private buffer: in-order LDS
       {
+        // A fixed number of stores per lane with no branch, so that the compiler counts
+        // them and the next tile's wait for its Q fragments (loaded before these stores)
+        // leaves them in flight. Rows past the chunk's entries store the tile's first row
+        // of the same head again (the same bytes to the same address).
         constexpr int PIECES_ROW = DH * L::ES / 16;  // 16-byte pieces per output row
-        const int pieces = 16 * PIECES_ROW;          // the whole tile
-        for (int pc = lane; pc < pieces; pc += 64) {
-          const int row = pc / PIECES_ROW, off = pc % PIECES_ROW;
-          const int qq = row >> log2g, hh = row & (G - 1);
-          const int ee = tt * QPT + qq;
-          if (ee < n_e) {
-            const int en = s_list[ee];
-            const long pss = ((((long)b * a.h_kv + r) * a.n_q + (en >> 6)) * a.top_k + (en & 63)) * G + hh;
-            __builtin_nontemporal_store(
-                *reinterpret_cast<const u32x4 *>(so + row * OROW + off * 16),
-                reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.part_o) + pss * DH * L::ES + off * 16));
-          }
+        constexpr int NST = 16 * PIECES_ROW / 64;    // the whole tile, per lane
+        static_assert(16 * PIECES_ROW % 64 == 0, "output pieces must fill whole waves");
+        u32x4 val[NST];
+        u32x4 *dst[NST];
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+          const int pc = lane + 64 * i, off = pc % PIECES_ROW;
+          int row = pc / PIECES_ROW;
+          if (tt * QPT + (row >> log2g) >= n_e) row &= G - 1;
+          const int en = s_list[tt * QPT + (row >> log2g)];
+          const long pss = ((((long)b * a.h_kv + r) * a.n_q + (en >> 6)) * a.top_k + (en & 63)) * G + (row & (G - 1));
+          val[i] = *reinterpret_cast<const u32x4 *>(so + row * OROW + off * 16);
+          dst[i] = reinterpret_cast<u32x4 *>(reinterpret_cast<unsigned char *>(a.part_o) + pss * DH * L::ES + off * 16);
         }
+#pragma unroll
+        for (int i = 0; i < NST; ++i) __builtin_nontemporal_store(val[i], dst[i]);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
