@@ -31,8 +31,19 @@ namespace {
 
 constexpr int CHUNK = KV_CHUNK;           // entries per kv_attend work item
 constexpr long KV_Q_SLICE = 64L << 20;    // bytes of one group's Q rows per list segment
-constexpr int HIST_ROWS_ENTRIES = 32768;  // entries per list-build workgroup
+constexpr int HIST_ROWS_ENTRIES = 32768;  // entries per list-build workgroup, at most
 constexpr int HIST_MAX_BLOCKS = 32768;    // LDS histogram capacity (128 KiB)
+
+// Rows per list-build workgroup: HIST_ROWS_ENTRIES entries, halved (down to 2048) while the
+// call would have fewer than 512 workgroups, so that short calls still spread the build
+// over the chip (the 8K prefill had 16 workgroups, the 1M-context chunk 32). Row segments
+// are whole multiples of it, so a workgroup's rows lie in one segment.
+__host__ __device__ __forceinline__ long hist_tile_rows(long batch, long h_kv, long n_q, long top_k) {
+  const long total = batch * h_kv * n_q * top_k;
+  long ent = HIST_ROWS_ENTRIES;
+  while (ent > 2048 && total / ent < 512) ent >>= 1;
+  return ent / top_k > 1 ? ent / top_k : 1;
+}
 
 __global__ void fill_i32(int32_t *p, long n, int32_t v) {
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
@@ -76,12 +87,11 @@ __global__ __launch_bounds__(256) void kv_fill(KvArgs a) {
   a.list[pos] = t * 64 + (int)(e % a.top_k);
 }
 
-__device__ __forceinline__ long hist_rows_per_wg(int top_k) { return max(1, HIST_ROWS_ENTRIES / top_k); }
 
 // Rows of this list-build workgroup (they lie in one row segment); `base` is the list
 // index of block 0 for them.
 __device__ __forceinline__ void hist_rows(const KvArgs &a, long &e_begin, long &e_end, long &base) {
-  const long rows_per_wg = hist_rows_per_wg(a.top_k);
+  const long rows_per_wg = hist_tile_rows(a.batch, a.h_kv, a.n_q, a.top_k);
   const long tiles_per_br = (a.n_q + rows_per_wg - 1) / rows_per_wg;
   const long br = blockIdx.x / tiles_per_br;
   const long r0 = (blockIdx.x % tiles_per_br) * rows_per_wg;
@@ -641,7 +651,7 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
       return (long)v;
     }();
     if (a.n_blocks <= HIST_MAX_BLOCKS && (long)a.n_blocks * (long)sizeof(int32_t) <= lds_max) {
-      const long rows_per_wg = std::max(1, HIST_ROWS_ENTRIES / a.top_k);  // divides seg_rows
+      const long rows_per_wg = hist_tile_rows(a.batch, a.h_kv, a.n_q, a.top_k);  // divides seg_rows
       const unsigned wgs = (unsigned)((long)a.batch * a.h_kv * ((a.n_q + rows_per_wg - 1) / rows_per_wg));
       const size_t lds = (size_t)a.n_blocks * sizeof(int32_t);
       hipLaunchKernelGGL(kv_count_hist, dim3(wgs), dim3(1024), lds, s, a);
@@ -686,9 +696,7 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
 int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long group, long d_h,
                     long elem_bytes) {
   // about KV_Q_SLICE bytes of one group's Q rows per segment, in whole list-build tiles
-  (void)batch;
-  (void)h_kv;
-  const long tile = std::max(1, HIST_ROWS_ENTRIES / (int)top_k);
+  const long tile = hist_tile_rows(batch, h_kv, n_q, top_k);
   const long per_row = group * d_h * elem_bytes;
   long rows = std::max(1L, KV_Q_SLICE / per_row);
   rows = std::max(tile, rows / tile * tile);
