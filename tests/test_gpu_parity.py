@@ -203,6 +203,22 @@ def test_prefill_workload_full_size(name):
         assert np.array_equal(buf.sel.cpu().numpy(), full["sel"]), "selections differ"
 
 
+def test_segments_with_small_list_batches():
+    """Several row segments (16 heads per group: 4 KiB of Q per row, 16384 rows per
+    segment) in a call with few selections, so the list build takes its smallest batches
+    (2048 entries, 1024 rows) and the last segment ends inside a batch."""
+    w = W("segments_small_batches", n_q=40000, n_k=40000, h_q=16, h_kv=1, d_h=128,
+          d_idx=32, block_size=64, top_k=2, needles=4)
+    log(f"case {w.name}: {w}")
+    inp = generate(w, device="cuda")
+    buf = run_gpu(w, inp)
+    check_selection_invariants(w, buf.sel)
+    rows = sorted(set(sample_rows(w, n_random=96)) |
+                  {x for e in (16384, 32768) for x in range(e - 3, e + 3)})
+    ref = oracle_run(w, to_cpu(inp), rows=rows)
+    compare(w, buf, ref, rows=rows, label=w.name)
+
+
 @pytest.mark.parametrize("name,seqs", [("decode_256k_b32", [0, 13, 31]),
                                        ("decode_1m_b4", [0, 3])])
 def test_decode_workload_full_size(name, seqs):
