@@ -32,10 +32,10 @@ __device__ __forceinline__ void select_chunk(const TopkArgs &a, long pid, int ch
   uint32_t key[VI];
   const StridedIdx idx{base + lane};  // item (s, lane) is block base + 64 s + lane
   float x[VI];
-  // The row address is the wave's (scalar); each item adds a 32-bit offset, clamped to
-  // the last candidate (items past it are blanked below).
-  // A row gets 16 or 32 items per lane only with more than 8 * 64 or 16 * 64 candidates,
-  // so the first half of its slots is always full: no clamp and no blanking there.
+  // The row address is the wave's (scalar); each item adds a 32-bit offset, clamped to the
+  // last candidate (items past it are blanked below). A row gets 16 or 32 items per lane
+  // only with more than 8 * 64 or 16 * 64 candidates, so the first half of its slots is
+  // always full: no clamp and no blanking there.
   constexpr int FULL = VI > 8 ? VI / 2 : 0;
   const unsigned char *rowb = reinterpret_cast<const unsigned char *>(row);
 #pragma unroll
@@ -91,10 +91,14 @@ __device__ __forceinline__ void select_chunk(const TopkArgs &a, long pid, int ch
 }
 
 // Pass 1. Grid: x = groups of 4 problems (one wave each), y = chunk. A wave ranks one
-// problem, so the loads' latency is hidden by other resident waves: the register budget is
-// held to five waves per SIMD (96 VGPRs, no spills; the unconstrained allocation took 106,
-// four waves). At 128K: 0.66 against 0.77 ms; six waves spill and were slower on long rows.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void topk_pass1(TopkArgs a) {
+// problem, so the loads' latency is hidden by other resident waves, and the register
+// budget is held to WPE waves per SIMD (the unconstrained allocation took 106 VGPRs, four
+// waves). Rows of one chunk (at most 2048 candidates, a mix of 8, 16 and 32 items per
+// lane) run best at six (80 VGPRs; 0.615 -> 0.576 ms at 128K), rows of several full
+// chunks (32 items per lane throughout) at five (96 VGPRs; 0.496 against 0.508 ms on the
+// 1M-context chunk), with no spills either way.
+template <int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE))) void topk_pass1(TopkArgs a) {
   __shared__ uint32_t s_key[4][SELECT_LDS];
   __shared__ int32_t s_idx[4][SELECT_LDS];
   // The wave index is made scalar so that the problem and its row address are too.
@@ -236,7 +240,10 @@ __global__ __launch_bounds__(MW * 64) void topk_merge_wide(TopkArgs a) {
 hipError_t launch_topk(const TopkArgs &a, hipStream_t s) {
   const long n_prob = (long)a.batch * a.h_kv * a.n_q;
   const unsigned groups = (unsigned)((n_prob + 3) / 4);
-  hipLaunchKernelGGL(topk_pass1, dim3(groups, (unsigned)a.n_chunks), dim3(256), 0, s, a);
+  if (a.n_chunks <= 1)
+    hipLaunchKernelGGL(topk_pass1<6>, dim3(groups, 1u), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_pass1<5>, dim3(groups, (unsigned)a.n_chunks), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks <= 1) return e;
   hipLaunchKernelGGL(topk_pass2, dim3(groups), dim3(256), 0, s, a);
