@@ -175,22 +175,22 @@ class PrefillRun:
         from block_sparse_gqa_msa_amd import binding as msa
         self.w, self.inputs, s = w, inputs, msa.shape_of(w)
         self.s = s
-        R, n, nb = w.h_kv, w.n_q, -(-w.n_k // w.block_size)
+        R, n = w.h_kv, w.n_q
         dev = "cuda"
-        self.scores = torch.empty((w.batch, R, n, nb), dtype=torch.float32, device=dev)
         self.sel = torch.empty((w.batch, R, n, w.top_k), dtype=torch.int32, device=dev)
         self.o = torch.empty((w.batch, w.h_q, n, w.d_h), dtype=inputs["q"].dtype, device=dev)
         self.lse = torch.empty((w.batch, w.h_q, n), dtype=torch.float32, device=dev)
-        self.ws_topk = torch.empty(max(1, msa.msa_topk_workspace_size(s)), dtype=torch.uint8,
-                                   device=dev)
+        # block maxima, top-k candidates and run scores: msa_index_topk's workspace, which
+        # its two stages share
+        self.ws_index = torch.empty(max(1, msa.msa_index_topk_workspace_size(s)),
+                                    dtype=torch.uint8, device=dev)
         self.ws_attn = torch.empty(max(1, msa.msa_sparse_attn_workspace_size(s)),
                                    dtype=torch.uint8, device=dev)
         i = inputs
         self.stages = [
-            ("index_scores", lambda: msa.msa_index_block_scores(s, i["q_idx"], i["k_idx"],
-                                                                self.scores)),
-            ("topk", lambda: msa.msa_topk_from_block_scores(s, self.scores, self.sel,
-                                                            self.ws_topk)),
+            ("index_scores", lambda: msa.msa_index_topk_scores(s, i["q_idx"], i["k_idx"], None,
+                                                               self.ws_index)),
+            ("topk", lambda: msa.msa_index_topk_select(s, self.sel, None, self.ws_index)),
             ("attn_plan", lambda: msa.msa_sparse_attn_prefill_plan(s, self.sel, self.ws_attn)),
             ("attn_partials", lambda: msa.msa_sparse_attn_prefill_partials(
                 s, i["q"], i["k"], i["v"], self.ws_attn)),

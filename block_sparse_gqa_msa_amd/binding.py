@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(PKG, "libmsa.so")
 
 MSA_F32, MSA_BF16 = 0, 1
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = 0, -1, -2, -3, -4
-EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_block_scores",
+EXPORTS = ("msa_index_topk_workspace_size", "msa_index_topk", "msa_index_topk_scores",
+           "msa_index_topk_select", "msa_index_block_scores",
            "msa_topk_workspace_size", "msa_topk_from_block_scores",
            "msa_sparse_attn_workspace_size", "msa_sparse_attn_prefill",
            "msa_sparse_attn_prefill_plan", "msa_sparse_attn_prefill_partials",
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.msa_index_block_scores.argtypes = [S, P, P, P, P]
     lib.msa_topk_from_block_scores.argtypes = [S, P, P, P, ctypes.c_size_t, P]
     lib.msa_index_topk.argtypes = [S, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_index_topk_scores.argtypes = [S, P, P, P, P, ctypes.c_size_t, P]
+    lib.msa_index_topk_select.argtypes = [S, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_prefill.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_prefill_plan.argtypes = [S, P, P, ctypes.c_size_t, P]
     lib.msa_sparse_attn_prefill_partials.argtypes = [S, P, P, P, P, ctypes.c_size_t, P]
@@ -191,6 +194,25 @@ def msa_index_topk(shape: MsaShape, q_idx, k_idx, sel, block_scores=None, worksp
         ctypes.byref(shape), _ptr(q_idx, et, "q_idx"), _ptr(k_idx, et, "k_idx"),
         _ptr(sel, torch.int32, "sel"), _ptr(block_scores, torch.float32, "block_scores"),
         wp, wn, _stream(stream, sel)))
+
+
+def msa_index_topk_scores(shape: MsaShape, q_idx, k_idx, block_scores=None, workspace=None,
+                          stream=None) -> None:
+    import torch
+    et = _elem_dtype(shape)
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_index_topk_scores(
+        ctypes.byref(shape), _ptr(q_idx, et, "q_idx"), _ptr(k_idx, et, "k_idx"),
+        _ptr(block_scores, torch.float32, "block_scores"), wp, wn, _stream(stream, q_idx)))
+
+
+def msa_index_topk_select(shape: MsaShape, sel, block_scores=None, workspace=None,
+                          stream=None) -> None:
+    import torch
+    wp, wn = _ws(workspace)
+    _check(load_library().msa_index_topk_select(
+        ctypes.byref(shape), _ptr(block_scores, torch.float32, "block_scores"),
+        _ptr(sel, torch.int32, "sel"), wp, wn, _stream(stream, sel)))
 
 
 def msa_index_block_scores(shape: MsaShape, q_idx, k_idx, block_scores, stream=None) -> None:

@@ -2,6 +2,7 @@
 // sizing and kernel launches. Every check runs on the host before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -36,6 +37,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 long long n_blocks(const msa_shape &s) { return ((long long)s.n_k + s.block_size - 1) / s.block_size; }
+long long n_runs(const msa_shape &s) { return (n_blocks(s) + msa::RUN_BLOCKS - 1) / msa::RUN_BLOCKS; }
 int cap_of(const msa_shape &s) { return s.kv_capacity ? s.kv_capacity : s.n_k; }
 
 // Checks shared by every entry point.
@@ -76,7 +78,9 @@ int topk_chunks(const msa_shape &s) {
 }
 
 struct IndexWs {
-  size_t bmax, cand, total;
+  // bytes of: the block maxima, each of the two candidate arrays, the run keys; laid out in
+  // that order
+  size_t bmax, cand, rkey, total;
   size_t dec_cand;  // fused decode path: candidate pairs of every index-select workgroup
   bool fused;       // the fused decode path applies
 };
@@ -91,7 +95,7 @@ bool fused_decode_ok(const msa_shape &s) {
          (long long)decode_select_wgs(s) * (s.top_k - 1) <= msa::TOPK_CHUNK;
 }
 
-int index_ws(const msa_shape &s, bool with_bmax, IndexWs *w) {
+int index_ws(const msa_shape &s, bool with_bmax, bool with_runs, IndexWs *w) {
   const long long rows = (long long)s.batch * s.h_kv * s.n_q;
   const int nch = topk_chunks(s);
   if (nch > 1 && (long long)nch * (s.top_k - 1) > msa::TOPK_CHUNK)
@@ -99,7 +103,11 @@ int index_ws(const msa_shape &s, bool with_bmax, IndexWs *w) {
                 ((long long)s.q_start + s.n_q - 1) / s.block_size, s.top_k);
   w->bmax = with_bmax ? align_up((size_t)rows * (size_t)n_blocks(s) * sizeof(float)) : 0;
   w->cand = nch > 1 ? align_up((size_t)rows * nch * (s.top_k - 1) * 4) : 0;
-  w->total = w->bmax + 2 * w->cand;
+  // run keys: prefill rows with more than one chunk of candidates (index kernel to top-k)
+  w->rkey = with_runs && nch > 1 && s.n_q > 1
+                ? align_up(((size_t)rows * (size_t)n_runs(s) + 1) * sizeof(uint32_t))
+                : 0;
+  w->total = w->bmax + 2 * w->cand + w->rkey;
   w->fused = fused_decode_ok(s);
   w->dec_cand = w->fused ? align_up((size_t)rows * decode_select_wgs(s) * (s.top_k - 1) * 4) : 0;
   if (2 * w->dec_cand > w->total) w->total = 2 * w->dec_cand;
@@ -153,7 +161,7 @@ struct StepWs {
 };
 int step_ws(const msa_shape &s, StepWs *w) {
   IndexWs iw;
-  int rc = index_ws(s, true, &iw);
+  int rc = index_ws(s, true, true, &iw);
   if (rc) return rc;
   w->cnt = align_up((size_t)s.batch * s.h_kv * sizeof(int32_t));
   w->idx = align_up(iw.total);
@@ -243,14 +251,15 @@ int msa_index_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
     return ok();
   }
   IndexWs w;
-  if ((rc = index_ws(*shape, true, &w))) return rc;
+  if ((rc = index_ws(*shape, true, true, &w))) return rc;
   *bytes = w.total;
   return ok();
 }
 
-// Shared by msa_index_topk and the two split calls.
+// Shared by msa_index_topk, its two stages and the two split calls. With rkey (prefill only),
+// the index kernel also writes run keys; its key chunks are then whole runs.
 static int launch_scores(const msa_shape &s, const void *q_idx, const void *k_idx, float *bmax,
-                         hipStream_t st) {
+                         uint32_t *rkey, hipStream_t st) {
   msa::IndexArgs ia{q_idx, k_idx, bmax, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
                     (int)n_blocks(s), cap_of(s), 0, nullptr, nullptr, s.top_k};
   hipError_t e;
@@ -259,31 +268,44 @@ static int launch_scores(const msa_shape &s, const void *q_idx, const void *k_id
     e = msa::launch_index_decode(ia, s.dtype, s.d_idx, s.block_size, st);
   } else {
     ia.key_chunk = key_chunk_prefill(s);
+    if (rkey) {  // both powers of two: the larger is a whole number of runs
+      ia.rkey = rkey;
+      ia.n_runs = (int)n_runs(s);
+      ia.key_chunk = std::max(ia.key_chunk, msa::RUN_BLOCKS * s.block_size);
+    }
     e = msa::launch_index_prefill(ia, s.dtype, s.d_idx, s.block_size, st);
   }
   return e == hipSuccess ? MSA_OK : hip_fail(e, "index kernel launch");
 }
 
 static int launch_select(const msa_shape &s, const float *bmax, int32_t *sel, unsigned char *cand,
-                         size_t cand_bytes, hipStream_t st) {
+                         size_t cand_bytes, const uint32_t *rkey, hipStream_t st) {
   msa::TopkArgs ta{bmax, sel, reinterpret_cast<uint32_t *>(cand),
                    reinterpret_cast<int32_t *>(cand + cand_bytes), s.batch, s.n_q, s.q_start,
                    s.h_kv, (int)n_blocks(s), s.block_size, s.top_k, topk_chunks(s),
                    msa::TOPK_CHUNK, 0};
+  ta.rkey = rkey;
+  ta.n_runs = rkey ? (int)n_runs(s) : 0;
   hipError_t e = msa::launch_topk(ta, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e, "top-k kernel launch");
 }
 
-int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx, int32_t *sel,
-                   float *block_scores, void *workspace, size_t workspace_bytes, void *stream) {
+enum { INDEX_STAGE_SCORES = 1, INDEX_STAGE_SELECT = 2, INDEX_STAGE_ALL = 3 };
+
+// msa_index_topk and its two stages: the same workspace layout and kernels either way.
+static int index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx, int32_t *sel,
+                      float *block_scores, void *workspace, size_t workspace_bytes, void *stream,
+                      int stages) {
   int rc = check_shape(shape);
   if (rc) return rc;
   const msa_shape &s = *shape;
   if ((rc = check_index_dims(s))) return rc;
   if (empty(s)) return ok();
-  if (!q_idx || !k_idx || !sel) return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx and sel must be non-NULL");
+  if ((stages & INDEX_STAGE_SCORES) && (!q_idx || !k_idx))
+    return fail(MSA_ERR_INVALID_ARG, "q_idx and k_idx must be non-NULL");
+  if ((stages & INDEX_STAGE_SELECT) && !sel) return fail(MSA_ERR_INVALID_ARG, "sel must be non-NULL");
   IndexWs w;
-  if ((rc = index_ws(s, block_scores == nullptr, &w))) return rc;
+  if ((rc = index_ws(s, block_scores == nullptr, true, &w))) return rc;
   if (w.total && (!workspace || workspace_bytes < w.total))
     return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -292,25 +314,54 @@ int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx,
   if (!block_scores && w.fused) {  // decode: first selection stage inside the index kernel
     uint32_t *ck = reinterpret_cast<uint32_t *>(ws);
     int32_t *ci = reinterpret_cast<int32_t *>(ws + w.dec_cand);
-    msa::IndexArgs ia{q_idx, k_idx, nullptr, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
-                      (int)n_blocks(s), cap_of(s), 0, ck, ci, s.top_k};
-    hipError_t e = msa::launch_index_select_decode(ia, s.dtype, s.d_idx, s.block_size, st);
-    if (e != hipSuccess) return hip_fail(e, "index-select kernel launch");
-    msa::TopkArgs ta{nullptr, sel, ck, ci, s.batch, s.n_q, s.q_start, s.h_kv, (int)n_blocks(s),
-                     s.block_size, s.top_k, decode_select_wgs(s), msa::SEL_NBLK, 1};
-    e = msa::launch_topk_final(ta, st);
-    if (e != hipSuccess) return hip_fail(e, "top-k merge launch");
+    if (stages & INDEX_STAGE_SCORES) {
+      msa::IndexArgs ia{q_idx, k_idx, nullptr, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
+                        (int)n_blocks(s), cap_of(s), 0, ck, ci, s.top_k};
+      hipError_t e = msa::launch_index_select_decode(ia, s.dtype, s.d_idx, s.block_size, st);
+      if (e != hipSuccess) return hip_fail(e, "index-select kernel launch");
+    }
+    if (stages & INDEX_STAGE_SELECT) {
+      msa::TopkArgs ta{nullptr, sel, ck, ci, s.batch, s.n_q, s.q_start, s.h_kv, (int)n_blocks(s),
+                       s.block_size, s.top_k, decode_select_wgs(s), msa::SEL_NBLK, 1};
+      hipError_t e = msa::launch_topk_final(ta, st);
+      if (e != hipSuccess) return hip_fail(e, "top-k merge launch");
+    }
     return ok();
   }
   float *bmax = block_scores ? block_scores : reinterpret_cast<float *>(ws);
-  if (block_scores) {
-    const long long rows = (long long)s.batch * s.h_kv * s.n_q;
-    hipError_t e = msa::launch_fill(block_scores, (size_t)rows * (size_t)n_blocks(s), -INFINITY, st);
-    if (e != hipSuccess) return hip_fail(e, "block score fill");
+  uint32_t *rkey = w.rkey ? reinterpret_cast<uint32_t *>(ws + w.bmax + 2 * w.cand) : nullptr;
+  if (stages & INDEX_STAGE_SCORES) {
+    if (block_scores) {
+      const long long rows = (long long)s.batch * s.h_kv * s.n_q;
+      hipError_t e = msa::launch_fill(block_scores, (size_t)rows * (size_t)n_blocks(s), -INFINITY, st);
+      if (e != hipSuccess) return hip_fail(e, "block score fill");
+    }
+    if ((rc = launch_scores(s, q_idx, k_idx, bmax, rkey, st))) return rc;
   }
-  if ((rc = launch_scores(s, q_idx, k_idx, bmax, st))) return rc;
-  if ((rc = launch_select(s, bmax, sel, ws + w.bmax, w.cand, st))) return rc;
+  if (stages & INDEX_STAGE_SELECT) {
+    if ((rc = launch_select(s, bmax, sel, ws + w.bmax, w.cand, rkey, st))) return rc;
+  }
   return ok();
+}
+
+int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx, int32_t *sel,
+                   float *block_scores, void *workspace, size_t workspace_bytes, void *stream) {
+  return index_topk(shape, q_idx, k_idx, sel, block_scores, workspace, workspace_bytes, stream,
+                    INDEX_STAGE_ALL);
+}
+
+int msa_index_topk_scores(const msa_shape *shape, const void *q_idx, const void *k_idx,
+                          float *block_scores, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  return index_topk(shape, q_idx, k_idx, nullptr, block_scores, workspace, workspace_bytes,
+                    stream, INDEX_STAGE_SCORES);
+}
+
+int msa_index_topk_select(const msa_shape *shape, const float *block_scores, int32_t *sel,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+  // The select stage only reads block_scores (when given): the stage-1 call wrote them.
+  return index_topk(shape, nullptr, nullptr, sel, const_cast<float *>(block_scores), workspace,
+                    workspace_bytes, stream, INDEX_STAGE_SELECT);
 }
 
 int msa_index_block_scores(const msa_shape *shape, const void *q_idx, const void *k_idx,
@@ -322,7 +373,7 @@ int msa_index_block_scores(const msa_shape *shape, const void *q_idx, const void
   if (empty(s)) return ok();
   if (!q_idx || !k_idx || !block_scores)
     return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx and block_scores must be non-NULL");
-  if ((rc = launch_scores(s, q_idx, k_idx, block_scores, reinterpret_cast<hipStream_t>(stream))))
+  if ((rc = launch_scores(s, q_idx, k_idx, block_scores, nullptr, reinterpret_cast<hipStream_t>(stream))))
     return rc;
   return ok();
 }
@@ -336,7 +387,7 @@ int msa_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
     return ok();
   }
   IndexWs w;
-  if ((rc = index_ws(*shape, false, &w))) return rc;
+  if ((rc = index_ws(*shape, false, false, &w))) return rc;
   *bytes = w.total;
   return ok();
 }
@@ -349,12 +400,12 @@ int msa_topk_from_block_scores(const msa_shape *shape, const float *block_scores
   if (empty(s)) return ok();
   if (!block_scores || !sel) return fail(MSA_ERR_INVALID_ARG, "block_scores and sel must be non-NULL");
   IndexWs w;
-  if ((rc = index_ws(s, false, &w))) return rc;
+  if ((rc = index_ws(s, false, false, &w))) return rc;
   if (w.total && (!workspace || workspace_bytes < w.total))
     return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total,
                 workspace ? workspace_bytes : (size_t)0);
   if ((rc = launch_select(s, block_scores, sel, reinterpret_cast<unsigned char *>(workspace),
-                          w.cand, reinterpret_cast<hipStream_t>(stream))))
+                          w.cand, nullptr, reinterpret_cast<hipStream_t>(stream))))
     return rc;
   return ok();
 }
@@ -711,7 +762,7 @@ int msa_decode_step(const msa_shape *shape, const void *q, const void *k_cache, 
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   IndexWs iw;
-  if ((rc = index_ws(s, true, &iw))) return rc;
+  if ((rc = index_ws(s, true, true, &iw))) return rc;
   uint32_t *ck = reinterpret_cast<uint32_t *>(ws_idx);
   int32_t *ci = reinterpret_cast<int32_t *>(ws_idx + iw.dec_cand);
   int32_t *cnt = reinterpret_cast<int32_t *>(ws);

@@ -44,10 +44,12 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 // columns 64w..64w+63 as four 16-column N-tiles) and one chunk of keys. The k_idx tile
 // is staged once in LDS (double-buffered) and feeds every group: the index key is shared.
 // Pooled maxima are collected in LDS for OUT_RUN consecutive blocks and written as
-// contiguous runs of each output row.
-constexpr int OUT_RUN = 32;
+// contiguous runs of each output row. With RK, each lane also keeps the largest maximum of
+// its column over the run and writes its order key, -0 counted as +0, as the run's key
+// (key chunks are then whole runs, so runs are aligned: blocks 32 r .. 32 r + 31).
+constexpr int OUT_RUN = RUN_BLOCKS;
 
-template <typename E, int DI, int BS>
+template <typename E, int DI, int BS, bool RK>
 __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
   using L = KTile<E, DI>;
   using F = typename Frag<E>::type;
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
   if (k_begin > p_last) return;  // uniform over the workgroup
   const long k_end = min(k_begin + (long)a.key_chunk, p_last + 1);
   const int n_tiles = (int)((k_end - k_begin + KT - 1) / KT);
-  const long c_begin = k_begin / BS;  // first block of the chunk (a multiple of OUT_RUN)
+  const long c_begin = k_begin / BS;  // first block of the chunk (a multiple of OUT_RUN with RK)
 
   // B operand: q_idx of this lane's four columns (column = lane % 16 of each N-tile).
   const E *qi = reinterpret_cast<const E *>(a.q_idx);
@@ -128,6 +130,7 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
 
   const int my_col = w * 64 + g * 16 + c16;  // the column whose pooled value this lane holds
   int run = 0;  // blocks collected in s_out
+  float rk = -INFINITY;  // RK: largest maximum of my_col's blocks in the current run
   // One key tile: pooled maxima of LDS buffer `buf` into s_out, the next tile's pieces
   // (register set `nxt`, loaded a tile earlier) into the other buffer, and the flush of a
   // full run of blocks.
@@ -183,7 +186,9 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
           }
           m[nt] = max_chain<4 * MPB>(v);
         }
-        s_out[my_col][run + blk] = max_groups_transpose(m[0], m[1], m[2], m[3]);
+        const float pv = max_groups_transpose(m[0], m[1], m[2], m[3]);
+        s_out[my_col][run + blk] = pv;
+        if constexpr (RK) rk = fmaxf(rk, pv);
       }
     };
     if (need_mask)
@@ -203,6 +208,16 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
       // also wait for the tile loaded a step later and undo the two-tile distance.
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
+      if constexpr (RK) {
+        // One store per lane, after the wait and with no branch (columns past the rows
+        // write the spare word after the array), so the compiler counts it and the next
+        // tiles' waits leave it in flight.
+        const int r = my_col / TQ, t = t0 + my_col % TQ;
+        const long at = t < a.n_q ? (((long)b * R + r) * a.n_q + t) * a.n_runs + c0 / OUT_RUN
+                                  : (long)a.batch * R * a.n_q * a.n_runs;
+        a.rkey[at] = order_key(rk + 0.0f);  // the sum turns -0 into +0
+        rk = -INFINITY;
+      }
     }
     // This set is free again: tile + 3 goes into it (two tiles ahead of its stash). Past
     // the last tile the loads re-read it (cache hits): unconditional loads let the
@@ -462,7 +477,10 @@ hipError_t launch_prefill_t(const IndexArgs &a, hipStream_t s) {
   const long keys = (long)a.q_start + a.n_q;  // last position + 1
   dim3 grid((unsigned)((a.n_q + TQ - 1) / TQ), (unsigned)((keys + a.key_chunk - 1) / a.key_chunk),
             (unsigned)a.batch);
-  hipLaunchKernelGGL((index_pool_prefill<E, DI, BS>), grid, dim3(256), 0, s, a);
+  if (a.rkey)
+    hipLaunchKernelGGL((index_pool_prefill<E, DI, BS, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((index_pool_prefill<E, DI, BS, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,11 @@ struct IndexArgs {
   int top_k;
   int32_t *zero = nullptr;  // index_select_decode: n_zero words cleared for the next kernel
   int n_zero = 0;
+  // index_pool_prefill, when set: per (b, group, row) and aligned run of RUN_BLOCKS blocks,
+  // the run key: order_key of the run's largest block maximum, -0 counted as +0. One more
+  // word after the array takes the stores of columns past the rows.
+  uint32_t *rkey = nullptr;  // [B, R, n_q, n_runs] + 1
+  int n_runs = 0;
 };
 
 constexpr int SEL_NBLK = 256;  // key blocks per fused decode index-select workgroup
@@ -32,6 +37,10 @@ struct TopkArgs {
   int n_chunks;        // candidate chunks per problem (stride of cand_key / cand_idx)
   int chunk_blocks;    // blocks per chunk (TOPK_CHUNK, or SEL_NBLK after the fused decode kernel)
   int final_all;       // merge pass also writes problems with a single chunk (fused decode path)
+  // Run keys from the index kernel (see IndexArgs::rkey), or null. With them, problems with
+  // more than TOPK_CHUNK candidates read only the runs that can hold a winner.
+  const uint32_t *rkey = nullptr;  // [B, R, n_q, n_runs]
+  int n_runs = 0;
 };
 
 struct AttnArgs {
@@ -130,6 +139,7 @@ size_t kv_bwd_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long 
                               long d_h, long block_size, long elem_bytes, BwdLayout *lay);
 
 constexpr int TOPK_CHUNK = 2048;  // candidate blocks one wave ranks at a time
+constexpr int RUN_BLOCKS = 32;    // blocks per run key (aligned runs: blocks 32 r .. 32 r + 31)
 
 // Each launcher validates nothing (the C-ABI layer did) and returns the launch status.
 hipError_t launch_fill(float *p, size_t n, float value, hipStream_t s);

@@ -98,8 +98,32 @@ int msa_index_topk(const msa_shape *shape, const void *q_idx, const void *k_idx,
                    float *block_scores, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The index branch in two calls, for callers that want the block scores (the
- * same kernels msa_index_topk runs, one launch each):
+ * msa_index_topk as two stages on one workspace (for timing or overlapping them
+ * separately): running msa_index_topk_scores then msa_index_topk_select on the same
+ * stream, with the same shape, block_scores (both NULL, or both the same buffer) and
+ * workspace, does exactly what msa_index_topk does with those arguments.
+ *   msa_index_topk_scores  S^idx and the causal block max-pool M^idx: the block
+ *                          maxima (into block_scores if given, else the workspace)
+ *                          and, for rows with more than 2048 candidate blocks, the
+ *                          largest score of every aligned run of 32 blocks, which
+ *                          lets the select stage read only the runs that can hold a
+ *                          winner. Decode shapes: the first selection stage as well.
+ *   msa_index_topk_select  the TopK with the local block forced, from the workspace
+ *                          (and block_scores) the scores stage filled; writes sel.
+ * Arguments, layouts and errors as for msa_index_topk; the workspace holds the
+ * stage-1 results until the select stage has run.
+ */
+int msa_index_topk_scores(const msa_shape *shape, const void *q_idx, const void *k_idx,
+                          float *block_scores, void *workspace, size_t workspace_bytes,
+                          void *stream);
+int msa_index_topk_select(const msa_shape *shape, const float *block_scores, int32_t *sel,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The index branch in two calls with the block scores in a caller-owned buffer
+ * and no shared workspace: the same index kernel as msa_index_topk, then a TopK
+ * that ranks every candidate of the scores (rows with more than 2048 candidates in
+ * chunks of 2048 plus a merge):
  *
  * msa_index_block_scores: token scores and causal block max-pool only. Writes,
  *   for every (b, group, row), the raw block maxima of q_idx . k_idx over the
