@@ -75,26 +75,33 @@ __device__ __forceinline__ float sum_xor16(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Maximum of scores for the index branch's pooling: the IEEE 754-2019 maximum (gfx950's
+// v_maximum3_f32). For values that are not NaN it is the same maximum as fmaxf, -0 below
+// +0; unlike fmaxf it needs no quieting pass (a v_max_f32 x, x, x per operand that the
+// compiler cannot prove canonical, such as matrix-core results and lane swaps), which
+// had been a third of the pooling's instructions.
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Transposing max-reduction over the four lane groups: given per-lane values v0..v3 (one
 // per 16-column N-tile), returns in lane group g the maximum of v_g over all four groups.
 // Uses v_permlane32_swap (x <-> upper half of the other operand) then v_permlane16_swap.
 __device__ __forceinline__ float max_groups_transpose(float v0, float v1, float v2, float v3) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
-  const float t0 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));  // N-tile 0 (lo) / 2 (hi)
-  const float t1 = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));  // N-tile 1 (lo) / 3 (hi)
+  const float t0 = smax(__uint_as_float(a[0]), __uint_as_float(a[1]));  // N-tile 0 (lo) / 2 (hi)
+  const float t1 = smax(__uint_as_float(b[0]), __uint_as_float(b[1]));  // N-tile 1 (lo) / 3 (hi)
   auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(t0), __float_as_uint(t1), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  return smax(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-// Max of N values as a chain of three-input maxima (v_max3_f32).
+// Max of N values as a chain of three-input maxima (v_maximum3_f32).
 template <int N>
 __device__ __forceinline__ float max_chain(const float (&v)[N]) {
   static_assert(N >= 2, "max_chain needs two values");
-  float m = fmaxf(v[0], v[1]);
+  float m = smax(v[0], v[1]);
 #pragma unroll
-  for (int i = 2; i + 1 < N; i += 2) m = fmaxf(fmaxf(m, v[i]), v[i + 1]);
-  if constexpr (N % 2 == 1) m = fmaxf(m, v[N - 1]);
+  for (int i = 2; i + 1 < N; i += 2) m = smax(smax(m, v[i]), v[i + 1]);
+  if constexpr (N % 2 == 1) m = smax(m, v[N - 1]);
   return m;
 }
 
