@@ -116,10 +116,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
-// Order-preserving map of a finite float (or -inf) to uint32: a > b <=> key(a) > key(b).
-// Key 0 is below every float and marks "no candidate".
+// Order-preserving map of a float that is not NaN (infinities included) to uint32:
+// a > b <=> key(a) > key(b) and a == b <=> key(a) == key(b); -0 is first made +0 (the sum
+// below), the same score, so that equal scores tie. Key 0 is below every such float and
+// marks "no candidate".
 __device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
+  uint32_t u = __float_as_uint(x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -45,8 +45,8 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 // is staged once in LDS (double-buffered) and feeds every group: the index key is shared.
 // Pooled maxima are collected in LDS for OUT_RUN consecutive blocks and written as
 // contiguous runs of each output row. With RK, each lane also keeps the largest maximum of
-// its column over the run and writes its order key, -0 counted as +0, as the run's key
-// (key chunks are then whole runs, so runs are aligned: blocks 32 r .. 32 r + 31).
+// its column over the run and writes its order key as the run's key (key chunks are then
+// whole runs, so runs are aligned: blocks 32 r .. 32 r + 31).
 constexpr int OUT_RUN = RUN_BLOCKS;
 
 template <typename E, int DI, int BS, bool RK>
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
         const int r = my_col / TQ, t = t0 + my_col % TQ;
         const long at = t < a.n_q ? (((long)b * R + r) * a.n_q + t) * a.n_runs + c0 / OUT_RUN
                                   : (long)a.batch * R * a.n_q * a.n_runs;
-        a.rkey[at] = order_key(rk + 0.0f);  // the sum turns -0 into +0
+        a.rkey[at] = order_key(rk);
         rk = -INFINITY;
       }
     }

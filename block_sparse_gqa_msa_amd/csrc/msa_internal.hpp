@@ -20,8 +20,8 @@ struct IndexArgs {
   int32_t *zero = nullptr;  // index_select_decode: n_zero words cleared for the next kernel
   int n_zero = 0;
   // index_pool_prefill, when set: per (b, group, row) and aligned run of RUN_BLOCKS blocks,
-  // the run key: order_key of the run's largest block maximum, -0 counted as +0. One more
-  // word after the array takes the stores of columns past the rows.
+  // the run key: order_key of the run's largest block maximum. One more word after the
+  // array takes the stores of columns past the rows.
   uint32_t *rkey = nullptr;  // [B, R, n_q, n_runs] + 1
   int n_runs = 0;
 };

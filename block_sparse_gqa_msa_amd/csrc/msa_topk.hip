@@ -214,16 +214,15 @@ __global__ __launch_bounds__(256) void topk_pass2(TopkArgs a) {
 }
 
 // Candidates 0 .. n_c-1 of one problem, with run keys (the order key of each aligned run's
-// largest block maximum, a largest maximum of -0 taking +0's key). Let T be the m-th
-// largest key of the nf runs that lie wholly before the local block: at least m runs have a
-// key >= T, and a run whose key is below T has its largest maximum strictly below the
-// largest maximum of each of those (keys order the maxima exactly apart from -0 and +0, and
-// a run whose largest maximum is -0 has +0's key), so none of its blocks is among the best
-// m, ties included. The winners therefore lie in the runs whose key reaches T or in the
-// tail after the last whole run: phase 1 finds those runs, phase 2 ranks their blocks and
-// the tail's. Normally about m runs reach T: 2 KiB of run keys and about m cache lines of
-// maxima per problem at 1M context, against 64 KiB for the whole row. (A NaN block maximum,
-// which finite inputs cannot give, does not raise its run's key.)
+// largest block maximum). Let T be the m-th largest key of the nf runs that lie wholly
+// before the local block: at least m runs have a key >= T, each holding a block with that
+// key, and a run whose key is below T has every block below each of those, so none of its
+// blocks is among the best m, ties included. The winners therefore lie in the runs whose
+// key reaches T or in the tail after the last whole run: phase 1 finds those runs, phase
+// 2 ranks their blocks and the tail's. Normally about m runs reach T: 2 KiB of run keys
+// and about m cache lines of maxima per problem at 1M context, against 64 KiB for the
+// whole row. (A NaN block maximum, which finite inputs cannot give, does not raise its
+// run's key.)
 
 // Phase 1: the nf runs' keys, VI per lane; the runs whose key reaches the m-th largest,
 // in ascending order, go to runs[] (64 entries; more are counted, not stored).

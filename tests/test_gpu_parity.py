@@ -99,6 +99,39 @@ def test_few_distinct_scores():
     compare(w, buf, ref, label=w.name)
 
 
+@pytest.mark.parametrize("q_start", [20000, 80000], ids=["one_chunk", "two_chunks"])
+def test_signed_zero_scores_tie(q_start):
+    """Block scores of -0 and +0 are equal scores: the ties at zero go to the lowest blocks,
+    whatever the signs (caller scores through msa_topk_from_block_scores; 32-token blocks,
+    about 625 or 2500 candidates). Expected by construction: five blocks with distinct
+    positive scores, then the lowest-index zero blocks, then the local block."""
+    w = W("signed_zeros", n_q=48, n_k=q_start + 48, q_start=q_start, h_kv=2, h_q=8,
+          block_size=32, top_k=16)
+    s = msa.shape_of(w)
+    nb = -(-w.n_k // w.block_size)
+    rng = np.random.default_rng(5)
+    scores = np.full((1, w.h_kv, w.n_q, nb), -1.0, dtype=np.float32)
+    expect = np.full((1, w.h_kv, w.n_q, w.top_k), -1, dtype=np.int32)
+    for r in range(w.h_kv):
+        for t in range(w.n_q):
+            local = (q_start + t) // w.block_size
+            picks = rng.choice(local, size=45, replace=False)
+            pos, zer = picks[:5], picks[5:]
+            scores[0, r, t, pos] = rng.uniform(1.0, 2.0, size=5).astype(np.float32)
+            scores[0, r, t, zer] = np.where(rng.random(40) < 0.5, -0.0, 0.0).astype(np.float32)
+            chosen = np.concatenate([pos, np.sort(zer)[:w.top_k - 1 - 5], [local]])
+            expect[0, r, t] = np.sort(chosen)
+    assert np.signbit(scores[scores == 0]).any() and (~np.signbit(scores[scores == 0])).any()
+    sc = torch.from_numpy(scores).cuda()
+    sel = torch.full((1, w.h_kv, w.n_q, w.top_k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(1, msa.msa_topk_workspace_size(s)), dtype=torch.uint8, device="cuda")
+    msa.msa_topk_from_block_scores(s, sc, sel, ws)
+    torch.cuda.synchronize()
+    got = sel.cpu().numpy()
+    bad = int((got != expect).any(-1).sum())
+    assert bad == 0, f"{bad} (row, group) selections differ from the expected ties at zero"
+
+
 DECODE_SMALL = [
     W("decode_ragged_bf16", batch=3, n_q=1, n_k=5000, q_start=4999, top_k=16, needles=4),
     W("decode_f32_g2", dtype="f32", batch=2, n_q=1, n_k=3001, q_start=3000, h_q=8, h_kv=4,
