@@ -78,9 +78,9 @@ int topk_chunks(const msa_shape &s) {
 }
 
 struct IndexWs {
-  // bytes of: the block maxima, each of the two candidate arrays, the run keys; laid out in
-  // that order
-  size_t bmax, cand, rkey, total;
+  // bytes of: the block maxima, each of the two candidate arrays, the run keys, the index
+  // kernel's spare destination; laid out in that order
+  size_t bmax, cand, rkey, spare, total;
   size_t dec_cand;  // fused decode path: candidate pairs of every index-select workgroup
   bool fused;       // the fused decode path applies
 };
@@ -107,7 +107,8 @@ int index_ws(const msa_shape &s, bool with_bmax, bool with_runs, IndexWs *w) {
   w->rkey = with_runs && nch > 1 && s.n_q > 1
                 ? align_up(((size_t)rows * (size_t)n_runs(s) + 1) * sizeof(uint32_t))
                 : 0;
-  w->total = w->bmax + 2 * w->cand + w->rkey;
+  w->spare = with_runs && s.n_q > 1 ? 256 : 0;
+  w->total = w->bmax + 2 * w->cand + w->rkey + w->spare;
   w->fused = fused_decode_ok(s);
   w->dec_cand = w->fused ? align_up((size_t)rows * decode_select_wgs(s) * (s.top_k - 1) * 4) : 0;
   if (2 * w->dec_cand > w->total) w->total = 2 * w->dec_cand;
@@ -259,9 +260,10 @@ int msa_index_topk_workspace_size(const msa_shape *shape, size_t *bytes) {
 // Shared by msa_index_topk, its two stages and the two split calls. With rkey (prefill only),
 // the index kernel also writes run keys; its key chunks are then whole runs.
 static int launch_scores(const msa_shape &s, const void *q_idx, const void *k_idx, float *bmax,
-                         uint32_t *rkey, hipStream_t st) {
+                         uint32_t *rkey, float *spare, hipStream_t st) {
   msa::IndexArgs ia{q_idx, k_idx, bmax, s.batch, s.n_q, s.n_k, s.q_start, s.h_kv,
                     (int)n_blocks(s), cap_of(s), 0, nullptr, nullptr, s.top_k};
+  ia.spare = spare;
   hipError_t e;
   if (s.n_q == 1) {
     ia.key_chunk = key_chunk_decode(s);
@@ -330,13 +332,14 @@ static int index_topk(const msa_shape *shape, const void *q_idx, const void *k_i
   }
   float *bmax = block_scores ? block_scores : reinterpret_cast<float *>(ws);
   uint32_t *rkey = w.rkey ? reinterpret_cast<uint32_t *>(ws + w.bmax + 2 * w.cand) : nullptr;
+  float *spare = w.spare ? reinterpret_cast<float *>(ws + w.bmax + 2 * w.cand + w.rkey) : nullptr;
   if (stages & INDEX_STAGE_SCORES) {
     if (block_scores) {
       const long long rows = (long long)s.batch * s.h_kv * s.n_q;
       hipError_t e = msa::launch_fill(block_scores, (size_t)rows * (size_t)n_blocks(s), -INFINITY, st);
       if (e != hipSuccess) return hip_fail(e, "block score fill");
     }
-    if ((rc = launch_scores(s, q_idx, k_idx, bmax, rkey, st))) return rc;
+    if ((rc = launch_scores(s, q_idx, k_idx, bmax, rkey, spare, st))) return rc;
   }
   if (stages & INDEX_STAGE_SELECT) {
     if ((rc = launch_select(s, bmax, sel, ws + w.bmax, w.cand, rkey, st))) return rc;
@@ -373,7 +376,8 @@ int msa_index_block_scores(const msa_shape *shape, const void *q_idx, const void
   if (empty(s)) return ok();
   if (!q_idx || !k_idx || !block_scores)
     return fail(MSA_ERR_INVALID_ARG, "q_idx, k_idx and block_scores must be non-NULL");
-  if ((rc = launch_scores(s, q_idx, k_idx, block_scores, nullptr, reinterpret_cast<hipStream_t>(stream))))
+  if ((rc = launch_scores(s, q_idx, k_idx, block_scores, nullptr, nullptr,
+                          reinterpret_cast<hipStream_t>(stream))))
     return rc;
   return ok();
 }

@@ -49,8 +49,8 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 // whole runs, so runs are aligned: blocks 32 r .. 32 r + 31).
 constexpr int OUT_RUN = RUN_BLOCKS;
 
-template <typename E, int DI, int BS, bool RK>
-__global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
+template <typename E, int DI, int BS, bool RK, bool CF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void index_pool_prefill(IndexArgs a) {
   using L = KTile<E, DI>;
   using F = typename Frag<E>::type;
   constexpr int DC = DI / 32;
@@ -128,6 +128,39 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
     }
   };
 
+  // CF (rows a whole number of runs long, runs aligned, a spare destination given): each
+  // wave writes its own 64 columns' run, 8 lanes per column and 16 bytes per lane, always 8
+  // stores per lane with no branch. Blocks past the run's end are written as -inf, their
+  // value: they lie past every row's local block (the run ends where the last row's keys
+  // do) and inside the row. Columns past the rows write the spare 16 bytes. The compiler
+  // counts these stores, so no wait for them follows, and no barrier either: only this
+  // wave's lanes wrote these columns of s_out and only they read them.
+  auto flush_counted = [&](long c0, int n) {
+    // The lane index as the asm leaves it: the addresses below are then computed here, not
+    // hoisted out of the tile loop into registers held all along.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = ln + 64 * i, col = w * 64 + (pc >> 3), j0 = (pc & 7) * 4;
+      const int r = col / TQ, t = t0 + col % TQ;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = s_out[col][j0 + e];  // every lane reads, then selects
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pin(x[e]);
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = j0 + e < n ? x[e] : -INFINITY;
+      float *dst = t < a.n_q ? a.bmax + (((long)b * R + r) * a.n_q + t) * a.n_blocks + c0 + j0
+                             : a.spare;
+      *reinterpret_cast<f32x4 *>(dst) = v;
+      // one store at a time: hoisting every piece's reads and address ahead of the stores
+      // took the registers of the main loop
+      asm volatile("" ::: "memory");
+    }
+  };
+
   const int my_col = w * 64 + g * 16 + c16;  // the column whose pooled value this lane holds
   int run = 0;  // blocks collected in s_out
   float rk = -INFINITY;  // RK: largest maximum of my_col's blocks in the current run
@@ -198,18 +231,28 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
     run += BPT;
     if (tile + 1 < n_tiles) stash(buf ^ 1, nxt);
     __syncthreads();
+    // This set is free again: tile + 3 goes into it (two tiles ahead of its stash). Past
+    // the last tile the loads re-read it (cache hits): unconditional loads let the
+    // compiler wait for exactly the set it stashes, not for every load in flight. With the
+    // counted flush the loads go first, so that the set's registers are live across the
+    // flush and are not reused for its stores (which would make the loads wait for them).
+    if constexpr (CF) fetch(min(tile + 3, n_tiles - 1), nxt);
     if (run == OUT_RUN || tile + 1 == n_tiles) {
       const long c0 = c_begin + (long)(tile + 1) * BPT - run;
-      flush(c0, run);
+      if constexpr (CF) {
+        flush_counted(c0, run);
+      } else {
+        flush(c0, run);
+        // Wait for the maxima stores here, once per run: with stores of unknown completion
+        // in flight the compiler makes every later wait for a k_idx tile a wait for all
+        // memory operations (loads and stores need not complete in order), which would
+        // also wait for the tile loaded a step later and undo the two-tile distance.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+      }
       run = 0;
-      // Wait for the maxima stores here, once per run: with stores of unknown completion
-      // in flight the compiler makes every later wait for a k_idx tile a wait for all
-      // memory operations (loads and stores need not complete in order), which would
-      // also wait for the tile loaded a step later and undo the two-tile distance.
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __syncthreads();
       if constexpr (RK) {
-        // One store per lane, after the wait and with no branch (columns past the rows
+        // One store per lane, after the maxima and with no branch (columns past the rows
         // write the spare word after the array), so the compiler counts it and the next
         // tiles' waits leave it in flight.
         const int r = my_col / TQ, t = t0 + my_col % TQ;
@@ -219,10 +262,7 @@ __global__ __launch_bounds__(256) void index_pool_prefill(IndexArgs a) {
         rk = -INFINITY;
       }
     }
-    // This set is free again: tile + 3 goes into it (two tiles ahead of its stash). Past
-    // the last tile the loads re-read it (cache hits): unconditional loads let the
-    // compiler wait for exactly the set it stashes, not for every load in flight.
-    fetch(min(tile + 3, n_tiles - 1), nxt);
+    if constexpr (!CF) fetch(min(tile + 3, n_tiles - 1), nxt);
   };
   fetch(0, pa);
   fetch(min(1, n_tiles - 1), pb);
@@ -477,10 +517,16 @@ hipError_t launch_prefill_t(const IndexArgs &a, hipStream_t s) {
   const long keys = (long)a.q_start + a.n_q;  // last position + 1
   dim3 grid((unsigned)((a.n_q + TQ - 1) / TQ), (unsigned)((keys + a.key_chunk - 1) / a.key_chunk),
             (unsigned)a.batch);
-  if (a.rkey)
-    hipLaunchKernelGGL((index_pool_prefill<E, DI, BS, true>), grid, dim3(256), 0, s, a);
+  // the counted flush needs whole, aligned runs in every row and a spare destination
+  const bool cf = a.spare && a.n_blocks % OUT_RUN == 0 && (a.key_chunk / BS) % OUT_RUN == 0;
+  if (a.rkey && cf)
+    hipLaunchKernelGGL((index_pool_prefill<E, DI, BS, true, true>), grid, dim3(256), 0, s, a);
+  else if (a.rkey)
+    hipLaunchKernelGGL((index_pool_prefill<E, DI, BS, true, false>), grid, dim3(256), 0, s, a);
+  else if (cf)
+    hipLaunchKernelGGL((index_pool_prefill<E, DI, BS, false, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((index_pool_prefill<E, DI, BS, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((index_pool_prefill<E, DI, BS, false, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -24,6 +24,9 @@ struct IndexArgs {
   // array takes the stores of columns past the rows.
   uint32_t *rkey = nullptr;  // [B, R, n_q, n_runs] + 1
   int n_runs = 0;
+  // index_pool_prefill: 16 bytes (16-byte aligned) that take the stores of columns past
+  // the rows, or null; with it the maxima are flushed with a fixed number of stores.
+  float *spare = nullptr;
 };
 
 constexpr int SEL_NBLK = 256;  // key blocks per fused decode index-select workgroup

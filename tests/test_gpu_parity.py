@@ -236,6 +236,37 @@ def test_prefill_workload_full_size(name):
         assert np.array_equal(buf.sel.cpu().numpy(), full["sel"]), "selections differ"
 
 
+@pytest.mark.parametrize("shape", [
+    # 512 key blocks per row, key chunks of 32 blocks: the counted flush without run keys
+    dict(name="counted_flush_32k", n_q=32768, n_k=32768, q_start=0, block_size=64, h_kv=4,
+         h_q=32, top_k=16, sampled=True),
+    # 2208 blocks of 32 keys (rows past one top-k chunk: run keys, key chunks of 32+
+    # blocks), 656 rows in row tiles of 128 (the last one ragged: the spare destination)
+    dict(name="counted_flush_runs", n_q=656, n_k=70656, q_start=70000, block_size=32,
+         h_kv=2, h_q=8, top_k=24, sampled=False),
+], ids=lambda d: d["name"])
+def test_counted_flush_block_scores(shape):
+    """The maxima flushed with a fixed number of stores per lane (rows a whole number of
+    32-block runs, a workspace for the spare destination): block scores bit-exact against
+    the oracle, -inf past each row's local block, then the selection and the outputs."""
+    d = dict(shape)
+    name, sampled = d.pop("name"), d.pop("sampled")
+    w = W(name, d_h=64, d_idx=64, needles=8, **d)
+    assert (-(-w.n_k // w.block_size)) % 32 == 0
+    log(f"case {w.name}: {w}")
+    inp = generate(w, device="cuda")
+    buf = run_gpu(w, inp, block_scores=True)
+    check_selection_invariants(w, buf.sel)
+    rows = sample_rows(w, n_random=96) if sampled else None
+    ref = oracle_run(w, to_cpu(inp), rows=rows, block_scores=True)
+    bs = buf.block_scores
+    if rows is not None:
+        bs = bs[:, :, torch.as_tensor(rows, device=bs.device)]
+    assert np.array_equal(bs.cpu().numpy().astype(np.float64), ref["block_scores"]), \
+        "block scores differ"
+    compare(w, buf, ref, rows=rows, label=name)
+
+
 def test_segments_with_small_list_batches():
     """Several row segments (16 heads per group: 4 KiB of Q per row, 16384 rows per
     segment) in a call with few selections, so the list build takes its smallest batches
