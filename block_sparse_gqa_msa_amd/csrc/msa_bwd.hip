@@ -86,31 +86,42 @@ struct BwdLds {
   static constexpr int NT = 64 * NW;                 // threads
   static constexpr int DSL = DH / NW;                // dq columns per wave
   static constexpr int PE = 16 / ES;                 // elements per 16-byte piece
-  static constexpr int QROW = DH * ES + 16;          // Q, dO row-major rows
-  static constexpr int TROW = TR * ES + 16;         // Q^T, dO^T rows (one per d)
-  static constexpr int SROW = BS * ES + 16;          // dS rows, K^T rows
-  static constexpr int OROW = DSL * ES + 16;         // per-wave dq staging rows
+  // Row pitches. A matrix-core fragment read puts rows 0-7 at 16-byte piece p and rows
+  // 8-15 at piece p + 1 in one 16-lane group of the LDS; bf16 rows of 256 or 128 bytes
+  // padded by 32 bytes place the two halves on even and odd 16-byte bank groups, with
+  // addresses that stay linear (16-byte padding collided there). Other shapes keep 16.
+  static constexpr bool P32Q = ES == 2 && DH * ES == 256;
+  static constexpr bool P32S = ES == 2 && BS * ES == 128;
+  static constexpr int QPIECES = DH * ES / 16;             // 16-byte pieces per Q, dO row
+  static constexpr int QROW = DH * ES + (P32Q ? 32 : 16);  // Q, dO row-major rows
+  static constexpr int TROW = TR * ES + 16;               // Q^T, dO^T rows (one per d)
+  static constexpr int SROW = BS * ES + (P32S ? 32 : 16);  // dS rows, K^T rows
+  static constexpr int OROW = DSL * ES + 16;              // per-wave dq staging rows
   static constexpr int NTASK = 16 * (DH / PE);       // (row pair, piece) tasks per tensor
   static constexpr int TPT = 2 * NTASK / NT;         // staging tasks per thread (Q and dO)
   static_assert(NT == 4 * BS && 2 * NTASK % NT == 0, "staging tasks must divide evenly");
 };
 
-// bf16 transposed staging rows hold 16 dwords of row-head pairs; the dword of pair p in row
-// d is p ^ tr_swz(d). The XOR (even, so 4-row-head units stay whole) spreads the staging
-// writes, whose lanes step d by 8, over the banks, while the fragment reads, whose lanes
-// step d by 1 within a 16-row tile, see one swizzle per instruction.
-__device__ __forceinline__ int tr_swz(int d) { return 2 * ((d >> 4) & 7); }
-
-// The 8 K-elements of a 32-wide chunk whose A side comes from two accumulator tiles:
-// row-heads 4g + 0..3 of the first, then 4g + 0..3 of the second (16 + 4g + 0..3), read
-// from transposed staging row d.
-__device__ __forceinline__ bf16x8 tr_frag(const unsigned char *row, int d, int g, const bf16_t *) {
-  const int sw = tr_swz(d);
-  const u32x2 lo = *reinterpret_cast<const u32x2 *>(row + ((2 * g) ^ sw) * 4);
-  const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + ((8 + 2 * g) ^ sw) * 4);
-  return __builtin_bit_cast(bf16x8, (u32x4{lo[0], lo[1], hi[0], hi[1]}));
+// B side of dV += P^T dO and dK += dS^T Q, bf16: the 8 K-elements of a 32-wide chunk whose
+// A side comes from two accumulator tiles are row-heads 4g + 0..3, then 16 + 4g + 0..3,
+// for column d0 + lane % 16. They are read transposed straight from the row-major tile with
+// ds_read_b64_tr_b16: in each 16-lane group, lanes 4s .. 4s + 3 give the addresses of the
+// four 4-element pieces of row s (columns d0 .. d0 + 15), and lane i receives element i of
+// the group's four rows. With 288-byte rows the 8 rows of a 32-lane group sit on distinct
+// pairs of 16-byte bank groups.
+template <typename L>
+__device__ __forceinline__ bf16x8 tr_frag_rm(const unsigned char *tile, int d0, int g, int lane) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  typedef __attribute__((address_space(3))) v4s *lds_v4s;
+  const int s = (lane & 15) >> 2, j = lane & 3;
+  unsigned char *p = const_cast<unsigned char *>(tile) + (4 * g + s) * L::QROW + (d0 + 4 * j) * 2;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 16 * L::QROW));
+  return __builtin_bit_cast(bf16x8, (v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}));
 }
-__device__ __forceinline__ f32x8 tr_frag(const unsigned char *row, int, int g, const float *) {
+// fp32: the same 8 K-elements from transposed staging row d (one row per column).
+__device__ __forceinline__ f32x8 tr_frag(const unsigned char *row, int g) {
   const f32x4 lo = *reinterpret_cast<const f32x4 *>(row + (4 * g) * 4);
   const f32x4 hi = *reinterpret_cast<const f32x4 *>(row + (16 + 4 * g) * 4);
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -208,8 +219,9 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
   constexpr int QN = DSL / 16, KS = BS / 32;
   __shared__ __attribute__((aligned(16))) unsigned char s_q[TR * L::QROW];
   __shared__ __attribute__((aligned(16))) unsigned char s_do[TR * L::QROW];
-  __shared__ __attribute__((aligned(16))) unsigned char s_qt[DH * L::TROW];
-  __shared__ __attribute__((aligned(16))) unsigned char s_dot[DH * L::TROW];
+  // transposed copies: fp32 only (bf16 reads the row-major tiles transposed)
+  __shared__ __attribute__((aligned(16))) unsigned char s_qt[L::ES == 2 ? 16 : DH * L::TROW];
+  __shared__ __attribute__((aligned(16))) unsigned char s_dot[L::ES == 2 ? 16 : DH * L::TROW];
   __shared__ __attribute__((aligned(16))) unsigned char s_ds[TR * L::SROW];
   __shared__ __attribute__((aligned(16))) unsigned char s_kt[DH * L::SROW];
   __shared__ __attribute__((aligned(16))) unsigned char s_o[NW][TR * L::OROW];
@@ -336,18 +348,10 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
           const int tensor = task / L::NTASK, tk = task % L::NTASK;
           const int p = tk / (DH / L::PE), dg = tk % (DH / L::PE);
           unsigned char *rm = tensor ? s_do : s_q;
-          unsigned char *tr = tensor ? s_dot : s_qt;
           *reinterpret_cast<u32x4 *>(rm + (2 * p) * L::QROW + dg * 16) = px[j][0];
           *reinterpret_cast<u32x4 *>(rm + (2 * p + 1) * L::QROW + dg * 16) = px[j][1];
-          if constexpr (L::ES == 2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t x = px[j][0][e], y = px[j][1][e];
-              const int d = dg * 8 + 2 * e, col = (p ^ tr_swz(d)) * 4;  // d and d + 1 share it
-              *reinterpret_cast<uint32_t *>(tr + d * L::TROW + col) = (x & 0xffffu) | (y << 16);
-              *reinterpret_cast<uint32_t *>(tr + (d + 1) * L::TROW + col) = (x >> 16) | (y & 0xffff0000u);
-            }
-          } else {
+          if constexpr (L::ES == 4) {  // fp32: transposed copy (one row per d)
+            unsigned char *tr = tensor ? s_dot : s_qt;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               *reinterpret_cast<u32x2 *>(tr + (dg * 4 + e) * L::TROW + p * 8) = u32x2{px[j][0][e], px[j][1][e]};
@@ -406,9 +410,14 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
           const F as = acc_frag(dp[0], dp[1], tagp);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int d = dt * 16 + c16;
-            dv[dt] = mfma_chunk(ap, tr_frag(s_dot + d * L::TROW, d, g, tagp), dv[dt]);
-            dk[dt] = mfma_chunk(as, tr_frag(s_qt + d * L::TROW, d, g, tagp), dk[dt]);
+            if constexpr (L::ES == 2) {
+              dv[dt] = mfma_chunk(ap, tr_frag_rm<L>(s_do, dt * 16, g, lane), dv[dt]);
+              dk[dt] = mfma_chunk(as, tr_frag_rm<L>(s_q, dt * 16, g, lane), dk[dt]);
+            } else {
+              const int d = dt * 16 + c16;
+              dv[dt] = mfma_chunk(ap, tr_frag(s_dot + d * L::TROW, g), dv[dt]);
+              dk[dt] = mfma_chunk(as, tr_frag(s_qt + d * L::TROW, g), dk[dt]);
+            }
           }
         }
         // dS (as the matrix cores take it) to LDS for the dq product
@@ -449,10 +458,19 @@ __global__ __launch_bounds__(4 * BS) void kv_bwd(KvArgs a, BwdArgs w, int log2g)
           static_assert(TR * PPR % 64 == 0, "dq pieces must fill whole waves");
           u32x4 val[NST];
           u32x4 *dst[NST];
+          // 80-byte rows of 4 pieces: each 16-lane group of the 16-byte reads takes four
+          // rows whose bank groups do not overlap (rows 4 j + group for j = 0..3).
+          constexpr bool REMAP = L::ES == 2 && PPR == 4 && L::OROW == 80;
+          int qrow = lane >> 2;
+          if constexpr (REMAP) {
+            const int hi = qrow >> 3, lo = qrow & 7, inner = ((lo + 2) >> 2) & 1;
+            const int grp = 2 * hi + inner, j = inner ? lo - 2 : (lo < 2 ? lo : lo - 4);
+            qrow = 4 * j + grp;
+          }
 #pragma unroll
           for (int i = 0; i < NST; ++i) {
             const int pc = lane + 64 * i, off = pc % PPR;
-            int m = pc / PPR;
+            int m = REMAP ? 16 * i + qrow : pc / PPR;
             if (tt * RPT + (m >> log2g) >= n_e) m &= G - 1;
             const int en = s_list[tt * RPT + (m >> log2g)];
             const long pss = ((((long)b * a.h_kv + r) * a.n_q + (en >> 6)) * a.top_k + (en & 63)) * G + (m & (G - 1));
