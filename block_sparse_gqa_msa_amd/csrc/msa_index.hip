@@ -61,8 +61,11 @@ __global__ void fill_kernel(float *p, size_t n, float value) {
 // whole runs, so runs are aligned: blocks 32 r .. 32 r + 31).
 constexpr int OUT_RUN = RUN_BLOCKS;
 
+// bf16 asks the compiler for three waves per SIMD; fp32 (twice the fragment registers)
+// cannot fit three and takes the default.
 template <typename E, int DI, int BS, bool RK, bool CF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void index_pool_prefill(IndexArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 3 : 1)))
+void index_pool_prefill(IndexArgs a) {
   using L = KTile<E, DI>;
   using F = typename Frag<E>::type;
   constexpr int DC = DI / 32;

@@ -83,7 +83,14 @@ template <typename E, int DH, int DI, int BS, int LG>
 __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   using F = typename Frag<E>::type;
   constexpr int ES = (int)sizeof(E);
-  constexpr int KROW = DH * ES + 16, IROW = DI * ES + 16;
+  // Row pitches. A fragment read's 16 lanes of one LDS pass take rows 0-7 at 16-byte piece
+  // p and rows 8-15 at piece p + 1: bf16 rows padded by 32 bytes put the two halves on the
+  // even and odd 16-byte bank groups (16 bytes of padding left two lanes on one group).
+  constexpr int PAD = ES == 2 ? 32 : 16;
+  constexpr int KROW = DH * ES + PAD, IROW = DI * ES + PAD;
+  // Index-score tile rows of BS + 4 floats: a write's lane groups (rows 4 g + i) start 16
+  // banks apart.
+  constexpr int SXR = BS + 4;
   constexpr int DC = DH / 32, DCI = DI / 32, KTN = BS / 16;
   constexpr int R4 = 4 >> LG;  // rows per lane group
   __shared__ __attribute__((aligned(16))) unsigned char s_k[BS * KROW];
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(256) void kv_kl(KvArgs a, KlArgs k, int log2g) {
   static_assert(KV_CHUNK <= 256, "kv_kl: chunks longer than the workgroup are untested");
   __shared__ float4 s_part[KV_CHUNK];  // the chunk's results, stored once per chunk: a store
   __shared__ float2 s_ml[KV_CHUNK];    // per tile would be waited for with the next loads
-  __shared__ float s_sx[4][16][BS + 1];  // per wave: index scores of 16 entry rows x BS keys
+  __shared__ float s_sx[4][16][SXR];  // per wave: index scores of 16 entry rows x BS keys
 
   const long NB = (long)a.n_seg * a.batch * a.h_kv * a.n_blocks;
   const int n_chunks = a.coff[NB];

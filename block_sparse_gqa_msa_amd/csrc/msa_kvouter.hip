@@ -245,13 +245,30 @@ __global__ __launch_bounds__(256) void kv_scan_apply(KvArgs a) {
 
 // ---------------------------------------------------------------- attention per block
 
+// LDS layout of a staged block. The matrix-core fragment reads of K take 16-byte pieces:
+// in each pass of the LDS, 16 lanes read rows 0-7 at piece p and rows 8-15 at piece p + 1,
+// and those 16 pieces must fall on distinct 16-byte bank groups (the 64 banks hold 16).
+//   bf16, 256-byte K rows of 64-key blocks: unpadded, the piece XORed by 2 * (row & 7):
+//     rows 0-7 take the 8 pieces of p's parity, rows 8-15 the other 8, with no LDS spent
+//     on padding (that kernel holds three workgroups per compute unit only within this
+//     budget). The XOR costs a VGPR per piece address, so it is used only there.
+//   bf16, other K rows: padded by 32 bytes, which places rows 0-7 and 8-15 on the even
+//     and odd bank groups.
+//   bf16 V^T rows padded by 8 bytes: the two 8-byte halves of a fragment, 32 bytes apart,
+//     are read by one ds_read2_b64, which measured free of bank conflicts at this pitch
+//     (and at 7.5 conflict cycles per instruction with 16 bytes of padding).
 template <typename E, int DH, int BS>
 struct KvLds {
   static constexpr int ES = (int)sizeof(E);
-  static constexpr int KROW = DH * ES + 16;                  // K row-major, padded rows
+  static constexpr bool KSWZ = ES == 2 && DH * ES == 256 && BS == 64;
+  static constexpr int KROW = KSWZ ? DH * ES : DH * ES + (ES == 2 ? 32 : 16);  // K row-major
   static constexpr int VROW = BS * ES + (ES == 2 ? 8 : 16);  // V^T rows (one per d)
   static constexpr int K_BYTES = BS * KROW;
   static constexpr int V_BYTES = DH * VROW;
+  // byte offset of 16-byte piece `piece` of K row `row`
+  __device__ static __forceinline__ int k_at(int row, int piece) {
+    return row * KROW + (KSWZ ? piece ^ (2 * (row & 7)) : piece) * 16;
+  }
 };
 
 // Stage block rows [kb, kb+BS) of K (row-major) and V (transposed) into LDS, 256 threads.
@@ -300,7 +317,7 @@ __device__ __forceinline__ void stage_block(const E *kp, const E *vp, long kb, i
     for (int i = 0; i < KPT; ++i) {
       const int pc = tid + 256 * i;
       if (KPIECES % 256 == 0 || pc < KPIECES)
-        *reinterpret_cast<u32x4 *>(ks + (pc / PER_ROW) * L::KROW + (pc % PER_ROW) * 16) = kx[i];
+        *reinterpret_cast<u32x4 *>(ks + L::k_at(pc / PER_ROW, pc % PER_ROW)) = kx[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -333,7 +350,7 @@ __device__ __forceinline__ void stage_block(const E *kp, const E *vp, long kb, i
     for (int i = 0; i < KPT; ++i) {
       const int pc = tid + 256 * i;
       if (KPIECES % 256 == 0 || pc < KPIECES)
-        *reinterpret_cast<u32x4 *>(ks + (pc / PER_ROW) * L::KROW + (pc % PER_ROW) * 16) = kx[i];
+        *reinterpret_cast<u32x4 *>(ks + L::k_at(pc / PER_ROW, pc % PER_ROW)) = kx[i];
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -445,8 +462,8 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dc = 0; dc < DC; ++dc) {
-          const F af = load_frag(reinterpret_cast<const E *>(s_k + (kt * 16 + c16) * L::KROW +
-                                                              (dc * 32 + g * 8) * L::ES));
+          const F af = load_frag(reinterpret_cast<const E *>(
+              s_k + L::k_at(kt * 16 + c16, (dc * 32 + g * 8) * L::ES / 16)));
           acc = mfma_chunk(af, bq[dc], acc);
         }
         s[kt] = acc;
@@ -492,8 +509,27 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
       // contiguous 16-byte pieces (consecutive lanes, consecutive addresses), non-temporal:
       // the merge reads them once, long after.
       unsigned char *so = s_o[w];
+      if constexpr (L::ES == 2) {
+        // Lane (c16, g) holds d = 16 dt + 4 g + 0..3 of row-head c16. Lane groups g and g ^ 1
+        // swap halves (v_permlane16_swap pairs the odd 16-lane rows of its first operand
+        // with the even rows of its second), after which even groups hold the 8 consecutive
+        // d from 16 dt + 4 g of tile dt and odd groups those from 16 (dt + 1) + 4 (g - 1) of
+        // tile dt + 1: one 16-byte store each. Pairs of 8-byte stores merge into
+        // ds_write2_b64, which measured 7.5 bank-conflict cycles per instruction here.
+        static_assert(DT % 2 == 0, "output tiles are stored in pairs");
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) store4(reinterpret_cast<E *>(so + c16 * OROW) + dt * 16 + g * 4, o[dt]);
+        for (int dt = 0; dt < DT; dt += 2) {
+          const auto lo = __builtin_amdgcn_permlane16_swap(pack_bf16x2(o[dt][0], o[dt][1]),
+                                                           pack_bf16x2(o[dt + 1][0], o[dt + 1][1]), false, false);
+          const auto hi = __builtin_amdgcn_permlane16_swap(pack_bf16x2(o[dt][2], o[dt][3]),
+                                                           pack_bf16x2(o[dt + 1][2], o[dt + 1][3]), false, false);
+          const int d0 = (g & 1) ? 16 * (dt + 1) + 4 * (g - 1) : 16 * dt + 4 * g;
+          *reinterpret_cast<u32x4 *>(so + c16 * OROW + d0 * 2) = u32x4{lo[0], hi[0], lo[1], hi[1]};
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) store4(reinterpret_cast<E *>(so + c16 * OROW) + dt * 16 + g * 4, o[dt]);
+      }
       if (valid && g == 0) {
         const long ps = ((((long)b * a.h_kv + r) * a.n_q + t) * a.top_k + slot) * G + hd;
         reinterpret_cast<float2 *>(a.part_ml)[ps] = make_float2(rs > 0.f ? m : -INFINITY, rs);
@@ -507,12 +543,18 @@ __global__ __launch_bounds__(256) void kv_attend(KvArgs a, int log2g) {
         constexpr int PIECES_ROW = DH * L::ES / 16;  // 16-byte pieces per output row
         constexpr int NST = 16 * PIECES_ROW / 64;    // the whole tile, per lane
         static_assert(16 * PIECES_ROW % 64 == 0, "output pieces must fill whole waves");
+        // With 17-piece rows (256-byte rows padded by 16), piece p of row rw sits on bank
+        // group (rw + p) % 16. Lanes of row lane / 16 + 4 i take piece lane - lane / 16,
+        // which lies on bank group lane + 4 i, so the 16 lanes of an LDS pass (two rows)
+        // cover all 16 groups, with one address per lane for every i.
+        constexpr bool ROT = PIECES_ROW == 16 && OROW == 17 * 16;
         u32x4 val[NST];
         u32x4 *dst[NST];
 #pragma unroll
         for (int i = 0; i < NST; ++i) {
-          const int pc = lane + 64 * i, off = pc % PIECES_ROW;
+          const int pc = lane + 64 * i;
           int row = pc / PIECES_ROW;
+          const int off = ROT ? (lane - (lane >> 4)) & 15 : pc % PIECES_ROW;
           if (tt * QPT + (row >> log2g) >= n_e) row &= G - 1;
           const int en = s_list[tt * QPT + (row >> log2g)];
           const long pss = ((((long)b * a.h_kv + r) * a.n_q + (en >> 6)) * a.top_k + (en & 63)) * G + (row & (G - 1));
