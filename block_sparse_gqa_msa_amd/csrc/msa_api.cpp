@@ -135,7 +135,7 @@ size_t attn_prefill_ws(const msa_shape &s, msa::KvLayout *lay) {
 }
 
 int kv_seg_rows(const msa_shape &s) {
-  return msa::kv_segment_rows(s.batch, s.h_kv, s.n_q, s.top_k, s.h_q / s.h_kv, s.d_h,
+  return msa::kv_segment_rows(s.batch, s.h_kv, s.n_q, s.top_k, n_blocks(s), s.h_q / s.h_kv, s.d_h,
                               s.dtype == MSA_F32 ? 4 : 2);
 }
 

@@ -687,7 +687,7 @@ size_t kv_bwd_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long 
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   BwdLayout L;
   size_t o = kv_workspace_bytes(batch, h_kv, n_q, top_k, n_blocks, group, d_h, elem_bytes, &L.kv);
-  const long seg_rows = kv_segment_rows(batch, h_kv, n_q, top_k, group, d_h, elem_bytes);
+  const long seg_rows = kv_segment_rows(batch, h_kv, n_q, top_k, n_blocks, group, d_h, elem_bytes);
   const long n_seg = (n_q + seg_rows - 1) / seg_rows;
   const long NB = n_seg * batch * h_kv * n_blocks;
   const long slots = batch * h_kv * n_q * top_k;

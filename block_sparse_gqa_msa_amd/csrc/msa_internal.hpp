@@ -114,8 +114,8 @@ struct KvLayout {
 };
 
 // Rows per list segment for a prefill of this size (a multiple of the list-build tile).
-int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long group, long d_h,
-                    long elem_bytes);
+int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
+                    long d_h, long elem_bytes);
 size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
                           long d_h, long elem_bytes, KvLayout *lay);
 

@@ -34,14 +34,19 @@ constexpr long KV_Q_SLICE = 64L << 20;    // bytes of one group's Q rows per lis
 constexpr int HIST_ROWS_ENTRIES = 32768;  // entries per list-build workgroup, at most
 constexpr int HIST_MAX_BLOCKS = 32768;    // LDS histogram capacity (128 KiB)
 
-// Rows per list-build workgroup: HIST_ROWS_ENTRIES entries, halved (down to 2048) while the
-// call would have fewer than 512 workgroups, so that short calls still spread the build
-// over the chip (the 8K prefill had 16 workgroups, the 1M-context chunk 32). Row segments
-// are whole multiples of it, so a workgroup's rows lie in one segment.
-__host__ __device__ __forceinline__ long hist_tile_rows(long batch, long h_kv, long n_q, long top_k) {
+// Rows per list-build workgroup: HIST_ROWS_ENTRIES entries, halved while the call would
+// have fewer than 512 workgroups, so that short calls still spread the build over the chip
+// (the 8K prefill had 16 workgroups), but not below 2048 entries nor below n_blocks: a
+// histogram with fewer entries than bins holds mostly single counts, and its reservations
+// become one global atomic per entry (the 1M-context chunk's build took 512 workgroups of
+// 2048 entries over 16384 bins). Row segments are whole multiples of it, so a workgroup's
+// rows lie in one segment.
+__host__ __device__ __forceinline__ long hist_tile_rows(long batch, long h_kv, long n_q, long top_k,
+                                                        long n_blocks) {
   const long total = batch * h_kv * n_q * top_k;
+  const long least = n_blocks > 2048 ? n_blocks : 2048;
   long ent = HIST_ROWS_ENTRIES;
-  while (ent > 2048 && total / ent < 512) ent >>= 1;
+  while (ent > least && total / ent < 512) ent >>= 1;
   return ent / top_k > 1 ? ent / top_k : 1;
 }
 
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(256) void kv_fill(KvArgs a) {
 // Rows of this list-build workgroup (they lie in one row segment); `base` is the list
 // index of block 0 for them.
 __device__ __forceinline__ void hist_rows(const KvArgs &a, long &e_begin, long &e_end, long &base) {
-  const long rows_per_wg = hist_tile_rows(a.batch, a.h_kv, a.n_q, a.top_k);
+  const long rows_per_wg = hist_tile_rows(a.batch, a.h_kv, a.n_q, a.top_k, a.n_blocks);
   const long tiles_per_br = (a.n_q + rows_per_wg - 1) / rows_per_wg;
   const long br = blockIdx.x / tiles_per_br;
   const long r0 = (blockIdx.x % tiles_per_br) * rows_per_wg;
@@ -693,7 +698,7 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
       return (long)v;
     }();
     if (a.n_blocks <= HIST_MAX_BLOCKS && (long)a.n_blocks * (long)sizeof(int32_t) <= lds_max) {
-      const long rows_per_wg = hist_tile_rows(a.batch, a.h_kv, a.n_q, a.top_k);  // divides seg_rows
+      const long rows_per_wg = hist_tile_rows(a.batch, a.h_kv, a.n_q, a.top_k, a.n_blocks);  // divides seg_rows
       const unsigned wgs = (unsigned)((long)a.batch * a.h_kv * ((a.n_q + rows_per_wg - 1) / rows_per_wg));
       const size_t lds = (size_t)a.n_blocks * sizeof(int32_t);
       hipLaunchKernelGGL(kv_count_hist, dim3(wgs), dim3(1024), lds, s, a);
@@ -735,10 +740,10 @@ hipError_t run_kv(const KvArgs &a, int log2g, int stages, hipStream_t s) {
 
 }  // namespace
 
-int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long group, long d_h,
-                    long elem_bytes) {
+int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
+                    long d_h, long elem_bytes) {
   // about KV_Q_SLICE bytes of one group's Q rows per segment, in whole list-build tiles
-  const long tile = hist_tile_rows(batch, h_kv, n_q, top_k);
+  const long tile = hist_tile_rows(batch, h_kv, n_q, top_k, n_blocks);
   const long per_row = group * d_h * elem_bytes;
   long rows = std::max(1L, KV_Q_SLICE / per_row);
   rows = std::max(tile, rows / tile * tile);
@@ -748,7 +753,7 @@ int kv_segment_rows(long batch, long h_kv, long n_q, long top_k, long group, lon
 size_t kv_workspace_bytes(long batch, long h_kv, long n_q, long top_k, long n_blocks, long group,
                           long d_h, long elem_bytes, KvLayout *lay) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const long seg_rows = kv_segment_rows(batch, h_kv, n_q, top_k, group, d_h, elem_bytes);
+  const long seg_rows = kv_segment_rows(batch, h_kv, n_q, top_k, n_blocks, group, d_h, elem_bytes);
   const long n_seg = (n_q + seg_rows - 1) / seg_rows;
   const size_t NB = (size_t)(n_seg * batch * h_kv * n_blocks);
   const size_t slots = (size_t)(batch * h_kv * n_q * top_k);
