@@ -336,7 +336,10 @@ __global__ __launch_bounds__(256) void decode_finish(AttnArgs a, FinishArgs f, i
   using VS = VStage<E, DH, BS>;
   constexpr int DC = DH / 32, DT = DH / 16;
   constexpr int SEL_BYTES = 8 * SELECT_LDS * 4 + 2 * 256 * 4;  // lk, li per wave; w_key, w_idx
-  constexpr int MRG_BYTES = 4 * 16 * DH * 4 + 4 * 16 * 8;      // per wave: o[16][DH], (m, l)[16]
+  // per wave: o[16][MROW], (m, l)[16]; rows of DH + 4 floats, so the 16-byte stores of 8
+  // consecutive lanes (8 rows) start on different bank groups (DH floats put them on one)
+  constexpr int MROW = DH + 4;
+  constexpr int MRG_BYTES = 4 * 16 * MROW * 4 + 4 * 16 * 8;
   constexpr int BUF = cmax(4 * VS::BYTES, cmax(SEL_BYTES, MRG_BYTES));
   __shared__ __attribute__((aligned(16))) unsigned char s_buf[BUF];
   __shared__ int32_t s_sel[64];
@@ -398,11 +401,11 @@ __global__ __launch_bounds__(256) void decode_finish(AttnArgs a, FinishArgs f, i
 
   // 3. the four waves' partials, merged in LDS (the V^T regions are free once all are done)
   __syncthreads();
-  float *mo = reinterpret_cast<float *>(s_buf);                       // [4][16][DH]
-  float2 *mml = reinterpret_cast<float2 *>(s_buf + 4 * 16 * DH * 4);  // [4][16]
+  float *mo = reinterpret_cast<float *>(s_buf);                         // [4][16][MROW]
+  float2 *mml = reinterpret_cast<float2 *>(s_buf + 4 * 16 * MROW * 4);  // [4][16]
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
-    *reinterpret_cast<f32x4 *>(mo + (w * 16 + c16) * DH + dt * 16 + g * 4) = st.o[dt];
+    *reinterpret_cast<f32x4 *>(mo + (w * 16 + c16) * MROW + dt * 16 + g * 4) = st.o[dt];
   if (g == 0) mml[w * 16 + c16] = make_float2(st.m, st.l);
   __syncthreads();
   E *o = reinterpret_cast<E *>(a.o);
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(256) void decode_finish(AttnArgs a, FinishArgs f, i
       if (ml.y > 0.f) {
         const float wt = __builtin_amdgcn_exp2f(ml.x - M);
         L += wt * ml.y;
-        O += wt * mo[(u * 16 + hh) * DH + d];
+        O += wt * mo[(u * 16 + hh) * MROW + d];
       }
     }
     const long bh = (long)b * a.h_q + r * G + hh;

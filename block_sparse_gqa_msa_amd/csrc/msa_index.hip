@@ -360,13 +360,23 @@ __global__ __launch_bounds__(256) void index_pool_decode(IndexArgs a) {
 // fragment pattern, 64 bytes of each of 16 rows per instruction, made the kernel slower).
 // So each 64-key tile is read as contiguous 1 KiB pieces, one 16-byte piece per lane, into
 // registers a tile ahead, written to a wave-private LDS tile and read back as fragments.
+//
+// A fragment read's 16 lanes of one LDS pass take keys 0-7 at piece p and keys 8-15 at
+// piece p + 1. bf16 rows of 128 bytes stay unpadded with the piece XORed by key & 7, which
+// puts those 16 on distinct bank groups (rows padded by 16 bytes measured 3.8 conflict
+// cycles per read); other rows keep 16 bytes of padding.
 template <typename E, int DI>
 struct SelStage {
   static constexpr int RB = DI * (int)sizeof(E);  // bytes of one key row
   static constexpr int PPK = RB / 16;             // 16-byte pieces per key
   static constexpr int PPL = KT * PPK / 64;       // pieces per lane and tile
-  static constexpr int ROW = RB + 16;             // padded LDS row: fragment reads conflict-free
+  static constexpr bool SWZ = sizeof(E) == 2 && RB == 128;
+  static constexpr int ROW = SWZ ? RB : RB + 16;
   static constexpr int WAVE_BYTES = KT * ROW;
+  // byte offset of 16-byte piece `piece` of staged key `key`
+  __device__ static __forceinline__ int at(int key, int piece) {
+    return key * ROW + (SWZ ? piece ^ (key & 7) : piece) * 16;
+  }
 };
 
 template <typename E, int DI, int BS>
@@ -423,7 +433,7 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
 #pragma unroll
     for (int i = 0; i < ST::PPL; ++i) {
       const int pc = i * 64 + lane;
-      *reinterpret_cast<u32x4 *>(stg + (pc / ST::PPK) * ST::ROW + (pc % ST::PPK) * 16) = src[i];
+      *reinterpret_cast<u32x4 *>(stg + ST::at(pc / ST::PPK, pc % ST::PPK)) = src[i];
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // wave-private tile: in-order LDS
     F cur[4][DC];
@@ -431,8 +441,8 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void index_select_decode(IndexArgs 
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int dc = 0; dc < DC; ++dc)
-        cur[mt][dc] = load_frag(reinterpret_cast<const E *>(stg + (mt * 16 + c16) * ST::ROW) +
-                                dc * 32 + g * 8);
+        cur[mt][dc] = load_frag(reinterpret_cast<const E *>(
+            stg + ST::at(mt * 16 + c16, (dc * 32 + g * 8) * (int)sizeof(E) / 16)));
     const bool need_mask = k0 + KT - 1 > p;
 #pragma unroll
     for (int blk = 0; blk < BPT; ++blk) {
