@@ -28,10 +28,16 @@ __global__ __launch_bounds__(256) void index_project(ProjArgs a) {
   using F = typename Frag<E>::type;
   constexpr int ES = (int)sizeof(E);
   constexpr int PM = 16 * MT;                   // rows per workgroup
-  constexpr int XROW = PJ_K * ES + 16;
+  // x rows in LDS: a fragment read's 16 lanes of one LDS pass take rows 0-7 at 16-byte
+  // piece p and rows 8-15 at piece p + 1; bf16 rows of 128 bytes stay unpadded with the
+  // piece XORed by row & 7, which puts the 16 on distinct bank groups (16 bytes of padding
+  // left two on one); fp32 rows keep the padding.
+  constexpr bool XSW = ES == 2 && PJ_K * ES == 128;
+  constexpr int XROW = XSW ? PJ_K * ES : PJ_K * ES + 16;
   constexpr int PPR = PJ_K * ES / 16;           // 16-byte pieces per staged row
   constexpr int PT = PM * PPR / 256;            // pieces per thread
   __shared__ __attribute__((aligned(16))) unsigned char s_x[2][PM * XROW];
+  auto x_at = [](int row, int piece) { return row * XROW + (XSW ? piece ^ (row & 7) : piece) * 16; };
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
   const long rows = (long)a.batch * a.n_q;
@@ -80,7 +86,7 @@ __global__ __launch_bounds__(256) void index_project(ProjArgs a) {
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int pc = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(dst + (pc / PPR) * XROW + (pc % PPR) * 16) = xp[i];
+      *reinterpret_cast<u32x4 *>(dst + x_at(pc / PPR, pc % PPR)) = xp[i];
     }
   };
   const int n_tiles = a.d_model / PJ_K;
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256) void index_project(ProjArgs a) {
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const F af = load_frag(reinterpret_cast<const E *>(cur + (mt * 16 + c16) * XROW + (kc * 32 + g * 8) * ES));
+          const F af = load_frag(reinterpret_cast<const E *>(cur + x_at(mt * 16 + c16, (kc * 32 + g * 8) * ES / 16)));
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_chunk(af, wf[kc][nt], acc[mt][nt]);
         }
