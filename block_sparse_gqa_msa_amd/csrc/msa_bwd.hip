@@ -15,8 +15,9 @@
 //               tile (32 / G rows x the G heads) every wave computes S = Q K_w^T and
 //               dP = dO V_w^T on the matrix cores with the row-heads down the accumulator
 //               rows; the accumulator layout is then directly the A operand of
-//               dV_w += P^T dO and dK_w += dS^T Q (Q and dO are staged transposed in LDS
-//               for the B operands). dS goes to LDS, and each wave
+//               dV_w += P^T dO and dK_w += dS^T Q, whose B operands are the staged Q and
+//               dO tiles read transposed (bf16: in place, with the matrix cores'
+//               transposing LDS read; fp32: from transposed copies). dS goes to LDS, and each wave
 //               computes dq for its slice of d over the whole block, written as one partial
 //               per (row, slot, head). dK_w and dV_w stay in registers while a run stays on
 //               one list and are written as one fp32 partial per (run, list) segment.
@@ -94,7 +95,7 @@ struct BwdLds {
   static constexpr bool P32S = ES == 2 && BS * ES == 128;
   static constexpr int QPIECES = DH * ES / 16;             // 16-byte pieces per Q, dO row
   static constexpr int QROW = DH * ES + (P32Q ? 32 : 16);  // Q, dO row-major rows
-  static constexpr int TROW = TR * ES + 16;               // Q^T, dO^T rows (one per d)
+  static constexpr int TROW = TR * ES + 16;               // fp32 Q^T, dO^T rows (one per d)
   static constexpr int SROW = BS * ES + (P32S ? 32 : 16);  // dS rows, K^T rows
   static constexpr int OROW = DSL * ES + 16;              // per-wave dq staging rows
   static constexpr int NTASK = 16 * (DH / PE);       // (row pair, piece) tasks per tensor
